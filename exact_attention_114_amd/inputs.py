@@ -1,0 +1,161 @@
+"""Seeded synthetic attention inputs and the workload table.
+
+This module only draws and rounds numbers; it computes nothing of attention.
+Both the fp64 oracle (through the tests and the benchmark's CPU leg) and the
+HIP path consume what it produces, so the two sides see bit-identical inputs.
+
+Recipe (the same for every workload):
+  * ``numpy.random.Generator(PCG64(seed))``;
+  * draw Q, then K, then V with ``standard_normal(shape, dtype=float32)``;
+  * optionally multiply K by a power of two (exact in fp32);
+  * round each fp32 value to the storage type with round-to-nearest-even:
+    fp16 through numpy's ``astype(float16)``, bf16 by rounding the fp32 bit
+    pattern to its upper 16 bits.
+
+Storage is returned as ``uint16`` bit patterns (numpy has no bf16 type) plus
+an exact float64 upcast for the oracle.
+
+Shapes follow the pages' workloads: the [B, H, L, D] layout of the memory
+table in the CUDA-fusion lecture page (section 1, "traditional attention
+memory bottleneck"), the GPT-2 N=1024, d=64 check in the Triton FA2
+walkthrough, and that walkthrough's benchmark shape B=4, H=48, d=64 with a
+causal mask; grouped-query attention is named in the FA-principles page,
+section 1.3.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention forward problem, fully determined by its fields."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str  # F16 or BF16: storage type of Q, K, V
+    causal: bool
+    scale: float  # passed to the kernel as a float32
+    seed: int
+    k_mult: float = 1.0  # exact power-of-two multiplier applied to K before rounding
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOPs: two N x N x d contractions, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+    def q_shape(self):
+        return (self.B, self.Hq, self.N, self.d)
+
+    def kv_shape(self):
+        return (self.B, self.Hkv, self.N, self.d)
+
+
+def _c4(n: int) -> Workload:
+    return Workload(f"causal_b4_h48_n{n}_d64_f16", 4, 48, 48, n, 64, F16, True, 0.125,
+                    40 + int(round(math.log2(n // 1024))))
+
+
+# The five workloads: single-head, GPT-2 shaped, long head dim, the causal
+# sweep, and GQA causal long sequence with K scaled by 2.
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("single_head_n256_d64_f16", 1, 1, 1, 256, 64, F16, False, 0.125, 1),
+        Workload("gpt2_b8_h12_n1024_d64_bf16", 8, 12, 12, 1024, 64, BF16, False, 0.125, 2),
+        Workload("long_head_b1_h16_n2048_d128_f16", 1, 16, 16, 2048, 128, F16, False,
+                 1.0 / math.sqrt(128.0), 3),
+        _c4(1024), _c4(2048), _c4(4096), _c4(8192), _c4(16384),
+        Workload("gqa_causal_b4_hq32_hkv8_n8192_d128_bf16", 4, 32, 8, 8192, 128, BF16, True,
+                 1.0 / math.sqrt(128.0), 5, k_mult=2.0),
+    ]
+}
+
+CAUSAL_SWEEP: List[str] = [_c4(n).name for n in (1024, 2048, 4096, 8192, 16384)]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (round to nearest even); uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of fp16/bf16 bit patterns to float64."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == F16:
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F16:
+        return f32_to_f16_bits(x)
+    if dtype == BF16:
+        return f32_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+@dataclasses.dataclass
+class QKV:
+    """Storage bit patterns (uint16) for Q, K, V."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    dtype: str
+
+    def f64(self):
+        return (bits_to_f64(self.q, self.dtype), bits_to_f64(self.k, self.dtype),
+                bits_to_f64(self.v, self.dtype))
+
+
+def draw_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
+             k_mult: float = 1.0) -> QKV:
+    """Draw Q [B,Hq,N,d], K and V [B,Hkv,N,d] per the recipe in the module doc."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = g.standard_normal((B, Hq, N, d), dtype=np.float32)
+    k = g.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    v = g.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    if k_mult != 1.0:
+        k = k * np.float32(k_mult)
+    return QKV(to_bits(q, dtype), to_bits(k, dtype), to_bits(v, dtype), dtype)
+
+
+def workload_qkv(w: Workload) -> QKV:
+    return draw_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.k_mult)
+
+
+def scale_f32(scale: float) -> float:
+    """The scale as the kernel receives it: rounded to float32, returned as a Python float."""
+    return float(np.float32(scale))
+
+
+def small_case(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str, causal: bool,
+               seed: int, scale: Optional[float] = None, k_mult: float = 1.0) -> Workload:
+    """An ad-hoc workload (parity sweeps over odd shapes)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return Workload(f"case_b{B}_hq{Hq}_hkv{Hkv}_n{N}_d{d}_{dtype}_{'c' if causal else 'nc'}_s{seed}",
+                    B, Hq, Hkv, N, d, dtype, causal, scale, seed, k_mult)
