@@ -1,0 +1,141 @@
+"""ctypes binding over the C ABI of libfa_fwd.so (declared in include/fa.h).
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, outputs are allocated when the caller does not pass them, and every
+step of the computation runs in the HIP kernels behind ``fa_fwd``. There is
+no fallback: when the library is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+LIB_NAME = "libfa_fwd.so"
+
+FA_F16, FA_BF16, FA_F32 = 0, 1, 2
+FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_HIP = range(6)
+
+# Every function include/fa.h declares, with its ctypes signature.
+SIGNATURES = {
+    "fa_fwd": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5
+               + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "fa_last_hip_error": (ctypes.c_int, []),
+    "fa_fwd_tile": (ctypes.c_int, [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int,
+                                                          ctypes.POINTER(ctypes.c_int),
+                                                          ctypes.POINTER(ctypes.c_int),
+                                                          ctypes.POINTER(ctypes.c_int64)]),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """An fa_status other than FA_OK, or a missing library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Open libfa_fwd.so next to this file (raises FaError if it was never built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise FaError(-1, f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        lib = load_library()
+        msg = lib.fa_status_str(status).decode()
+        if status == FA_ERR_HIP:
+            msg += f" (hipError_t {lib.fa_last_hip_error()})"
+        raise FaError(status, msg)
+
+
+def fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: int, Hkv: int, N: int, d: int,
+            scale: float, causal: bool, in_dtype: int, out_dtype: int, stream: int = 0) -> int:
+    """Call fa_fwd with raw device addresses; returns the fa_status code."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, float(scale), int(causal),
+                                 in_dtype, out_dtype, stream)
+
+
+def tile(B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool, in_dtype: int) -> Tuple[int, int, int]:
+    """(query rows per work-group, keys per tile, work-group count) fa_fwd uses."""
+    bm, bn, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    _check(load_library().fa_fwd_tile(B, Hq, Hkv, N, d, int(bool(causal)), in_dtype,
+                                      ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(grid)))
+    return bm.value, bn.value, grid.value
+
+
+def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out_dtype=None,
+        out=None, lse=None, stream=None):
+    """Exact attention forward on the GPU: returns (O, LSE).
+
+    q: [B, Hq, N, d], k and v: [B, Hkv, N, d], contiguous fp16 or bf16 CUDA
+    tensors (on ROCm, HIP device tensors). scale defaults to 1/sqrt(d);
+    out_dtype defaults to float32 (or pass q.dtype); LSE is float32 [B, Hq, N].
+    Runs on ``stream`` (a torch stream) or torch's current stream.
+    """
+    import torch
+
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must be float16 or bfloat16")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must share one dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FaError(FA_ERR_SHAPE, "q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise FaError(FA_ERR_SHAPE, "q, k, v must be contiguous")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise FaError(FA_ERR_SHAPE, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out_dtype is None:
+        out_dtype = torch.float32
+    in_code = FA_F16 if q.dtype == torch.float16 else FA_BF16
+    if out_dtype == torch.float32:
+        out_code = FA_F32
+    elif out_dtype == q.dtype:
+        out_code = in_code
+    else:
+        raise FaError(FA_ERR_UNSUPPORTED, "out_dtype must be float32 or the input dtype")
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if out.shape != (B, Hq, N, d) or out.dtype != out_dtype or not out.is_contiguous():
+        raise FaError(FA_ERR_SHAPE, "out must be a contiguous [B, Hq, N, d] tensor of out_dtype")
+    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise FaError(FA_ERR_SHAPE, "lse must be a contiguous float32 [B, Hq, N] tensor")
+    if out.device != q.device or lse.device != q.device or k.device != q.device or v.device != q.device:
+        raise FaError(FA_ERR_SHAPE, "all tensors must be on one device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                   B, Hq, Hkv, N, d, scale, int(bool(causal)), in_code, out_code, stream.cuda_stream))
+    return out, lse

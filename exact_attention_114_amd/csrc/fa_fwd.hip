@@ -1,0 +1,144 @@
+// fa_fwd.hip — host launcher and C ABI (include/fa.h) of the gfx950 exact-attention forward.
+//
+// Argument checking happens on the host before any HIP call (the operator-interface
+// checks of the intelliparadigm page, section 2.2: 4-D [batch, heads, seq, head_dim]
+// inputs, outputs shaped like the query, fp32 statistics [batch, heads, seq]).
+// The launch is the FA2 grid over (batch, head, Q-tile) of the Triton FA2 walkthrough,
+// flattened to one dimension so the kernel can remap work-groups onto XCDs.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/fa.h"
+#include "fa_fwd_kernel.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Waves per work-group: 4 (BM = 128 query rows); two work-groups share a CU.
+constexpr int kWaves = 4;
+constexpr int kBlockM = 32 * kWaves;
+
+template <bool BF16, int D, bool CAUSAL, bool OUT_F32>
+fa_status launch(const fa::Params& p, hipStream_t stream) {
+  auto kern = fa::fa_fwd_kernel<BF16, D, CAUSAL, OUT_F32, kWaves>;
+  constexpr size_t lds = 2 * 2 * fa::kBN * D * 2;  // double-buffered K and V tiles
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (attr_err != hipSuccess) {
+    g_last_hip_error = (int)attr_err;
+    return FA_ERR_HIP;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), lds, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+template <bool BF16, int D, bool CAUSAL>
+fa_status dispatch_out(const fa::Params& p, bool out_f32, hipStream_t s) {
+  return out_f32 ? launch<BF16, D, CAUSAL, true>(p, s) : launch<BF16, D, CAUSAL, false>(p, s);
+}
+template <bool BF16, int D>
+fa_status dispatch_causal(const fa::Params& p, bool causal, bool out_f32, hipStream_t s) {
+  return causal ? dispatch_out<BF16, D, true>(p, out_f32, s) : dispatch_out<BF16, D, false>(p, out_f32, s);
+}
+template <bool BF16>
+fa_status dispatch_d(const fa::Params& p, int d, bool causal, bool out_f32, hipStream_t s) {
+  return d == 64 ? dispatch_causal<BF16, 64>(p, causal, out_f32, s) : dispatch_causal<BF16, 128>(p, causal, out_f32, s);
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Shared shape/type validation. Returns FA_OK and fills the derived sizes.
+fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype in_dtype,
+                        int64_t* n_qtiles, int64_t* grid) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (N >= lim / d) return FA_ERR_SHAPE;                 // row offsets within a head stay 32-bit
+  if (B >= lim / Hq || B * Hq >= lim / N) return FA_ERR_SHAPE;  // LSE index / head planes
+  const int64_t nq = (N + kBlockM - 1) / kBlockM;
+  if (B * Hq >= lim / nq) return FA_ERR_SHAPE;           // grid size
+  *n_qtiles = nq;
+  *grid = B * Hq * nq;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                 int64_t Hkv, int64_t N, int64_t d, float scale, int causal, fa_dtype in_dtype,
+                 fa_dtype out_dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+  int64_t nq = 0, grid = 0;
+  const fa_status st = check_problem(B, Hq, Hkv, N, d, in_dtype, &nq, &grid);
+  if (st != FA_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
+  if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+
+  fa::Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.N = (int)N;
+  p.group = (int)(Hq / Hkv);
+  p.n_qtiles = (int)nq;
+  p.total_wg = (int)grid;
+  p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+
+  const bool bf16 = in_dtype == FA_BF16;
+  const bool out_f32 = out_dtype == FA_F32;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return bf16 ? dispatch_d<true>(p, (int)d, causal != 0, out_f32, s)
+              : dispatch_d<false>(p, (int)d, causal != 0, out_f32, s);
+}
+
+fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, fa_dtype in_dtype,
+                      int* block_m, int* block_n, int64_t* grid) {
+  if (!block_m || !block_n || !grid) return FA_ERR_NULLPTR;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  int64_t nq = 0, g = 0;
+  const fa_status st = check_problem(B, Hq, Hkv, N, d, in_dtype, &nq, &g);
+  if (st != FA_OK) return st;
+  *block_m = kBlockM;
+  *block_n = fa::kBN;
+  *grid = g;
+  return FA_OK;
+}
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: a pointer argument is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes, head grouping, scale or causal flag";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128, inputs fp16/bf16, output fp32 or the input type";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error (see fa_last_hip_error)";
+  }
+  return "unknown fa_status";
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact-attention forward library, libfa_fwd.so.
+ *
+ * The operation (FlashAttention forward) is the standard scaled-dot-product
+ * attention the pages start from — "PyTorch Transformer Flash Attention机制：
+ * 内存访问优化与CUDA Kernel融合的底层实现" (zyxy.net), section 1, and
+ * "FlashAttention算法原理与性能优化实战" (intelliparadigm), section 1.1 —
+ * computed tile by tile with the online-softmax recurrence ("Flash Attention
+ * 是怎么做到又快又省显存的？", cnblogs, section 时间复杂度) in the FA2 loop order
+ * and grid (Triton FA2 walkthrough, xrbh.cn), so the N x N score matrix never
+ * reaches device memory. For every batch b, query head hq and query row i:
+ *
+ *   S_ij   = scale * sum_c Q[b,hq,i,c] * K[b,hkv,j,c],   hkv = hq / (Hq / Hkv)
+ *   keys j visible to row i: all j < N, or only j <= i when causal
+ *   O[b,hq,i,:] = sum_j softmax_j(S_i.) * V[b,hkv,j,:]
+ *   lse[b,hq,i] = ln sum_j exp(S_ij)          (natural log, over visible j)
+ *
+ * The per-row log-sum-exp is the statistic a backward pass recomputes the
+ * probabilities from (intelliparadigm page, section 1.2.3; the FA2
+ * walkthrough's logsumexp L). Grouped-query attention follows the
+ * intelliparadigm page, section 1.3: query heads are grouped consecutively,
+ * G = Hq / Hkv query heads per K/V head.
+ *
+ * Layout: every tensor is dense and row-major in the [batch, head, seq, dim]
+ * order of the zyxy.net page's section 1 (B, H, L, D):
+ *   q  [B][Hq ][N][d]   in_dtype
+ *   k  [B][Hkv][N][d]   in_dtype
+ *   v  [B][Hkv][N][d]   in_dtype
+ *   o  [B][Hq ][N][d]   out_dtype
+ *   lse[B][Hq ][N]      float32
+ *
+ * Ownership: all five pointers are device pointers owned by the caller (for
+ * example from PyTorch). The library allocates no device memory, takes no
+ * workspace and keeps no per-call state beyond a thread-local copy of the
+ * last HIP error. o and lse must not overlap q, k, v or each other.
+ *
+ * Execution: calls are asynchronous on `stream` (a hipStream_t; NULL means
+ * the default stream) and return once the kernel is enqueued. A device-side
+ * fault surfaces at the caller's next synchronisation, as usual for HIP.
+ * Results are deterministic: no atomics, a fixed reduction order.
+ *
+ * Errors: arguments are checked on the host before any HIP call; on any
+ * error nothing is launched and the outputs are left untouched.
+ */
+#ifndef FA_FWD_H_
+#define FA_FWD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. Inputs: FA_F16 or FA_BF16. Output O: FA_F32, or the input type. */
+typedef enum {
+  FA_F16 = 0,
+  FA_BF16 = 1,
+  FA_F32 = 2
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULLPTR = 1,     /* a pointer argument is NULL */
+  FA_ERR_SHAPE = 2,       /* B, Hq, Hkv, N or d < 1; Hq not a multiple of Hkv; non-finite
+                             or non-positive scale; sizes beyond the 32-bit index range */
+  FA_ERR_UNSUPPORTED = 3, /* d not 64 or 128; in_dtype not F16/BF16; out_dtype not F32 or in_dtype */
+  FA_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned */
+  FA_ERR_HIP = 5          /* the HIP runtime reported an error; see fa_last_hip_error() */
+} fa_status;
+
+/*
+ * fa_fwd — exact attention forward (O and the natural-log LSE), see above.
+ *
+ *   q, k, v   device pointers, layouts above, element type in_dtype
+ *   o         device pointer, [B][Hq][N][d] of out_dtype
+ *   lse       device pointer, [B][Hq][N] float32
+ *   B, Hq, Hkv, N, d   sizes; Hq % Hkv == 0; d in {64, 128}; N >= 1 (any N,
+ *             tails are masked); B*Hq*ceil(N/128) and N*d below 2^31
+ *   scale     multiplies Q.K^T (commonly 1/sqrt(d)); finite and > 0
+ *   causal    0: every key visible; 1: key j visible to query i iff j <= i
+ *   in_dtype  FA_F16 or FA_BF16
+ *   out_dtype FA_F32 (recommended: keeps O within fp32 rounding) or in_dtype
+ *   stream    hipStream_t to enqueue on, or NULL
+ *
+ * Returns FA_OK after enqueueing, or an error status with nothing launched.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 float scale, int causal, fa_dtype in_dtype, fa_dtype out_dtype,
+                 void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* The hipError_t value behind the most recent FA_ERR_HIP on the calling thread (0 if none). */
+int fa_last_hip_error(void);
+
+/*
+ * fa_fwd_tile — the work decomposition fa_fwd uses for a problem, so a
+ * caller can reason about the launch (for example to count the K/V bytes
+ * each work-group reads). Writes the query rows per work-group (*block_m),
+ * the keys per inner tile (*block_n) and the work-group count (*grid).
+ * Validates like fa_fwd (pointers to outputs must be non-NULL) and makes no
+ * HIP call.
+ */
+fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                      fa_dtype in_dtype, int* block_m, int* block_n, int64_t* grid);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H_ */

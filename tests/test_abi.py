@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call.
+
+Every call below carries at least one invalid argument, and all non-NULL
+pointers are odd addresses (misaligned), so even a validation bug could not
+reach a kernel launch: the alignment check would still refuse it.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_attention_114_amd import binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+BAD = 0x1001  # non-NULL, misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(bnd.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bnd.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", bnd.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings():
+    for s in range(6):
+        msg = bnd.status_str(s)
+        assert msg.startswith("FA_"), msg
+    assert "unknown" in bnd.status_str(99)
+    assert bnd.load_library().fa_last_hip_error() == 0
+
+
+def call(**kw):
+    args = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, B=1, Hq=2, Hkv=1, N=64, d=64, scale=0.125, causal=0,
+                in_dtype=bnd.FA_F16, out_dtype=bnd.FA_F32)
+    args.update(kw)
+    return bnd.fwd_raw(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["Hq"],
+                       args["Hkv"], args["N"], args["d"], args["scale"], args["causal"], args["in_dtype"],
+                       args["out_dtype"], 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_null_pointers(which):
+    assert call(**{which: 0}) == bnd.FA_ERR_NULLPTR
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0), dict(Hkv=0), dict(N=0), dict(d=0), dict(B=-1),
+                                dict(Hq=3, Hkv=2), dict(N=(1 << 31) // 64), dict(B=1 << 20, Hq=1 << 12),
+                                dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=0.0),
+                                dict(scale=-0.125), dict(causal=2)])
+def test_shape_errors(kw):
+    assert call(**kw) == bnd.FA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(d=256), dict(in_dtype=bnd.FA_F32),
+                                dict(in_dtype=7), dict(out_dtype=bnd.FA_BF16),
+                                dict(in_dtype=bnd.FA_BF16, out_dtype=bnd.FA_F16)])
+def test_unsupported(kw):
+    assert call(**kw) == bnd.FA_ERR_UNSUPPORTED
+
+
+def test_alignment_is_checked_last():
+    # every other argument valid: only the misaligned pointers stop the call
+    assert call() == bnd.FA_ERR_ALIGN
+    assert call(in_dtype=bnd.FA_BF16, out_dtype=bnd.FA_BF16, d=128, causal=1, Hq=8, Hkv=2, N=1) == bnd.FA_ERR_ALIGN
+
+
+def test_tile_query():
+    bm, bn, grid = bnd.tile(4, 32, 8, 8192, 128, True, bnd.FA_BF16)
+    assert bn == 64 and bm % 32 == 0 and grid == 4 * 32 * ((8192 + bm - 1) // bm)
+    bm, bn, grid = bnd.tile(1, 1, 1, 1, 64, False, bnd.FA_F16)
+    assert grid == 1
+    with pytest.raises(bnd.FaError):
+        bnd.tile(1, 3, 2, 64, 64, False, bnd.FA_F16)
+    lib = bnd.load_library()
+    x = ctypes.c_int()
+    g = ctypes.c_int64()
+    assert lib.fa_fwd_tile(1, 1, 1, 64, 64, 0, 0, None, ctypes.byref(x), ctypes.byref(g)) == bnd.FA_ERR_NULLPTR
+
+
+def test_binding_has_no_cpu_path():
+    """The Python side only marshals: CPU tensors are refused, nothing is computed on the host."""
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(bnd.FaError):
+        bnd.fwd(q, q, q)

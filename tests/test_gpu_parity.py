@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (written here, applied everywhere below):
+  * O: max |O_gpu - O_ref| <= 2e-3 for fp16 inputs, <= 1e-2 for bf16 inputs (N(0,1) data);
+  * LSE: |LSE_gpu - LSE_ref| <= 1e-4 * max(1, |LSE_ref|) (relative, with a floor of 1 so that
+    rows whose LSE is near 0 -- causal row 0 is a single score -- are not held to an
+    ill-posed relative bound).
+Inputs are the seeded generator's bit patterns; oracle and kernel see identical bits.
+Small and ragged shapes are compared element by element; the full-size workloads (the
+shapes and launch configuration the benchmark times) on sampled rows the oracle computes
+one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_114_amd as fa
+from exact_attention_114_amd import binding as bnd
+from exact_attention_114_amd import inputs as I
+from oracle import attention_fp64, head_attention_fp64, kv_head_of
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {I.F16: 2e-3, I.BF16: 1e-2}
+TOL_LSE = 1e-4
+DEV = "cuda:0"
+
+
+def tdtype(dt):
+    return torch.float16 if dt == I.F16 else torch.bfloat16
+
+
+def to_dev(bits, dt):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdtype(dt)).to(DEV)
+
+
+def run_gpu(w, qkv, out_dtype=torch.float32):
+    print(f"[gpu] fa_fwd {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} {w.dtype} "
+          f"causal={w.causal} seed={w.seed} out={out_dtype}", flush=True)
+    q, k, v = (to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v))
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def assert_close(O, L, O_ref, L_ref, dt, what=""):
+    assert np.isfinite(O).all() and np.isfinite(L).all(), f"{what}: non-finite output"
+    err_o = np.abs(O - O_ref).max()
+    err_l = (np.abs(L - L_ref) / np.maximum(1.0, np.abs(L_ref))).max()
+    assert err_o <= TOL_O[dt], f"{what}: max|dO| = {err_o:.3e} > {TOL_O[dt]}"
+    assert err_l <= TOL_LSE, f"{what}: max LSE rel err = {err_l:.3e} > {TOL_LSE}"
+    return err_o, err_l
+
+
+def check_full(w, out_dtype=torch.float32):
+    qkv = I.workload_qkv(w)
+    O, L = run_gpu(w, qkv, out_dtype)
+    O_ref, L_ref = attention_fp64(*qkv.f64(), I.scale_f32(w.scale), w.causal)
+    if out_dtype != torch.float32:
+        # the stored output is rounded to the input type: compare with the rounded oracle
+        O_ref = I.bits_to_f64(I.to_bits(O_ref.astype(np.float32), w.dtype), w.dtype)
+    return assert_close(O, L, O_ref, L_ref, w.dtype, w.name)
+
+
+# ---------------------------------------------------------------- small and ragged shapes
+
+RAGGED_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 257]
+
+
+@pytest.mark.parametrize("N", RAGGED_N)
+@pytest.mark.parametrize("d,dt", [(64, I.F16), (64, I.BF16), (128, I.F16), (128, I.BF16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_shapes(N, d, dt, causal):
+    check_full(I.small_case(1, 2, 1, N, d, dt, causal, seed=100 + N))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (8, 2), (8, 1), (16, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_groups(Hq, Hkv, causal):
+    check_full(I.small_case(2, Hq, Hkv, 300, 64, I.F16, causal, seed=200 + Hq))
+    check_full(I.small_case(1, Hq, Hkv, 200, 128, I.BF16, causal, seed=300 + Hq, k_mult=2.0))
+
+
+@pytest.mark.parametrize("dt", [I.F16, I.BF16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_output_in_input_dtype(dt, causal):
+    check_full(I.small_case(2, 4, 2, 333, 64, dt, causal, seed=400), out_dtype=tdtype(dt))
+    check_full(I.small_case(1, 2, 2, 190, 128, dt, causal, seed=401), out_dtype=tdtype(dt))
+
+
+def test_scale_values():
+    for s in (1.0, 0.05, 0.3):
+        check_full(I.small_case(1, 2, 2, 150, 64, I.F16, True, seed=402, scale=s))
+
+
+# ---------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["single_head_n256_d64_f16", "gpt2_b8_h12_n1024_d64_bf16",
+                                  "long_head_b1_h16_n2048_d128_f16", "causal_b4_h48_n1024_d64_f16"])
+def test_workload_full(name):
+    check_full(I.WORKLOADS[name])
+
+
+def sampled_rows(N, rng, n_random=24):
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
+    rows = set(r for r in fixed if 0 <= r < N)
+    rows.update(int(x) for x in rng.integers(0, N, n_random))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["causal_b4_h48_n2048_d64_f16", "causal_b4_h48_n4096_d64_f16",
+                                  "causal_b4_h48_n8192_d64_f16", "causal_b4_h48_n16384_d64_f16",
+                                  "gqa_causal_b4_hq32_hkv8_n8192_d128_bf16"])
+def test_workload_sampled(name):
+    w = I.WORKLOADS[name]
+    qkv = I.workload_qkv(w)
+    O, L = run_gpu(w, qkv)
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    rng = np.random.default_rng(w.seed)
+    heads = {(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2), (1, min(w.Hq - 1, 5))}
+    scale = I.scale_f32(w.scale)
+    for (b, hq) in sorted(heads):
+        hk = kv_head_of(hq, w.Hq, w.Hkv)
+        rows = sampled_rows(w.N, rng)
+        q = I.bits_to_f64(qkv.q[b, hq][rows], w.dtype)
+        k = I.bits_to_f64(qkv.k[b, hk], w.dtype)
+        v = I.bits_to_f64(qkv.v[b, hk], w.dtype)
+        O_ref, L_ref = head_attention_fp64(q, k, v, scale, w.causal, q_pos=rows)
+        assert_close(O[b, hq][rows], L[b, hq][rows], O_ref, L_ref, w.dtype, f"{name} b={b} h={hq}")
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_v_ones_gives_ones():
+    w = I.small_case(2, 4, 2, 513, 128, I.BF16, True, seed=500)
+    qkv = I.workload_qkv(w)
+    qkv.v[...] = I.to_bits(np.ones(qkv.v.shape, np.float32), w.dtype)
+    O, _ = run_gpu(w, qkv)
+    # P enters P V rounded to the input type while l sums the unrounded exponentials, so the
+    # weights need not sum to exactly 1 on the GPU: the O bar applies, not exact equality.
+    assert np.abs(O - 1.0).max() <= TOL_O[w.dtype]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero_gives_mean(causal):
+    w = I.small_case(1, 2, 2, 400, 64, I.F16, causal, seed=501)
+    qkv = I.workload_qkv(w)
+    qkv.q[...] = 0
+    O, L = run_gpu(w, qkv)
+    v = I.bits_to_f64(qkv.v, w.dtype)
+    n = np.arange(1, w.N + 1)
+    for h in range(2):
+        if causal:
+            exp_O, exp_L = np.cumsum(v[0, h], axis=0) / n[:, None], np.log(n)
+        else:
+            exp_O, exp_L = np.broadcast_to(v[0, h].mean(axis=0), v[0, h].shape), np.full(w.N, math.log(w.N))
+        assert np.abs(O[0, h] - exp_O).max() <= TOL_O[w.dtype]
+        assert (np.abs(L[0, h] - exp_L) / np.maximum(1, exp_L)).max() <= TOL_LSE
+
+
+def test_gqa_equals_repeated_heads_bitwise():
+    w = I.small_case(2, 8, 2, 260, 64, I.F16, True, seed=502)
+    qkv = I.workload_qkv(w)
+    O1, L1 = run_gpu(w, qkv)
+    rep = I.QKV(qkv.q, np.repeat(qkv.k, 4, axis=1), np.repeat(qkv.v, 4, axis=1), qkv.dtype)
+    w2 = I.small_case(2, 8, 8, 260, 64, I.F16, True, seed=502)
+    O2, L2 = run_gpu(w2, rep)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(L1, L2)
+
+
+def test_deterministic_and_stream_respected():
+    w = I.WORKLOADS["gpt2_b8_h12_n1024_d64_bf16"]
+    qkv = I.workload_qkv(w)
+    q, k, v = (to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v))
+    o1, l1 = fa.fwd(q, k, v, scale=w.scale)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = fa.fwd(q, k, v, scale=w.scale, stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_outputs_written_in_place_and_errors_raise():
+    w = I.small_case(1, 2, 2, 100, 64, I.F16, False, seed=503)
+    qkv = I.workload_qkv(w)
+    q, k, v = (to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v))
+    out = torch.full((1, 2, 100, 64), float("nan"), device=DEV)
+    lse = torch.full((1, 2, 100), float("nan"), device=DEV)
+    o, l = fa.fwd(q, k, v, scale=w.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr() and torch.isfinite(out).all() and torch.isfinite(lse).all()
+    with pytest.raises(bnd.FaError):
+        fa.fwd(q[..., :32].contiguous(), k[..., :32].contiguous(), v[..., :32].contiguous())
+    with pytest.raises(bnd.FaError):
+        fa.fwd(q[:, :1].expand(1, 3, 100, 64).contiguous(), k, v)  # 3 query heads over 2 K/V heads
