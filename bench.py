@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention forward on one MI355X.
+
+One step = one fa_fwd launch over the whole batch of the workload (every step of
+the hot path: work decomposition, K/V streaming, Q K^T, masked online softmax,
+P V, epilogue with O and LSE). Inputs are seeded synthetic data already resident
+in HBM when the timed region starts. Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--calibrate-copy] [--sweep]
+
+--sweep additionally prints one line per workload (for tables; not the bench line).
+--calibrate-copy runs, after the timed region, one elementwise copy kernel of a known
+size, used to scale the FETCH_SIZE / WRITE_SIZE hardware counters into bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MFMA peak, 1 GPU"
+DEFAULT_WORKLOAD = "gqa_causal_b4_hq32_hkv8_n8192_d128_bf16"
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, fp16 / bf16
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_hbm_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_114_amd", "csrc", f)
+                  for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+
+    None when no summary exists for this workload or when the kernel sources changed
+    since the counters were taken (their hash is recorded with them).
+    """
+    try:
+        with open(COUNTERS_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get("workloads", {}).get(workload)
+    if not entry or data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def to_device(bits, dtype_name, dev):
+    import numpy as np
+    import torch
+
+    tdt = torch.float16 if dtype_name == "f16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+
+
+def algorithmic_bytes(w) -> float:
+    """Unique HBM bytes of one launch: Q, K, V read once, O (fp32) and LSE written once."""
+    q = w.B * w.Hq * w.N * w.d * 2
+    kv = 2 * w.B * w.Hkv * w.N * w.d * 2
+    o = w.B * w.Hq * w.N * w.d * 4
+    lse = w.B * w.Hq * w.N * 4
+    return float(q + kv + o + lse)
+
+
+def time_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import exact_attention_114_amd as fa
+    from exact_attention_114_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    qkv = I.workload_qkv(w)
+    q, k, v = (to_device(x, w.dtype, dev) for x in (qkv.q, qkv.k, qkv.v))
+    del qkv
+    out = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=out, lse=lse, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
+    return wall, ev_ms / steps
+
+
+def calibrate_copy():
+    """One elementwise copy of a known size (256 MiB read + 256 MiB written) for counter scaling."""
+    import torch
+
+    n = 64 * 1024 * 1024
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    return n * 4
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the workload, timed on the host cores.
+
+    Units of 1024 query rows of one (batch, head) run on a process pool (one BLAS thread per
+    process), batch element by batch element and head by head, in chunks of 2 units per core,
+    until ``budget_s`` seconds have elapsed or the whole workload is done.
+    """
+    import numpy as np
+
+    from exact_attention_114_amd import inputs as I
+    from oracle.pool import attention_rows_pool, available_cores
+
+    qkv = I.workload_qkv(w)
+    cores = max(1, min(16, available_cores()))
+    rows_per_unit = 1024
+    chunk = 2 * cores
+    flops = 0.0
+    n_units = 0
+    elapsed = 0.0
+    for b in range(w.B):
+        q = I.bits_to_f64(qkv.q[b:b + 1], w.dtype)
+        k = I.bits_to_f64(qkv.k[b:b + 1], w.dtype)
+        v = I.bits_to_f64(qkv.v[b:b + 1], w.dtype)
+        units = [(0, h, range(r0, min(w.N, r0 + rows_per_unit))) for h in range(w.Hq)
+                 for r0 in range(0, w.N, rows_per_unit)]
+        for c0 in range(0, len(units), chunk):
+            part = units[c0:c0 + chunk]
+            t0 = time.perf_counter()
+            res = attention_rows_pool(q, k, v, I.scale_f32(w.scale), w.causal, part, cores)
+            elapsed += time.perf_counter() - t0
+            assert len(res) == len(part) and all(np.isfinite(r[3]).all() for r in res)
+            for (_, _, rows) in part:
+                r = np.arange(rows.start, rows.stop, dtype=np.float64)
+                keys = (r + 1.0) if w.causal else np.full_like(r, float(w.N))
+                flops += 4.0 * w.d * keys.sum()
+            n_units += len(part)
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    total_units = w.B * w.Hq * ((w.N + rows_per_unit - 1) // rows_per_unit)
+    sample = (f"{n_units} of {total_units} units (1024 query rows of one head each, in batch/head order): "
+              f"{flops / 1e9:.1f} GFLOP (causal-halved count) in {elapsed:.1f} s on a {cores}-process pool")
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each (batch, head) unit is independent, so the path would shard across GPUs without communication). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_attention_114_amd import binding
+    from exact_attention_114_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load_library()  # fails loudly if the HIP library is missing
+
+    w = I.WORKLOADS[args.workload]
+    if args.sweep:
+        for name in I.WORKLOADS:
+            wk = I.WORKLOADS[name]
+            steps = max(5, min(200, int(2e13 / wk.flops)))
+            _, ms = time_gpu(wk, steps, 3)
+            tf = wk.flops / (ms * 1e-3) / 1e12
+            print(json.dumps({"sweep": name, "ms": round(ms, 5), "tflops": round(tf, 2),
+                              "pct_peak": round(100 * tf / PEAK_TFLOPS[wk.dtype], 2)}), flush=True)
+
+    torch.cuda.synchronize()
+    wall, ms_launch = time_gpu(w, args.steps, args.warmup)
+    flops = w.flops
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    if args.calibrate_copy:
+        calibrate_copy()
+    bm, bn, grid = binding.tile(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal,
+                                binding.FA_F16 if w.dtype == "f16" else binding.FA_BF16)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), K x2; PCG64 seed %d)" % w.seed if w.k_mult != 1.0
+        else "synthetic (seeded N(0,1); PCG64 seed %d)" % w.seed,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "in_dtype": w.dtype, "out_dtype": "f32", "scale": w.scale,
+                   "block_m": bm, "block_n": bn, "grid": grid, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
+                     "algorithmic_hbm_bytes": algorithmic_bytes(w),
+                     "kernel_ms": round(ms_launch, 5)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -36,6 +36,15 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs:
         print(errs, file=sys.stderr)
+    # A kernel whose host stub was not emitted leaves an undefined symbol behind: refuse a
+    # library that the dynamic loader cannot resolve.
+    import ctypes
+
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {e}") from None
     os.replace(tmp, OUTPUT)
     return OUTPUT
 

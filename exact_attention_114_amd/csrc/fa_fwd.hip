@@ -9,7 +9,6 @@
 
 #include <cmath>
 #include <cstdint>
-#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernel.hpp"
@@ -24,18 +23,9 @@ constexpr int kBlockM = 32 * kWaves;
 
 template <bool BF16, int D, bool CAUSAL, bool OUT_F32>
 fa_status launch(const fa::Params& p, hipStream_t stream) {
+  // The K/V double buffer is static LDS inside the kernel (4 tiles of 64 x d values).
   auto kern = fa::fa_fwd_kernel<BF16, D, CAUSAL, OUT_F32, kWaves>;
-  constexpr size_t lds = 2 * 2 * fa::kBN * D * 2;  // double-buffered K and V tiles
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  });
-  if (attr_err != hipSuccess) {
-    g_last_hip_error = (int)attr_err;
-    return FA_ERR_HIP;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;

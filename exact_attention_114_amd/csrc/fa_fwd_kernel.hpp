@@ -34,9 +34,8 @@
 //      (gfx950's transposing LDS read), so V is never transposed in memory.
 //      The row sum l is accumulated in fp32 from the unrounded exponentials.
 //   5. Causal (intelliparadigm page, section 1.3: skip the masked half): tiles
-//      past a work-group's last row are never loaded, tiles past a wave's last
-//      row are skipped by that wave, and only tiles straddling the diagonal
-//      (or the ragged end of the sequence) are masked.
+//      past a work-group's last row are never loaded or computed, and only tiles
+//      straddling the diagonal (or the ragged end of the sequence) are masked.
 // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l), stored with one lane per row.
 #pragma once
 
@@ -134,26 +133,42 @@ __device__ inline float wave_half_sum(float x) {
   return lo + hi;
 }
 
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
 template <bool BF16, int D, bool CAUSAL, bool OUT_F32, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
   constexpr int BM = 32 * NW;
   constexpr int BN = kBN;
-  constexpr int KCH = D / 8;                   // 16-byte chunks per row
-  constexpr int ROWB = D * 2;                  // bytes per row
-  constexpr int TILE_BYTES = BN * ROWB;        // one K or one V tile
-  constexpr int NKS = D / 16;                  // MFMA k-steps of Q K^T
-  constexpr int NDB = D / 32;                  // MFMA d-blocks of P V
+  constexpr int KCH = D / 8;             // 16-byte chunks per row
+  constexpr int ROWB = D * 2;            // bytes per row
+  constexpr int TILE_BYTES = BN * ROWB;  // one K or one V tile
+  constexpr int NKS = D / 16;            // MFMA k-steps of Q K^T
+  constexpr int NDB = D / 32;            // MFMA d-blocks of P V
+  constexpr int NLD = KCH / NW;          // 1 KiB tile-load instructions per wave per matrix
   static_assert(KCH % NW == 0, "each wave issues the same number of tile loads");
 
-  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
-  lds_char* const smem = (lds_char*)smem_raw;  // [buf][K tile | V tile]
+  // Two K/V buffers as four separate arrays: the compiler can then prove that the prefetch
+  // into one buffer never aliases the reads of the other, and does not stall on it.
+  __shared__ __attribute__((aligned(1024))) char sK0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[TILE_BYTES];
+  lds_char* const K0 = (lds_char*)sK0;
+  lds_char* const V0 = (lds_char*)sV0;
+  lds_char* const K1 = (lds_char*)sK1;
+  lds_char* const V1 = (lds_char*)sV1;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5;   // which half of the wave
+  const int h = lane >> 5;  // which half of the wave
   const int l32 = lane & 31;
+  const int i16 = lane & 15;
+  const int dh = (lane >> 4) & 1;
 
   // ---- work decomposition: XCD-aware remap, then (b, hkv) groups, longest Q-tiles first ----
   // Work-group i is dispatched to XCD i % 8. Logical work L is laid out so each XCD gets a
@@ -177,8 +192,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
 
   using T = unsigned short;
   const T* __restrict__ Qp = (const T*)p.q + ((int64_t)(b * p.Hq + hq)) * N * D;
-  const T* __restrict__ Kp = (const T*)p.k + ((int64_t)bk) * N * D;
-  const T* __restrict__ Vp = (const T*)p.v + ((int64_t)bk) * N * D;
+  const char* __restrict__ Kp = (const char*)((const T*)p.k + ((int64_t)bk) * N * D);
+  const char* __restrict__ Vp = (const char*)((const T*)p.v + ((int64_t)bk) * N * D);
 
   const int q0 = t * BM;
   const int q0w = q0 + wave * 32;
@@ -186,25 +201,53 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;
 
-  // ---- K/V tile j -> LDS buffer `buf` (direct global->LDS, 1 KiB per wave instruction) ------
-  auto load_tile = [&](int j, int buf) {
-    lds_char* kd = smem + buf * (2 * TILE_BYTES);
-    lds_char* vd = kd + TILE_BYTES;
+  // ---- per-lane tile-load offsets: instruction ii of this wave fills LDS bytes
+  // [ii*1024, ii*1024 + 1024) of a tile; lane l writes physical chunk ii*64 + l, which holds
+  // logical chunk (pch ^ swizzle(row)) of tile row `row`.
+  int ld_row[NLD], ld_koff[NLD], ld_voff[NLD];
 #pragma unroll
-    for (int ii0 = 0; ii0 < KCH; ii0 += NW) {
-      const int ii = ii0 + wave;  // instruction index: LDS bytes [ii*1024, ii*1024+1024)
-      const int c_lin = ii * 64 + lane;  // physical chunk index within the tile
-      const int row = c_lin / KCH;
-      const int pch = c_lin % KCH;
-      const int grow = min(j * BN + row, N - 1);  // clamp: rows past N are masked scores
-      const char* ksrc = (const char*)(Kp + (int64_t)grow * D) + ((pch ^ swz_k<D>(row)) << 4);
-      const char* vsrc = (const char*)(Vp + (int64_t)grow * D) + ((pch ^ swz_v<D>(row)) << 4);
-      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)(kd + ii * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(vd + ii * 1024), 16, 0, 0);
+  for (int n = 0; n < NLD; ++n) {
+    const int ii = n * NW + wave;
+    const int c_lin = ii * 64 + lane;
+    const int row = c_lin / KCH, pch = c_lin % KCH;
+    ld_row[n] = row;
+    ld_koff[n] = (pch ^ swz_k<D>(row)) << 4;
+    ld_voff[n] = (pch ^ swz_v<D>(row)) << 4;
+  }
+  auto load_tile = [&](int j, lds_char* kdst, lds_char* vdst) {
+    const int jrow = j * BN;
+    const bool full = jrow + BN <= N;  // uniform: only the ragged last tile clamps rows
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int ii = n * NW + wave;
+      const int grow = full ? jrow + ld_row[n] : min(jrow + ld_row[n], N - 1);
+      const int gbase = grow * ROWB;
+      // (the sources go through named locals: passed as expressions, the host compilation
+      // silently drops the kernel stub)
+      const char* ksrc = Kp + gbase + ld_koff[n];
+      const char* vsrc = Vp + gbase + ld_voff[n];
+      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)(kdst + ii * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(vdst + ii * 1024), 16, 0, 0);
     }
   };
 
-  load_tile(0, 0);
+  // ---- per-lane LDS read offsets, loop invariant
+  // K (A operand of S^T = K Q^T): row 32kb + l32 (kb adds an immediate), logical chunk 2ks + h.
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + h) ^ swz_k<D>(l32)) << 4);
+  // V^T via transposing reads: lane reads row 16t + 8u + 4h + i16/4 (t, u add immediates),
+  // columns 32db + 16dh + 4(i16%4) .. +3.
+  int voff[NDB];
+  {
+    const int vrow = 4 * h + (i16 >> 2);
+    const int sv = swz_v<D>(vrow);  // equals the swizzle of every row 16t + 8u + vrow
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      voff[db] = vrow * ROWB + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ sv) << 4) + ((i16 & 1) << 3);
+  }
+
+  load_tile(0, K0, V0);
 
   // ---- Q tile -> registers as the MFMA B operand (Q^T): lane l: query l%32, d = 16ks + 8h + 0..7
   u32x4 qreg[NKS];
@@ -225,110 +268,101 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int j = 0; j < nt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nt) load_tile(j + 1, buf ^ 1);
+  auto iter = [&](const int j, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const lds_char* kd = BUF ? K1 : K0;
+    const lds_char* vd = BUF ? V1 : V0;
+    if (j + 1 < nt) load_tile(j + 1, BUF ? K0 : K1, BUF ? V0 : V1);
 
     const int kbase = j * BN;
-    const bool active = !CAUSAL || kbase <= q0w + 31;  // this wave has a visible key in the tile
-    if (active) {
-      const lds_char* kd = smem + buf * (2 * TILE_BYTES);
-      const lds_char* vd = kd + TILE_BYTES;
-
-      // ---- S^T = K Q^T for two 32-key blocks
-      f32x16 s[2];
+    // ---- S^T = K Q^T for two 32-key blocks
+    f32x16 s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-        const int row = 32 * kb + l32;
-        const lds_char* rp = kd + row * ROWB;
-        const int sw = swz_k<D>(row);
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16){};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4 a = *(const lds_u32x4*)(rp + (((2 * ks + h) ^ sw) << 4));
-          s[kb] = E::mfma(a, qreg[ks], s[kb]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 a = *(const lds_u32x4*)(kd + 32 * kb * ROWB + koff[ks]);
+        s[kb] = E::mfma(a, qreg[ks], s[kb]);
       }
+    }
 
-      // ---- mask: keys after the query (causal) or past the sequence end
-      const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            const bool hide = (CAUSAL && key > qrow) || key >= N;
-            s[kb][i] = hide ? -__builtin_inff() : s[kb][i];
-          }
-      }
-
-      // ---- online softmax: row max over the tile (in-lane, then across the two halves)
-      float mx = s[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-      mx = wave_half_max(mx);
-      const float mt = mx * c;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
-        m_run = m_new;
-      }
-
-      // ---- P = 2^(S*c - m): fp32 for the row sum (the LSE needs it unrounded), packed to the
-      // input type (round to nearest even) as the B operand of P V, one u32x4 per 16-key step
-      u32x4 pk[4];
-      float rs[16];  // pairwise partial row sums
+    // ---- mask: keys after the query (causal) or past the sequence end
+    const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int i = 8 * hf + 2 * w;
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_run));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_run));
-            pk[2 * kb + hf][w] = E::pack2(e0, e1);
-            rs[8 * kb + 4 * hf + w] = e0 + e1;
-          }
-#pragma unroll
-      for (int n = 8; n >= 1; n >>= 1)
-#pragma unroll
-        for (int i = 0; i < n; ++i) rs[i] += rs[i + n];
-      l_run += rs[0];
-
-      // ---- O^T += V^T P^T: A = V^T via transposing LDS reads
-      // lane l (within its 16-lane block: i = l%16) reads row 16t + 8u + 4h + i/4,
-      // columns 32db + 16*((l/16)%2) + 4*(i%4) .. +3; the read hands it V^T[d][keys].
-      const int i16 = lane & 15;
-      const int dh = (lane >> 4) & 1;
-#pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          u32x4 a;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int row = 16 * t2 + 8 * u + 4 * h + (i16 >> 2);
-            const int lch = 4 * db + 2 * dh + ((i16 & 3) >> 1);
-            const lds_char* ap = vd + row * ROWB + ((lch ^ swz_v<D>(row)) << 4) + ((i16 & 1) << 3);
-            const i16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ap);
-            const u32x2 v2 = __builtin_bit_cast(u32x2, v4);
-            a[2 * u] = v2[0];
-            a[2 * u + 1] = v2[1];
-          }
-          acc_o[db] = E::mfma(a, pk[t2], acc_o[db]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+          const bool hide = (CAUSAL && key > qrow) || key >= N;
+          s[kb][i] = hide ? -__builtin_inff() : s[kb][i];
         }
+    }
+
+    // ---- online softmax: row max over the tile (in-lane, then across the two halves)
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = wave_half_max(mx);
+    const float mt = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      m_run = m_new;
+    }
+
+    // ---- P = 2^(S*c - m): fp32 for the row sum (the LSE needs it unrounded), packed to the
+    // input type (round to nearest even) as the B operand of P V, one u32x4 per 16-key step
+    u32x4 pk[4];
+    float rs[16];  // pairwise partial row sums
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int i = 8 * hf + 2 * w;
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_run));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_run));
+          pk[2 * kb + hf][w] = E::pack2(e0, e1);
+          rs[8 * kb + 4 * hf + w] = e0 + e1;
+        }
+#pragma unroll
+    for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+      for (int i = 0; i < n; ++i) rs[i] += rs[i + n];
+    l_run += rs[0];
+
+    // ---- O^T += V^T P^T: A = V^T through transposing LDS reads (two per operand)
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        u32x4 a;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const lds_char* ap = vd + (16 * t2 + 8 * u) * ROWB + voff[db];
+          const u32x2 v2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ap));
+          a[2 * u] = v2[0];
+          a[2 * u + 1] = v2[1];
+        }
+        acc_o[db] = E::mfma(a, pk[t2], acc_o[db]);
       }
     }
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  for (int j = 0; j < nt; j += 2) {
+    iter(j, IC<0>{});
+    if (j + 1 < nt) iter(j + 1, IC<1>{});
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
