@@ -12,6 +12,13 @@ in HBM when the timed region starts. Prints ONE JSON line.
 --sweep additionally prints one line per workload (for tables; not the bench line).
 --calibrate-copy runs, after the timed region, one elementwise copy kernel of a known
 size, used to scale the FETCH_SIZE / WRITE_SIZE hardware counters into bytes.
+
+  python bench.py --summarize-counters FETCH_CSV WRITE_CSV --workload NAME --command CMD
+
+reads the rocprofv3 counter collections of two such runs (one with FETCH_SIZE, one with
+WRITE_SIZE) and records the attention kernel's HBM bytes per launch, scaled by what the
+same counters read for the copy kernel (the last dispatch of each run), in
+profiles/fa_fwd_hbm_counters.json, stamped with the hash of the kernel sources.
 """
 from __future__ import annotations
 
@@ -107,11 +114,14 @@ def time_gpu(w, steps: int, warmup: int):
     return wall, ev_ms / steps
 
 
+COPY_BYTES = 64 * 1024 * 1024 * 4  # the calibration copy reads and writes this many bytes
+
+
 def calibrate_copy():
     """One elementwise copy of a known size (256 MiB read + 256 MiB written) for counter scaling."""
     import torch
 
-    n = 64 * 1024 * 1024
+    n = COPY_BYTES // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(x)
     torch.cuda.synchronize()
@@ -167,6 +177,47 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "sample": sample}
 
 
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:
+    """HBM bytes per launch of the attention kernel from two rocprofv3 --pmc collections.
+
+    FETCH_SIZE and WRITE_SIZE are in KiB per dispatch. Each is scaled by the ratio of the
+    copy kernel's known bytes to what the same counter reads for it (the copy is the last
+    dispatch of the run), so a counter that misses part of the traffic is corrected.
+    """
+    import csv
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        fa = [float(r["Counter_Value"]) for r in rows if "fa_fwd_kernel" in r["Kernel_Name"]]
+        copy_kib = float(rows[-1]["Counter_Value"])
+        return fa, copy_kib
+
+    fetch, fetch_copy = read(fetch_csv, "FETCH_SIZE")
+    write, write_copy = read(write_csv, "WRITE_SIZE")
+    fetch_scale = COPY_BYTES / (fetch_copy * 1024.0)
+    write_scale = COPY_BYTES / (write_copy * 1024.0)
+    fetch_kib = sum(fetch) / len(fetch)
+    write_kib = sum(write) / len(write)
+    entry = {"fetch_kib": round(fetch_kib, 3), "write_kib": round(write_kib, 3),
+             "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5),
+             "dispatches": [len(fetch), len(write)],
+             "hbm_bytes_per_launch": round(fetch_kib * 1024.0 * fetch_scale + write_kib * 1024.0 * write_scale),
+             "command": command}
+    try:
+        with open(COUNTERS_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        data = {"kernel_source_hash": kernel_source_hash(), "workloads": {}}
+    data["workloads"][workload] = entry
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+    return entry
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,7 +227,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--command", default="")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters, args.workload, args.command)))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

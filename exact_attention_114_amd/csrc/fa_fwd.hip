@@ -74,12 +74,12 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int64_t Hkv, int64_t N, int64_t d, float scale, int causal, fa_dtype in_dtype,
                  fa_dtype out_dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   int64_t nq = 0, grid = 0;
   const fa_status st = check_problem(B, Hq, Hkv, N, d, in_dtype, &nq, &grid);
   if (st != FA_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
   if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
-  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
 
   fa::Params p;

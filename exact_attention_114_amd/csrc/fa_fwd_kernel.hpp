@@ -8,12 +8,14 @@
 //
 // Per K/V tile of BN = 64 keys (intelliparadigm page, sections 1.2.1-1.2.2 and
 // 2.4: load a block, Q K^T, scale, online-softmax update, P V, accumulate):
-//   1. K and V tiles stream from HBM straight into LDS with gfx950's
-//      global_load_lds_dwordx4 (no VGPR staging), double-buffered so tile j+1
-//      loads while tile j computes (intelliparadigm page, section 3.1, double
-//      buffering). Rows are XOR-swizzled in 16-byte chunks so every LDS read
-//      below is bank-conflict free (section 3.1's goal; the printed padding
-//      formula is not used: a swizzle wastes no LDS).
+//   1. K and V tiles stream from HBM straight into LDS with buffer loads in LDS-DMA
+//      form (no VGPR staging), double-buffered so later tiles load while the
+//      current ones compute (intelliparadigm page, section 3.1, double
+//      buffering). Each tile gets its own buffer descriptor (base at the tile,
+//      size up to the sequence end), so the per-lane offsets never change and
+//      rows past the end read as zero. Rows are XOR-swizzled in 16-byte chunks
+//      so every LDS read below is bank-conflict free (section 3.1's goal; the
+//      printed padding formula is not used: a swizzle wastes no LDS).
 //   2. S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: A = K from LDS
 //      (ds_read_b128), B = Q^T held in VGPRs for the whole sweep (Q is read
 //      once, the FA2 point). Computing S^T rather than S puts one query per
@@ -36,6 +38,13 @@
 //   5. Causal (intelliparadigm page, section 1.3: skip the masked half): tiles
 //      past a work-group's last row are never loaded or computed, and only tiles
 //      straddling the diagonal (or the ragged end of the sequence) are masked.
+//
+// Software pipeline. A wave's softmax is VALU work and its two products are MFMA
+// work; on gfx950 an MFMA leaves the issue port free for about four VALU
+// instructions of the same wave while it runs. So iteration j exponentiates S_j
+// while the MFMAs of the neighbouring tiles run: S_{j+1} = K_{j+1} Q^T and
+// O += P_{j-1} V_{j-1}. K runs two tiles ahead of V in LDS: iteration j reads
+// K_{j+1} and V_{j-1} and loads K_{j+2} and V_j into the buffers it frees.
 // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l), stored with one lane per row.
 #pragma once
 
@@ -57,9 +66,12 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBN = 64;             // keys per inner tile
+constexpr int kBN = 64;                // keys per inner tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the row max may grow before rescaling
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
 
 struct Params {
   const void* q;
@@ -79,7 +91,6 @@ template <bool BF16>
 struct Elt;
 template <>
 struct Elt<false> {
-  using x8 = f16x8;
   static __device__ inline unsigned pack2(float a, float b) {
     return __builtin_bit_cast(unsigned, (f16x2){(_Float16)a, (_Float16)b});  // v_cvt_pk_f16_f32 (RNE)
   }
@@ -89,7 +100,6 @@ struct Elt<false> {
 };
 template <>
 struct Elt<true> {
-  using x8 = bf16x8;
   static __device__ inline unsigned pack2(float a, float b) {
     return __builtin_bit_cast(unsigned, (bf16x2){(__bf16)a, (__bf16)b});  // v_cvt_pk_bf16_f32 (RNE)
   }
@@ -133,6 +143,18 @@ __device__ inline float wave_half_sum(float x) {
   return lo + hi;
 }
 
+// An empty asm that claims to read and rewrite x: the value must exist at this point of the
+// program, so the compiler cannot sink its computation past it. (Inline asm with VGPR
+// operands lives in __device__ helpers: in a kernel body the host pass rejects the
+// constraint and silently drops the kernel's host stub.)
+__device__ inline void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+__device__ inline float max8(const f32x16& v, int o) {
+  return fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3])),
+               fmaxf(fmaxf(v[o + 4], v[o + 5]), fmaxf(v[o + 6], v[o + 7])));
+}
+
 template <int N>
 struct IC {
   static constexpr int value = N;
@@ -152,8 +174,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
   constexpr int NLD = KCH / NW;          // 1 KiB tile-load instructions per wave per matrix
   static_assert(KCH % NW == 0, "each wave issues the same number of tile loads");
 
-  // Two K/V buffers as four separate arrays: the compiler can then prove that the prefetch
-  // into one buffer never aliases the reads of the other, and does not stall on it.
+  // Two K and two V buffers as four separate arrays: the compiler can then prove that a
+  // prefetch into one buffer never aliases the reads of another, and does not stall on it.
   __shared__ __attribute__((aligned(1024))) char sK0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sK1[TILE_BYTES];
@@ -195,41 +217,38 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
   const char* __restrict__ Kp = (const char*)((const T*)p.k + ((int64_t)bk) * N * D);
   const char* __restrict__ Vp = (const char*)((const T*)p.v + ((int64_t)bk) * N * D);
 
-  const int q0 = t * BM;
-  const int q0w = q0 + wave * 32;
-  const int qrow = q0w + l32;  // this lane's query row
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kv_end + BN - 1) / BN;
-
-  // ---- per-lane tile-load offsets: instruction ii of this wave fills LDS bytes
-  // [ii*1024, ii*1024 + 1024) of a tile; lane l writes physical chunk ii*64 + l, which holds
-  // logical chunk (pch ^ swizzle(row)) of tile row `row`.
-  int ld_row[NLD], ld_koff[NLD], ld_voff[NLD];
+  // ---- tile loads: instruction n of this wave fills LDS bytes [ii*1024, ii*1024 + 1024) of a
+  // tile (ii = n*NW + wave); lane l writes physical chunk ii*64 + l, which holds logical chunk
+  // (pch ^ swizzle(row)) of tile row `row`. The byte offsets within the tile are loop invariant.
+  int ld_koff[NLD], ld_voff[NLD];
 #pragma unroll
   for (int n = 0; n < NLD; ++n) {
     const int ii = n * NW + wave;
     const int c_lin = ii * 64 + lane;
     const int row = c_lin / KCH, pch = c_lin % KCH;
-    ld_row[n] = row;
-    ld_koff[n] = (pch ^ swz_k<D>(row)) << 4;
-    ld_voff[n] = (pch ^ swz_v<D>(row)) << 4;
+    ld_koff[n] = row * ROWB + ((pch ^ swz_k<D>(row)) << 4);
+    ld_voff[n] = row * ROWB + ((pch ^ swz_v<D>(row)) << 4);
   }
-  auto load_tile = [&](int j, lds_char* kdst, lds_char* vdst) {
+  // One descriptor per tile: base at the tile's first row, size up to the sequence end, so
+  // rows past N (ragged last tile, or a prefetch past the end) read as zero.
+  auto tile_rsrc = [&](const char* base, int j) {
     const int jrow = j * BN;
-    const bool full = jrow + BN <= N;  // uniform: only the ragged last tile clamps rows
+    const int bytes = max(0, N - jrow) * ROWB;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)jrow * ROWB), (short)0, bytes, kBufferWord3);
+  };
+  // (The builtin's pointer and offset go through named locals: given as expressions, the host
+  // compilation silently drops the kernel's host stub.)
+  auto load_tile = [&](const char* base, int j, lds_char* dst, const int (&offs)[NLD]) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, j);
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-      const int ii = n * NW + wave;
-      const int grow = full ? jrow + ld_row[n] : min(jrow + ld_row[n], N - 1);
-      const int gbase = grow * ROWB;
-      // (the sources go through named locals: passed as expressions, the host compilation
-      // silently drops the kernel stub)
-      const char* ksrc = Kp + gbase + ld_koff[n];
-      const char* vsrc = Vp + gbase + ld_voff[n];
-      __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)(kdst + ii * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(vdst + ii * 1024), 16, 0, 0);
+      lds_void* ldst = (lds_void*)(dst + (n * NW + wave) * 1024);
+      const int voffs = offs[n];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ldst, 16, voffs, 0, 0, 0);
     }
   };
+  auto load_k = [&](int j, lds_char* dst) { load_tile(Kp, j, dst, ld_koff); };
+  auto load_v = [&](int j, lds_char* dst) { load_tile(Vp, j, dst, ld_voff); };
 
   // ---- per-lane LDS read offsets, loop invariant
   // K (A operand of S^T = K Q^T): row 32kb + l32 (kb adds an immediate), logical chunk 2ks + h.
@@ -247,144 +266,258 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
       voff[db] = vrow * ROWB + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ sv) << 4) + ((i16 & 1) << 3);
   }
 
-  load_tile(0, K0, V0);
-
-  // ---- Q tile -> registers as the MFMA B operand (Q^T): lane l: query l%32, d = 16ks + 8h + 0..7
-  u32x4 qreg[NKS];
-  {
-    const int qr = min(qrow, N - 1);
-    const u32x4* src = (const u32x4*)(Qp + (int64_t)qr * D + 8 * h);
+  // A ragged sequence end leaves tile rows that no load writes (if out-of-range lanes skip
+  // the LDS write) or writes as zero: clear the buffers once so they never hold stale bits
+  // that could be non-finite.
+  if (N % BN != 0) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = src[2 * ks];
+    for (int n = 0; n < TILE_BYTES / (NW * 64 * 16); ++n) {
+      const int off = (n * NW * 64 + (int)threadIdx.x) * 16;
+      *(lds_u32x4*)(K0 + off) = z;
+      *(lds_u32x4*)(K1 + off) = z;
+      *(lds_u32x4*)(V0 + off) = z;
+      *(lds_u32x4*)(V1 + off) = z;
+    }
+    __syncthreads();
   }
 
-  f32x16 acc_o[NDB];
+  // MFMA operands from LDS. K (A operand of S^T = K Q^T): block kb of 32 keys, k-step ks.
+  auto k_operand = [&](const lds_char* kd, int kb, int ks) -> u32x4 {
+    return *(const lds_u32x4*)(kd + 32 * kb * ROWB + koff[ks]);
+  };
+  // V^T (A operand of O^T += V^T P^T) for 16-key step t2 and d-block db: two transposing reads.
+  auto v_operand = [&](const lds_char* vd, int t2, int db) -> u32x4 {
+    u32x4 a;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
-  float m_run = -__builtin_inff();  // reference max (scaled, log2 units) shared by both halves
-  float l_run = 0.f;                // this lane's partial row sum (its 16 keys of each block)
-  const float c = p.c;
-
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  auto iter = [&](const int j, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    const lds_char* kd = BUF ? K1 : K0;
-    const lds_char* vd = BUF ? V1 : V0;
-    if (j + 1 < nt) load_tile(j + 1, BUF ? K0 : K1, BUF ? V0 : V1);
-
-    const int kbase = j * BN;
-    // ---- S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (f32x16){};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 a = *(const lds_u32x4*)(kd + 32 * kb * ROWB + koff[ks]);
-        s[kb] = E::mfma(a, qreg[ks], s[kb]);
-      }
+    for (int uu = 0; uu < 2; ++uu) {
+      const lds_char* ap = vd + (16 * t2 + 8 * uu) * ROWB + voff[db];
+      const u32x2 v2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ap));
+      a[2 * uu] = v2[0];
+      a[2 * uu + 1] = v2[1];
     }
-
-    // ---- mask: keys after the query (causal) or past the sequence end
-    const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          const bool hide = (CAUSAL && key > qrow) || key >= N;
-          s[kb][i] = hide ? -__builtin_inff() : s[kb][i];
-        }
-    }
-
-    // ---- online softmax: row max over the tile (in-lane, then across the two halves)
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = wave_half_max(mx);
-    const float mt = mx * c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
-      m_run = m_new;
-    }
-
-    // ---- P = 2^(S*c - m): fp32 for the row sum (the LSE needs it unrounded), packed to the
-    // input type (round to nearest even) as the B operand of P V, one u32x4 per 16-key step
-    u32x4 pk[4];
-    float rs[16];  // pairwise partial row sums
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int i = 8 * hf + 2 * w;
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_run));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_run));
-          pk[2 * kb + hf][w] = E::pack2(e0, e1);
-          rs[8 * kb + 4 * hf + w] = e0 + e1;
-        }
-#pragma unroll
-    for (int n = 8; n >= 1; n >>= 1)
-#pragma unroll
-      for (int i = 0; i < n; ++i) rs[i] += rs[i + n];
-    l_run += rs[0];
-
-    // ---- O^T += V^T P^T: A = V^T through transposing LDS reads (two per operand)
-#pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x4 a;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const lds_char* ap = vd + (16 * t2 + 8 * u) * ROWB + voff[db];
-          const u32x2 v2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ap));
-          a[2 * u] = v2[0];
-          a[2 * u + 1] = v2[1];
-        }
-        acc_o[db] = E::mfma(a, pk[t2], acc_o[db]);
-      }
-    }
-
+    return a;
+  };
+  auto sync_tiles = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
+  const float c = p.c;
 
-  for (int j = 0; j < nt; j += 2) {
-    iter(j, IC<0>{});
-    if (j + 1 < nt) iter(j + 1, IC<1>{});
-  }
+  // ---- the Q-tile: rows [t*BM, t*BM + BM) of head (b, hq) against its visible K/V tiles
+  {
+    const int q0 = t * BM;
+    const int q0w = q0 + wave * 32;
+    const int qrow = q0w + l32;  // this lane's query row
+    const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+    const int nt = (kv_end + BN - 1) / BN;
 
-  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
-  const float l_tot = wave_half_sum(l_run);
-  if (qrow < N) {
-    const float inv = 1.0f / l_tot;
-    const int64_t obase = ((int64_t)(b * p.Hq + hq) * N + qrow) * D;
+    // ---- prologue: K_0, K_1 into LDS; Q tile -> registers as the MFMA B operand (Q^T):
+    // lane l: query l%32, d = 16ks + 8h + 0..7
+    load_k(0, K0);
+    load_k(1, K1);
+    u32x4 qreg[NKS];
+    {
+      const int qr = min(qrow, N - 1);
+      const u32x4* src = (const u32x4*)(Qp + (int64_t)qr * D + 8 * h);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int ks = 0; ks < NKS; ++ks) qreg[ks] = src[2 * ks];
+    }
+
+    f32x16 acc_o[NDB];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dcol = 32 * db + 8 * g4 + 4 * h;
-        const float o0 = acc_o[db][4 * g4 + 0] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
-        const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
-        if (OUT_F32) {
-          *(f32x4*)((float*)p.o + obase + dcol) = (f32x4){o0, o1, o2, o3};
-        } else {
-          *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){E::pack2(o0, o1), E::pack2(o2, o3)};
-        }
+    for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
+    float m_run = -__builtin_inff();  // reference max (scaled, log2 units), one per row
+    float l_run = 0.f;                // this lane's partial row sum (its 16 keys of each block)
+
+    // S^T for the two 32-key blocks of one tile (used outside the pipelined steps)
+    auto s_tile = [&](const lds_char* kd, f32x16 (&s)[2]) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) s[kb] = E::mfma(k_operand(kd, kb, ks), qreg[ks], s[kb]);
       }
-    if (h == 0) p.lse[(int64_t)(b * p.Hq + hq) * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    };
+    sync_tiles();
+    f32x16 sA[2], sB[2];
+    u32x4 pA[4], pB[4];
+    s_tile(K0, sA);
+    // Every wave must be done reading K_0 before the first step refills its buffer.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // One pipeline step for tile j (PAR = j % 2): softmax of S_j (scur) into P_j (pcur), with
+    // the MFMAs of O += P_{j-1} V_{j-1} (HAS_PV) and of S_{j+1} (HAS_S) interleaved with it.
+    // The step is laid out as slots of one MFMA each; a slot also issues the LDS reads of the
+    // MFMA two slots ahead and an even share of the softmax's VALU work, and scheduling
+    // barriers keep that order, so the MFMA pipe stays fed while the VALU work issues in its
+    // shadow.
+    auto step = [&](const int j, auto par, auto has_s, auto has_pv, f32x16 (&scur)[2], f32x16 (&snext)[2],
+                    const u32x4 (&pprev)[4], u32x4 (&pcur)[4]) {
+      constexpr int PAR = decltype(par)::value;
+      constexpr bool HAS_S = decltype(has_s)::value;
+      constexpr bool HAS_PV = decltype(has_pv)::value;
+      constexpr int NPV = HAS_PV ? 4 * NDB : 0;  // MFMAs of P_{j-1} V_{j-1}
+      constexpr int NSM = HAS_S ? 2 * NKS : 0;   // MFMAs of S_{j+1}
+      constexpr int NM = NPV + NSM;
+      constexpr int NSLOT = NM > 0 ? NM : 1;
+      const lds_char* kread = PAR ? K0 : K1;  // K_{j+1}
+      const lds_char* vread = PAR ? V0 : V1;  // V_{j-1}
+      // Loads for the next step go into the buffers this step does not read: V_j where
+      // V_{j-2} was, K_{j+2} where K_j was.
+      load_v(j, PAR ? V1 : V0);
+      if (HAS_S) load_k(j + 2, PAR ? K1 : K0);
+
+      // ---- mask S_j: keys after the query (causal) or past the sequence end. In the S^T
+      // layout element i of block kb holds key kbase + 32kb + 8(i/4) + 4h + i%4: one per-lane
+      // threshold on the constant part covers both conditions.
+      const int kbase = j * BN;
+      const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
+      if (need_mask) {
+        const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;  // hide if part > lim
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int part = 32 * kb + 8 * (i >> 2) + (i & 3);
+            scur[kb][i] = part > lim ? -__builtin_inff() : scur[kb][i];
+          }
+      }
+
+      float alpha = 1.f;
+
+      // ---- the MFMA stream: P V first (its operands are ready), then S_{j+1}
+      u32x4 opnd[NM > 0 ? NM : 1];
+      auto fetch = [&](int m) {
+        if (m < NPV)
+          opnd[m] = v_operand(vread, m / NDB, m % NDB);
+        else
+          opnd[m] = k_operand(kread, (m - NPV) / NKS, (m - NPV) % NKS);
+      };
+      auto issue = [&](int m) {
+        if (m < NPV) {
+          acc_o[m % NDB] = E::mfma(opnd[m], pprev[m / NDB], acc_o[m % NDB]);
+        } else {
+          const int kb = (m - NPV) / NKS, ks = (m - NPV) % NKS;
+          snext[kb] = E::mfma(opnd[m], qreg[ks], ks == 0 ? (f32x16){} : snext[kb]);
+        }
+      };
+
+      // ---- the VALU work, as small items spread over the slots: items 0-3 are partial row
+      // maxima of 8 scores each, item 4 the wave row max and the rescale decision.
+      // Then one item per score (exponential, and for odd scores the pack and the pair sum),
+      // then the lane's total.
+      constexpr int NMAX = 5;
+      constexpr int NITEM = NMAX + 33;
+      float pm[4], ex[32], part[4], tile_sum = 0.f;
+      bool resc = false;
+      auto item = [&](int it) {
+        if (it < NMAX) {
+          if (it < 4) {
+            pm[it] = max8(scur[it >> 1], 8 * (it & 1));
+          } else {
+            const float mt = wave_half_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]))) * c;
+            // A wave-uniform decision; the per-lane updates are branch free so that the step
+            // stays one basic block (the O rescale, which is rare, runs after it).
+            resc = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0;
+            const float m_new = resc ? fmaxf(m_run, mt) : m_run;
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+          }
+        } else if (it < NMAX + 32) {
+          const int e = it - NMAX, kb = e >> 4, i = e & 15;
+          ex[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i], c, -m_run));
+          if (e & 1) {
+            const int q = (e >> 1);  // pair index: u32x4 (q / 4), word q % 4
+            unsigned w = E::pack2(ex[e - 1], ex[e]);
+            // Keep the packing in this slot: the value is only used after the step's
+            // closing branch, and the compiler would otherwise sink it out of the block.
+            pin(w);
+            pcur[q >> 2][q & 3] = w;
+            const float s2 = ex[e - 1] + ex[e];
+            part[q & 3] = q < 4 ? s2 : part[q & 3] + s2;
+          }
+        } else {
+          tile_sum = (part[0] + part[1]) + (part[2] + part[3]);
+          pin(tile_sum);
+        }
+      };
+
+      // Register reuse decides the split: the first 32-key block of S_j (items below ITEM_B) is
+      // consumed during the P V MFMAs, before the MFMAs of S_{j+1} overwrite that block, so
+      // the two tiles' first blocks can share registers. Without P V MFMAs those items run
+      // first.
+      constexpr int ITEM_B = NMAX + 16;
+      constexpr int I1 = HAS_S ? ITEM_B : NITEM;  // items of phase 1: [0, I1)
+      constexpr int S1 = HAS_S ? NPV : NSLOT;     // slots of phase 1: [0, S1)
+      if (S1 == 0) {
+#pragma unroll
+        for (int it = 0; it < I1; ++it) item(it);
+      }
+      if (NM > 0) fetch(0);
+      if (NM > 1) fetch(1);
+#pragma unroll
+      for (int sl = 0; sl < NSLOT; ++sl) {
+        if (sl + 2 < NM) fetch(sl + 2);
+        // items [lo, hi) of this slot: phase 1 spreads [0, I1) over slots [0, S1), phase 2
+        // spreads [I1, NITEM) over slots [S1, NSLOT)
+        constexpr int D1 = S1 > 0 ? S1 : 1, D2 = NSLOT - S1 > 0 ? NSLOT - S1 : 1;
+        const int lo = sl < S1 ? (sl * I1) / D1 : I1 + ((sl - S1) * (NITEM - I1)) / D2;
+        const int hi = sl < S1 ? ((sl + 1) * I1) / D1 : I1 + ((sl + 1 - S1) * (NITEM - I1)) / D2;
+#pragma unroll
+        for (int it = lo; it < hi; ++it) item(it);
+        if (sl < NM) issue(sl);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      l_run = l_run * alpha + tile_sum;
+      // The partial output P_{j-1} V_{j-1} was relative to the old reference.
+      if (HAS_PV && resc) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      }
+      sync_tiles();
+    };
+
+    // Buffers and registers alternate with j: even j uses (sA -> sB, pA), odd j (sB -> sA, pB).
+    // Every step after the first is a full one, run in pairs until step nt has added
+    // P_{nt-1} V_{nt-1}. Tiles from nt on lie wholly past the last visible key (past the Q-tile's
+    // last row when causal, else past the sequence end), so the mask hides all their scores:
+    // such a step adds exactly zero (no rescale, P = 0, zero row sum). One code path with a
+    // fixed register assignment costs at most one and a half extra steps per Q-tile.
+    const IC<0> E0;
+    const IC<1> E1;
+    const IC<true> Y;
+    const IC<false> Nn;
+    step(0, E0, Y, Nn, sA, sB, pB, pA);
+    for (int j = 1; j <= nt; j += 2) {
+      step(j, E1, Y, Y, sB, sA, pA, pB);
+      step(j + 1, E0, Y, Y, sA, sB, pB, pA);
+    }
+
+    // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
+    const float l_tot = wave_half_sum(l_run);
+    if (qrow < N) {
+      const float inv = 1.0f / l_tot;
+      const int64_t obase = ((int64_t)(b * p.Hq + hq) * N + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dcol = 32 * db + 8 * g4 + 4 * h;
+          const float o0 = acc_o[db][4 * g4 + 0] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
+          const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
+          if (OUT_F32) {
+            *(f32x4*)((float*)p.o + obase + dcol) = (f32x4){o0, o1, o2, o3};
+          } else {
+            *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){E::pack2(o0, o1), E::pack2(o2, o3)};
+          }
+        }
+      if (h == 0) p.lse[(int64_t)(b * p.Hq + hq) * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    }
   }
+
 }
 
 }  // namespace fa

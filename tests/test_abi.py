@@ -86,6 +86,7 @@ def test_alignment_is_checked_last():
 def test_tile_query():
     bm, bn, grid = bnd.tile(4, 32, 8, 8192, 128, True, bnd.FA_BF16)
     assert bn == 64 and bm % 32 == 0 and grid == 4 * 32 * ((8192 + bm - 1) // bm)
+    assert bnd.tile(4, 32, 8, 8192, 128, False, bnd.FA_BF16)[2] == grid
     bm, bn, grid = bnd.tile(1, 1, 1, 1, 64, False, bnd.FA_F16)
     assert grid == 1
     with pytest.raises(bnd.FaError):
