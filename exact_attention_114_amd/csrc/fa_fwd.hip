@@ -17,14 +17,20 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-// Waves per work-group: 4 (BM = 128 query rows); two work-groups share a CU.
+// Waves per work-group: 4, 32 query rows each, so a work-group takes BM = 128 rows.
 constexpr int kWaves = 4;
 constexpr int kBlockM = 32 * kWaves;
+// MI355X has 256 CUs. At d = 128 a step of one 32-key block needs fewer registers and half
+// the LDS of a two-block step, so three work-groups fit on a CU instead of two; that pays when
+// the grid can fill them, while a small grid does better with the longer step (fewer barriers).
+constexpr int64_t kOneBlockMinGrid = 2 * 256;
 
-template <bool BF16, int D, bool CAUSAL, bool OUT_F32>
+int key_blocks(int64_t d, int64_t grid) { return d == 128 && grid > kOneBlockMinGrid ? 1 : 2; }
+
+template <bool BF16, int D, bool CAUSAL, bool OUT_F32, int KB>
 fa_status launch(const fa::Params& p, hipStream_t stream) {
-  // The K/V double buffer is static LDS inside the kernel (4 tiles of 64 x d values).
-  auto kern = fa::fa_fwd_kernel<BF16, D, CAUSAL, OUT_F32, kWaves>;
+  // The K/V double buffer is static LDS inside the kernel (4 tiles of 32*KB x D values).
+  auto kern = fa::fa_fwd_kernel<BF16, D, CAUSAL, OUT_F32, kWaves, KB>;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -34,17 +40,25 @@ fa_status launch(const fa::Params& p, hipStream_t stream) {
   return FA_OK;
 }
 
+template <bool BF16, int D, bool CAUSAL, bool OUT_F32>
+fa_status dispatch_kb(const fa::Params& p, int kb, hipStream_t s) {
+  if constexpr (D == 128) {
+    if (kb == 1) return launch<BF16, D, CAUSAL, OUT_F32, 1>(p, s);
+  }
+  return launch<BF16, D, CAUSAL, OUT_F32, 2>(p, s);
+}
 template <bool BF16, int D, bool CAUSAL>
-fa_status dispatch_out(const fa::Params& p, bool out_f32, hipStream_t s) {
-  return out_f32 ? launch<BF16, D, CAUSAL, true>(p, s) : launch<BF16, D, CAUSAL, false>(p, s);
+fa_status dispatch_out(const fa::Params& p, bool out_f32, int kb, hipStream_t s) {
+  return out_f32 ? dispatch_kb<BF16, D, CAUSAL, true>(p, kb, s) : dispatch_kb<BF16, D, CAUSAL, false>(p, kb, s);
 }
 template <bool BF16, int D>
-fa_status dispatch_causal(const fa::Params& p, bool causal, bool out_f32, hipStream_t s) {
-  return causal ? dispatch_out<BF16, D, true>(p, out_f32, s) : dispatch_out<BF16, D, false>(p, out_f32, s);
+fa_status dispatch_causal(const fa::Params& p, bool causal, bool out_f32, int kb, hipStream_t s) {
+  return causal ? dispatch_out<BF16, D, true>(p, out_f32, kb, s) : dispatch_out<BF16, D, false>(p, out_f32, kb, s);
 }
 template <bool BF16>
-fa_status dispatch_d(const fa::Params& p, int d, bool causal, bool out_f32, hipStream_t s) {
-  return d == 64 ? dispatch_causal<BF16, 64>(p, causal, out_f32, s) : dispatch_causal<BF16, 128>(p, causal, out_f32, s);
+fa_status dispatch_d(const fa::Params& p, int d, bool causal, bool out_f32, int kb, hipStream_t s) {
+  return d == 64 ? dispatch_causal<BF16, 64>(p, causal, out_f32, kb, s)
+                 : dispatch_causal<BF16, 128>(p, causal, out_f32, kb, s);
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -99,9 +113,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
   const bool bf16 = in_dtype == FA_BF16;
   const bool out_f32 = out_dtype == FA_F32;
+  const int kb = key_blocks(d, grid);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return bf16 ? dispatch_d<true>(p, (int)d, causal != 0, out_f32, s)
-              : dispatch_d<false>(p, (int)d, causal != 0, out_f32, s);
+  return bf16 ? dispatch_d<true>(p, (int)d, causal != 0, out_f32, kb, s)
+              : dispatch_d<false>(p, (int)d, causal != 0, out_f32, kb, s);
 }
 
 fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, fa_dtype in_dtype,
@@ -112,7 +127,7 @@ fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
   const fa_status st = check_problem(B, Hq, Hkv, N, d, in_dtype, &nq, &g);
   if (st != FA_OK) return st;
   *block_m = kBlockM;
-  *block_n = fa::kBN;
+  *block_n = 32 * key_blocks(d, g);
   *grid = g;
   return FA_OK;
 }

@@ -6,7 +6,7 @@
 // sequence-dimension grid). Each wave owns 32 query rows for the whole K/V
 // sweep (the walkthrough's split of Q across warps, no inter-wave exchange).
 //
-// Per K/V tile of BN = 64 keys (intelliparadigm page, sections 1.2.1-1.2.2 and
+// Per K/V tile of BN = 32*KB keys (intelliparadigm page, sections 1.2.1-1.2.2 and
 // 2.4: load a block, Q K^T, scale, online-softmax update, P V, accumulate):
 //   1. K and V tiles stream from HBM straight into LDS with buffer loads in LDS-DMA
 //      form (no VGPR staging), double-buffered so later tiles load while the
@@ -34,7 +34,10 @@
 //      accumulator registers (packed to fp16/bf16 with round-to-nearest-even),
 //      A = V^T is read from the row-major V tile with ds_read_b64_tr_b16
 //      (gfx950's transposing LDS read), so V is never transposed in memory.
-//      The row sum l is accumulated in fp32 from the unrounded exponentials.
+//      Two row sums are kept in fp32: l of the unrounded exponentials, for the LSE, and
+//      l~ of the rounded values that enter the MFMA (one v_dot2 per packed pair), which
+//      normalises O. The weights that multiply V then sum to one, so the rounding of a
+//      dominant weight (up to 2^-8 relative in bf16) cancels rather than scaling the row.
 //   5. Causal (intelliparadigm page, section 1.3: skip the masked half): tiles
 //      past a work-group's last row are never loaded or computed, and only tiles
 //      straddling the diagonal (or the ragged end of the sequence) are masked.
@@ -45,7 +48,7 @@
 // while the MFMAs of the neighbouring tiles run: S_{j+1} = K_{j+1} Q^T and
 // O += P_{j-1} V_{j-1}. K runs two tiles ahead of V in LDS: iteration j reads
 // K_{j+1} and V_{j-1} and loads K_{j+2} and V_j into the buffers it frees.
-// Epilogue: O = acc / l, LSE = ln2 * (m + log2 l), stored with one lane per row.
+// Epilogue: O = acc / l~, LSE = ln2 * (m + log2 l), stored with one lane per row.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,7 +71,6 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBN = 64;                // keys per inner tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the row max may grow before rescaling
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
@@ -94,6 +96,11 @@ struct Elt<false> {
   static __device__ inline unsigned pack2(float a, float b) {
     return __builtin_bit_cast(unsigned, (f16x2){(_Float16)a, (_Float16)b});  // v_cvt_pk_f16_f32 (RNE)
   }
+  // acc + the two packed values, summed in fp32 (v_dot2c_f32_f16 with (1, 1))
+  static __device__ inline float sum2(unsigned w, float acc) {
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, acc, false);
+  }
   static __device__ inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
@@ -102,6 +109,11 @@ template <>
 struct Elt<true> {
   static __device__ inline unsigned pack2(float a, float b) {
     return __builtin_bit_cast(unsigned, (bf16x2){(__bf16)a, (__bf16)b});  // v_cvt_pk_bf16_f32 (RNE)
+  }
+  // acc + the two packed values, summed in fp32 (v_dot2c_f32_bf16 with (1, 1))
+  static __device__ inline float sum2(unsigned w, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
   }
   static __device__ inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -150,9 +162,12 @@ __device__ inline float wave_half_sum(float x) {
 __device__ inline void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 __device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 
+// Maximum of v[o .. o+7] as a chain the compiler folds into three v_max3_f32 and one v_max_f32.
 __device__ inline float max8(const f32x16& v, int o) {
-  return fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3])),
-               fmaxf(fmaxf(v[o + 4], v[o + 5]), fmaxf(v[o + 6], v[o + 7])));
+  float m = fmaxf(fmaxf(v[o], v[o + 1]), v[o + 2]);
+  m = fmaxf(fmaxf(m, v[o + 3]), v[o + 4]);
+  m = fmaxf(fmaxf(m, v[o + 5]), v[o + 6]);
+  return fmaxf(m, v[o + 7]);
 }
 
 template <int N>
@@ -160,19 +175,37 @@ struct IC {
   static constexpr int value = N;
 };
 
-template <bool BF16, int D, bool CAUSAL, bool OUT_F32, int NW>
+// f(IC<i>) for i = B .. E-1 with i a compile-time constant: a step's slots are expanded by
+// template recursion rather than loop unrolling, which gives up on long steps and would then
+// index register arrays at run time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Waves that share a SIMD for a tile shape: registers bound it (a d = 128 step with two key
+// blocks holds 189 VGPRs, with one 168; d = 64 about 135) and so does LDS (4 tiles of
+// 32*KB x D values per work-group).
+constexpr int waves_per_simd(int d, int kb) { return d == 128 && kb == 1 ? 3 : 2; }
+
+// One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
+// pipeline step takes KB blocks of 32 keys.
+template <bool BF16, int D, bool CAUSAL, bool OUT_F32, int NW, int KB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
   constexpr int BM = 32 * NW;
-  constexpr int BN = kBN;
+  constexpr int BN = 32 * KB;
   constexpr int KCH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;            // bytes per row
   constexpr int TILE_BYTES = BN * ROWB;  // one K or one V tile
   constexpr int NKS = D / 16;            // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;            // MFMA d-blocks of P V
-  constexpr int NLD = KCH / NW;          // 1 KiB tile-load instructions per wave per matrix
-  static_assert(KCH % NW == 0, "each wave issues the same number of tile loads");
+  constexpr int NLD = TILE_BYTES / (NW * 1024);  // 1 KiB tile-load instructions per wave per matrix
+  static_assert(NLD >= 1 && TILE_BYTES % (NW * 1024) == 0, "each wave issues the same number of tile loads");
 
   // Two K and two V buffers as four separate arrays: the compiler can then prove that a
   // prefetch into one buffer never aliases the reads of another, and does not stall on it.
@@ -219,31 +252,29 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
 
   // ---- tile loads: instruction n of this wave fills LDS bytes [ii*1024, ii*1024 + 1024) of a
   // tile (ii = n*NW + wave); lane l writes physical chunk ii*64 + l, which holds logical chunk
-  // (pch ^ swizzle(row)) of tile row `row`. The byte offsets within the tile are loop invariant.
-  int ld_koff[NLD], ld_voff[NLD];
-#pragma unroll
-  for (int n = 0; n < NLD; ++n) {
-    const int ii = n * NW + wave;
-    const int c_lin = ii * 64 + lane;
-    const int row = c_lin / KCH, pch = c_lin % KCH;
-    ld_koff[n] = row * ROWB + ((pch ^ swz_k<D>(row)) << 4);
-    ld_voff[n] = row * ROWB + ((pch ^ swz_v<D>(row)) << 4);
+  // (pch ^ swizzle(row)) of tile row `row`. Moving to the next instruction moves 64 rows'
+  // worth of chunks, which leaves the swizzle unchanged, so the source offset of instruction n
+  // is the lane's offset for n = 0 plus n*NW*1024 bytes: one loop-invariant VGPR per matrix,
+  // and the 1 KiB steps go into the (scalar) buffer base.
+  int ld_koff, ld_voff;
+  {
+    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
+    ld_koff = row * ROWB + ((pch ^ swz_k<D>(row)) << 4);
+    ld_voff = row * ROWB + ((pch ^ swz_v<D>(row)) << 4);
   }
-  // One descriptor per tile: base at the tile's first row, size up to the sequence end, so
-  // rows past N (ragged last tile, or a prefetch past the end) read as zero.
-  auto tile_rsrc = [&](const char* base, int j) {
-    const int jrow = j * BN;
-    const int bytes = max(0, N - jrow) * ROWB;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)jrow * ROWB), (short)0, bytes, kBufferWord3);
-  };
-  // (The builtin's pointer and offset go through named locals: given as expressions, the host
-  // compilation silently drops the kernel's host stub.)
-  auto load_tile = [&](const char* base, int j, lds_char* dst, const int (&offs)[NLD]) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, j);
+  // One descriptor per tile and instruction: base at the instruction's first byte of the tile,
+  // size up to the sequence end, so rows past N (ragged last tile, or a prefetch past the end)
+  // read as zero. (The builtin's pointer and offset go through named locals: given as
+  // expressions, the host compilation silently drops the kernel's host stub.)
+  auto load_tile = [&](const char* base, int j, lds_char* dst, const int voffs) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
+      const int64_t first = (int64_t)j * TILE_BYTES + n * NW * 1024;  // this instruction's part
+      const int64_t left = (int64_t)N * ROWB - first;                 // < 2^32 (N*d < 2^31)
+      const int bytes = (int)(unsigned)(left > 0 ? left : 0);         // the hardware reads it unsigned
+      void* bp = (void*)(base + first);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(bp, (short)0, bytes, kBufferWord3);
       lds_void* ldst = (lds_void*)(dst + (n * NW + wave) * 1024);
-      const int voffs = offs[n];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ldst, 16, voffs, 0, 0, 0);
     }
   };
@@ -304,220 +335,218 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(const Params p) {
   };
   const float c = p.c;
 
-  // ---- the Q-tile: rows [t*BM, t*BM + BM) of head (b, hq) against its visible K/V tiles
+  // ---- the Q-tile: rows [t*BM, t*BM + BM) of head (b, hq) against its visible K/V tiles;
+  // wave w owns rows t*BM + 32w + (0..31)
+  const int q0 = t * BM;
+  const int q0w = q0 + wave * 32;
+  const int qrow = q0w + l32;  // this lane's query row
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kv_end + BN - 1) / BN;
+
+  // ---- prologue: K_0, K_1 into LDS; Q tile -> registers as the MFMA B operand (Q^T):
+  // lane l: query l%32, d = 16ks + 8h + 0..7
+  load_k(0, K0);
+  load_k(1, K1);
+  u32x4 qreg[NKS];
   {
-    const int q0 = t * BM;
-    const int q0w = q0 + wave * 32;
-    const int qrow = q0w + l32;  // this lane's query row
-    const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-    const int nt = (kv_end + BN - 1) / BN;
-
-    // ---- prologue: K_0, K_1 into LDS; Q tile -> registers as the MFMA B operand (Q^T):
-    // lane l: query l%32, d = 16ks + 8h + 0..7
-    load_k(0, K0);
-    load_k(1, K1);
-    u32x4 qreg[NKS];
-    {
-      const int qr = min(qrow, N - 1);
-      const u32x4* src = (const u32x4*)(Qp + (int64_t)qr * D + 8 * h);
+    const int qr = min(qrow, N - 1);
+    const u32x4* src = (const u32x4*)(Qp + (int64_t)qr * D + 8 * h);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qreg[ks] = src[2 * ks];
-    }
-
-    f32x16 acc_o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
-    float m_run = -__builtin_inff();  // reference max (scaled, log2 units), one per row
-    float l_run = 0.f;                // this lane's partial row sum (its 16 keys of each block)
-
-    // S^T for the two 32-key blocks of one tile (used outside the pipelined steps)
-    auto s_tile = [&](const lds_char* kd, f32x16 (&s)[2]) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s[kb] = E::mfma(k_operand(kd, kb, ks), qreg[ks], s[kb]);
-      }
-    };
-    sync_tiles();
-    f32x16 sA[2], sB[2];
-    u32x4 pA[4], pB[4];
-    s_tile(K0, sA);
-    // Every wave must be done reading K_0 before the first step refills its buffer.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // One pipeline step for tile j (PAR = j % 2): softmax of S_j (scur) into P_j (pcur), with
-    // the MFMAs of O += P_{j-1} V_{j-1} (HAS_PV) and of S_{j+1} (HAS_S) interleaved with it.
-    // The step is laid out as slots of one MFMA each; a slot also issues the LDS reads of the
-    // MFMA two slots ahead and an even share of the softmax's VALU work, and scheduling
-    // barriers keep that order, so the MFMA pipe stays fed while the VALU work issues in its
-    // shadow.
-    auto step = [&](const int j, auto par, auto has_s, auto has_pv, f32x16 (&scur)[2], f32x16 (&snext)[2],
-                    const u32x4 (&pprev)[4], u32x4 (&pcur)[4]) {
-      constexpr int PAR = decltype(par)::value;
-      constexpr bool HAS_S = decltype(has_s)::value;
-      constexpr bool HAS_PV = decltype(has_pv)::value;
-      constexpr int NPV = HAS_PV ? 4 * NDB : 0;  // MFMAs of P_{j-1} V_{j-1}
-      constexpr int NSM = HAS_S ? 2 * NKS : 0;   // MFMAs of S_{j+1}
-      constexpr int NM = NPV + NSM;
-      constexpr int NSLOT = NM > 0 ? NM : 1;
-      const lds_char* kread = PAR ? K0 : K1;  // K_{j+1}
-      const lds_char* vread = PAR ? V0 : V1;  // V_{j-1}
-      // Loads for the next step go into the buffers this step does not read: V_j where
-      // V_{j-2} was, K_{j+2} where K_j was.
-      load_v(j, PAR ? V1 : V0);
-      if (HAS_S) load_k(j + 2, PAR ? K1 : K0);
-
-      // ---- mask S_j: keys after the query (causal) or past the sequence end. In the S^T
-      // layout element i of block kb holds key kbase + 32kb + 8(i/4) + 4h + i%4: one per-lane
-      // threshold on the constant part covers both conditions.
-      const int kbase = j * BN;
-      const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
-      if (need_mask) {
-        const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;  // hide if part > lim
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int part = 32 * kb + 8 * (i >> 2) + (i & 3);
-            scur[kb][i] = part > lim ? -__builtin_inff() : scur[kb][i];
-          }
-      }
-
-      float alpha = 1.f;
-
-      // ---- the MFMA stream: P V first (its operands are ready), then S_{j+1}
-      u32x4 opnd[NM > 0 ? NM : 1];
-      auto fetch = [&](int m) {
-        if (m < NPV)
-          opnd[m] = v_operand(vread, m / NDB, m % NDB);
-        else
-          opnd[m] = k_operand(kread, (m - NPV) / NKS, (m - NPV) % NKS);
-      };
-      auto issue = [&](int m) {
-        if (m < NPV) {
-          acc_o[m % NDB] = E::mfma(opnd[m], pprev[m / NDB], acc_o[m % NDB]);
-        } else {
-          const int kb = (m - NPV) / NKS, ks = (m - NPV) % NKS;
-          snext[kb] = E::mfma(opnd[m], qreg[ks], ks == 0 ? (f32x16){} : snext[kb]);
-        }
-      };
-
-      // ---- the VALU work, as small items spread over the slots: items 0-3 are partial row
-      // maxima of 8 scores each, item 4 the wave row max and the rescale decision.
-      // Then one item per score (exponential, and for odd scores the pack and the pair sum),
-      // then the lane's total.
-      constexpr int NMAX = 5;
-      constexpr int NITEM = NMAX + 33;
-      float pm[4], ex[32], part[4], tile_sum = 0.f;
-      bool resc = false;
-      auto item = [&](int it) {
-        if (it < NMAX) {
-          if (it < 4) {
-            pm[it] = max8(scur[it >> 1], 8 * (it & 1));
-          } else {
-            const float mt = wave_half_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]))) * c;
-            // A wave-uniform decision; the per-lane updates are branch free so that the step
-            // stays one basic block (the O rescale, which is rare, runs after it).
-            resc = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0;
-            const float m_new = resc ? fmaxf(m_run, mt) : m_run;
-            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-          }
-        } else if (it < NMAX + 32) {
-          const int e = it - NMAX, kb = e >> 4, i = e & 15;
-          ex[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i], c, -m_run));
-          if (e & 1) {
-            const int q = (e >> 1);  // pair index: u32x4 (q / 4), word q % 4
-            unsigned w = E::pack2(ex[e - 1], ex[e]);
-            // Keep the packing in this slot: the value is only used after the step's
-            // closing branch, and the compiler would otherwise sink it out of the block.
-            pin(w);
-            pcur[q >> 2][q & 3] = w;
-            const float s2 = ex[e - 1] + ex[e];
-            part[q & 3] = q < 4 ? s2 : part[q & 3] + s2;
-          }
-        } else {
-          tile_sum = (part[0] + part[1]) + (part[2] + part[3]);
-          pin(tile_sum);
-        }
-      };
-
-      // Register reuse decides the split: the first 32-key block of S_j (items below ITEM_B) is
-      // consumed during the P V MFMAs, before the MFMAs of S_{j+1} overwrite that block, so
-      // the two tiles' first blocks can share registers. Without P V MFMAs those items run
-      // first.
-      constexpr int ITEM_B = NMAX + 16;
-      constexpr int I1 = HAS_S ? ITEM_B : NITEM;  // items of phase 1: [0, I1)
-      constexpr int S1 = HAS_S ? NPV : NSLOT;     // slots of phase 1: [0, S1)
-      if (S1 == 0) {
-#pragma unroll
-        for (int it = 0; it < I1; ++it) item(it);
-      }
-      if (NM > 0) fetch(0);
-      if (NM > 1) fetch(1);
-#pragma unroll
-      for (int sl = 0; sl < NSLOT; ++sl) {
-        if (sl + 2 < NM) fetch(sl + 2);
-        // items [lo, hi) of this slot: phase 1 spreads [0, I1) over slots [0, S1), phase 2
-        // spreads [I1, NITEM) over slots [S1, NSLOT)
-        constexpr int D1 = S1 > 0 ? S1 : 1, D2 = NSLOT - S1 > 0 ? NSLOT - S1 : 1;
-        const int lo = sl < S1 ? (sl * I1) / D1 : I1 + ((sl - S1) * (NITEM - I1)) / D2;
-        const int hi = sl < S1 ? ((sl + 1) * I1) / D1 : I1 + ((sl + 1 - S1) * (NITEM - I1)) / D2;
-#pragma unroll
-        for (int it = lo; it < hi; ++it) item(it);
-        if (sl < NM) issue(sl);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      l_run = l_run * alpha + tile_sum;
-      // The partial output P_{j-1} V_{j-1} was relative to the old reference.
-      if (HAS_PV && resc) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
-      }
-      sync_tiles();
-    };
-
-    // Buffers and registers alternate with j: even j uses (sA -> sB, pA), odd j (sB -> sA, pB).
-    // Every step after the first is a full one, run in pairs until step nt has added
-    // P_{nt-1} V_{nt-1}. Tiles from nt on lie wholly past the last visible key (past the Q-tile's
-    // last row when causal, else past the sequence end), so the mask hides all their scores:
-    // such a step adds exactly zero (no rescale, P = 0, zero row sum). One code path with a
-    // fixed register assignment costs at most one and a half extra steps per Q-tile.
-    const IC<0> E0;
-    const IC<1> E1;
-    const IC<true> Y;
-    const IC<false> Nn;
-    step(0, E0, Y, Nn, sA, sB, pB, pA);
-    for (int j = 1; j <= nt; j += 2) {
-      step(j, E1, Y, Y, sB, sA, pA, pB);
-      step(j + 1, E0, Y, Y, sA, sB, pB, pA);
-    }
-
-    // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
-    const float l_tot = wave_half_sum(l_run);
-    if (qrow < N) {
-      const float inv = 1.0f / l_tot;
-      const int64_t obase = ((int64_t)(b * p.Hq + hq) * N + qrow) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int dcol = 32 * db + 8 * g4 + 4 * h;
-          const float o0 = acc_o[db][4 * g4 + 0] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
-          const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
-          if (OUT_F32) {
-            *(f32x4*)((float*)p.o + obase + dcol) = (f32x4){o0, o1, o2, o3};
-          } else {
-            *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){E::pack2(o0, o1), E::pack2(o2, o3)};
-          }
-        }
-      if (h == 0) p.lse[(int64_t)(b * p.Hq + hq) * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
-    }
+    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = src[2 * ks];
   }
 
+  f32x16 acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
+  float m_run = -__builtin_inff();  // reference max (scaled, log2 units), one per row
+  float l_run = 0.f;   // this lane's partial row sum of the exponentials (its 16 keys of each block)
+  float lr_run = 0.f;  // the same sum over the rounded values that enter P V
+
+  sync_tiles();
+  f32x16 sA[KB], sB[KB];
+  u32x4 pA[2 * KB], pB[2 * KB];
+  // S^T of tile 0, block by block
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    sA[kb] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sA[kb] = E::mfma(k_operand(K0, kb, ks), qreg[ks], sA[kb]);
+  }
+  // Every wave must be done reading K_0 before the first step refills its buffer.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // One pipeline step for tile j (PAR = j % 2): softmax of S_j (scur) into P_j (pcur), with the
+  // MFMAs of O += P_{j-1} V_{j-1} (HAS_PV) and of S_{j+1} (HAS_S) interleaved with it. The step
+  // is laid out as slots of one MFMA each; a slot also issues the LDS reads of the MFMA two
+  // slots ahead and an even share of the softmax's VALU work, and scheduling barriers keep that
+  // order, so the MFMA pipe stays fed while the VALU work issues in its shadow.
+  auto step = [&](const int j, auto par, auto has_s, auto has_pv, f32x16 (&scur)[KB], f32x16 (&snext)[KB],
+                  const u32x4 (&pprev)[2 * KB], u32x4 (&pcur)[2 * KB]) {
+    constexpr int PAR = decltype(par)::value;
+    constexpr bool HAS_S = decltype(has_s)::value;
+    constexpr bool HAS_PV = decltype(has_pv)::value;
+    constexpr int NPV = HAS_PV ? 2 * KB * NDB : 0;  // MFMAs of P_{j-1} V_{j-1}
+    constexpr int NSM = HAS_S ? KB * NKS : 0;       // MFMAs of S_{j+1}
+    constexpr int NM = NPV + NSM;
+    constexpr int NSLOT = NM > 0 ? NM : 1;
+    const lds_char* kread = PAR ? K0 : K1;  // K_{j+1}
+    const lds_char* vread = PAR ? V0 : V1;  // V_{j-1}
+    // Loads for the next step go into the buffers this step does not read: V_j where V_{j-2}
+    // was, K_{j+2} where K_j was.
+    load_v(j, PAR ? V1 : V0);
+    if (HAS_S) load_k(j + 2, PAR ? K1 : K0);
+
+    // ---- mask S_j: keys after the query (causal) or past the sequence end. In the S^T layout
+    // element i of block kb holds key kbase + 32kb + 8(i/4) + 4h + i%4: one per-lane threshold
+    // on the constant part covers both conditions.
+    const int kbase = j * BN;
+    const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
+    if (need_mask) {
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;  // hide if part > lim
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int part = 32 * kb + 8 * (i >> 2) + (i & 3);
+          scur[kb][i] = part > lim ? -__builtin_inff() : scur[kb][i];
+        }
+    }
+
+    // ---- the MFMA stream: P V first (its operands are ready), then S_{j+1}
+    u32x4 opnd[NM > 0 ? NM : 1];
+    auto fetch = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NPV)
+        opnd[m] = v_operand(vread, m / NDB, m % NDB);
+      else
+        opnd[m] = k_operand(kread, (m - NPV) / NKS, (m - NPV) % NKS);
+    };
+    auto issue = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NPV) {
+        acc_o[m % NDB] = E::mfma(opnd[m], pprev[m / NDB], acc_o[m % NDB]);
+      } else {
+        constexpr int kb = (m - NPV) / NKS, ks = (m - NPV) % NKS;
+        snext[kb] = E::mfma(opnd[m], qreg[ks], ks == 0 ? (f32x16){} : snext[kb]);
+      }
+    };
+
+    // ---- the VALU work, as small items spread over the slots: 2*KB partial row maxima of 8
+    // scores, then the wave row max with the rescale decision; then one item per score
+    // (exponential, and for odd scores the pack and the pair sum); then the lane's total.
+    constexpr int NMAXI = 2 * KB + 1, NITEM = NMAXI + 16 * KB + 1;
+    float pm[2 * KB], ex[16 * KB], part[2], tile_sum = 0.f, tile_rsum = 0.f, alpha = 1.f;
+    bool resc = false;
+    auto item = [&](auto itc) {
+      constexpr int it = decltype(itc)::value;
+      if constexpr (it < 2 * KB) {
+        pm[it] = max8(scur[it >> 1], 8 * (it & 1));
+      } else if constexpr (it == 2 * KB) {
+        float mx = KB == 1 ? fmaxf(pm[0], pm[1]) : fmaxf(fmaxf(fmaxf(pm[0], pm[1]), pm[2]), pm[3 % (2 * KB)]);
+        const float mt = wave_half_max(mx) * c;
+        // A wave-uniform decision; the per-lane updates are branch free so that the step
+        // stays one basic block (the O rescale, which is rare, runs after it).
+        resc = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0;
+        const float m_new = resc ? fmaxf(m_run, mt) : m_run;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+      } else if constexpr (it < NITEM - 1) {
+        // P = 2^(S*c - m): fp32 for the row sum (the LSE needs it unrounded), packed to the
+        // input type (round to nearest even) as the B operand of P V, one u32x4 per 16 keys
+        constexpr int e = it - NMAXI, kb = e >> 4, i = e & 15;
+        ex[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i], c, -m_run));
+        if constexpr ((e & 1) != 0) {
+          constexpr int q = e >> 1;  // pair index: u32x4 (q / 4), word q % 4
+          unsigned w = E::pack2(ex[e - 1], ex[e]);
+          // Keep the packing in this slot: the value is only used after the step's closing
+          // branch, and the compiler would otherwise sink it out of the interleaved block.
+          pin(w);
+          pcur[q >> 2][q & 3] = w;
+          const float s2 = ex[e - 1] + ex[e];
+          part[q & 1] = q < 2 ? s2 : part[q & 1] + s2;
+          tile_rsum = E::sum2(w, q == 0 ? 0.f : tile_rsum);
+        }
+      } else {
+        tile_sum = part[0] + part[1];
+        pin(tile_sum);
+        pin(tile_rsum);
+      }
+    };
+
+    // Register reuse decides the split with two key blocks: block 0 of S_j (items below I1) is
+    // consumed during the P V MFMAs, before the MFMAs of S_{j+1} overwrite that block, so the
+    // two tiles' first blocks can share registers (without P V MFMAs those items run first).
+    // With one key block the items simply spread over every slot.
+    constexpr bool SPLIT = HAS_S && KB > 1;
+    constexpr int I1 = SPLIT ? NMAXI + 16 : NITEM;  // items of phase 1: [0, I1)
+    constexpr int S1 = SPLIT ? NPV : NSLOT;         // slots of phase 1: [0, S1)
+    if constexpr (S1 == 0) static_for<0, I1>(item);
+    if constexpr (NM > 0) fetch(IC<0>{});
+    if constexpr (NM > 1) fetch(IC<1>{});
+    static_for<0, NSLOT>([&](auto slc) {
+      constexpr int sl = decltype(slc)::value;
+      if constexpr (sl + 2 < NM) fetch(IC<sl + 2>{});
+      // items [lo, hi) of this slot: phase 1 spreads [0, I1) over slots [0, S1), phase 2
+      // spreads [I1, NITEM) over slots [S1, NSLOT)
+      constexpr int D1 = S1 > 0 ? S1 : 1, D2 = NSLOT - S1 > 0 ? NSLOT - S1 : 1;
+      constexpr int lo = sl < S1 ? (sl * I1) / D1 : I1 + ((sl - S1) * (NITEM - I1)) / D2;
+      constexpr int hi = sl < S1 ? ((sl + 1) * I1) / D1 : I1 + ((sl + 1 - S1) * (NITEM - I1)) / D2;
+      static_for<lo, hi>(item);
+      if constexpr (sl < NM) issue(IC<sl>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    l_run = l_run * alpha + tile_sum;
+    lr_run = lr_run * alpha + tile_rsum;
+    // The partial output P_{j-1} V_{j-1} was relative to the old reference.
+    if (HAS_PV && resc) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+    }
+    sync_tiles();
+  };
+
+  // Buffers and registers alternate with j: even j uses (sA -> sB, pA), odd j (sB -> sA, pB).
+  // Every step after the first is a full one, run in pairs until step nt has added
+  // P_{nt-1} V_{nt-1}. Tiles from nt on lie wholly past the last visible key (past the Q-tile's
+  // last row when causal, else past the sequence end), so the mask hides all their scores:
+  // such a step adds exactly zero (no rescale, P = 0, zero row sum). One code path with a fixed
+  // register assignment costs at most one and a half extra steps per Q-tile.
+  const IC<0> E0;
+  const IC<1> E1;
+  const IC<true> Y;
+  const IC<false> Nn;
+  step(0, E0, Y, Nn, sA, sB, pB, pA);
+  for (int j = 1; j <= nt; j += 2) {
+    step(j, E1, Y, Y, sB, sA, pA, pB);
+    step(j + 1, E0, Y, Y, sA, sB, pB, pA);
+  }
+
+  // ---- epilogue: O = acc / lr, LSE = ln2 * (m + log2 l). O is divided by the sum of the very
+  // values P V was formed with, so the weights that multiply V sum to one: the rounding of a
+  // dominant weight to the input type then cancels instead of scaling the whole row. The LSE
+  // keeps the unrounded sum.
+  const float l_tot = wave_half_sum(l_run);
+  const float lr_tot = wave_half_sum(lr_run);
+  if (qrow < N) {
+    const float inv = 1.0f / lr_tot;
+    const int64_t obase = ((int64_t)(b * p.Hq + hq) * N + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dcol = 32 * db + 8 * g4 + 4 * h;
+        const float o0 = acc_o[db][4 * g4 + 0] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
+        const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
+        if (OUT_F32) {
+          *(f32x4*)((float*)p.o + obase + dcol) = (f32x4){o0, o1, o2, o3};
+        } else {
+          *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){E::pack2(o0, o1), E::pack2(o2, o3)};
+        }
+      }
+    if (h == 0) p.lse[(int64_t)(b * p.Hq + hq) * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+  }
 }
 
 }  // namespace fa
