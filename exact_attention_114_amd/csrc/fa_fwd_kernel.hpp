@@ -359,6 +359,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
   float m_run = -__builtin_inff();  // reference max (scaled, log2 units), one per row
+  float m_thr = -__builtin_inff();  // m_run + slack: a tile max above it triggers a rescale
   float l_run = 0.f;   // this lane's partial row sum of the exponentials (its 16 keys of each block)
   float lr_run = 0.f;  // the same sum over the rounded values that enter P V
 
@@ -436,21 +437,25 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     // scores, then the wave row max with the rescale decision; then one item per score
     // (exponential, and for odd scores the pack and the pair sum); then the lane's total.
     constexpr int NMAXI = 2 * KB + 1, NITEM = NMAXI + 16 * KB + 1;
-    float pm[2 * KB], ex[16 * KB], part[2], tile_sum = 0.f, tile_rsum = 0.f, alpha = 1.f;
+    float pm[2 * KB], ex[16 * KB], part[2], tile_sum = 0.f, tile_rsum = 0.f;
+    float m_old = m_run;
     bool resc = false;
     auto item = [&](auto itc) {
       constexpr int it = decltype(itc)::value;
       if constexpr (it < 2 * KB) {
         pm[it] = max8(scur[it >> 1], 8 * (it & 1));
       } else if constexpr (it == 2 * KB) {
-        float mx = KB == 1 ? fmaxf(pm[0], pm[1]) : fmaxf(fmaxf(fmaxf(pm[0], pm[1]), pm[2]), pm[3 % (2 * KB)]);
+        float mx;
+        if constexpr (KB == 1)
+          mx = fmaxf(pm[0], pm[1]);
+        else
+          mx = fmaxf(fmaxf(fmaxf(pm[0], pm[1]), pm[2]), pm[3]);
         const float mt = wave_half_max(mx) * c;
-        // A wave-uniform decision; the per-lane updates are branch free so that the step
-        // stays one basic block (the O rescale, which is rare, runs after it).
-        resc = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0;
-        const float m_new = resc ? fmaxf(m_run, mt) : m_run;
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        // A wave-uniform decision. The exponentials below need the new reference, so it is
+        // chosen here branch free (the step stays one basic block); the rescale of what was
+        // accumulated against the old one is rare and runs after the step's MFMAs.
+        resc = __builtin_amdgcn_ballot_w64(mt > m_thr) != 0;
+        m_run = resc ? fmaxf(m_run, mt) : m_run;
       } else if constexpr (it < NITEM - 1) {
         // P = 2^(S*c - m): fp32 for the row sum (the LSE needs it unrounded), packed to the
         // input type (round to nearest even) as the B operand of P V, one u32x4 per 16 keys
@@ -497,13 +502,20 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    l_run = l_run * alpha + tile_sum;
-    lr_run = lr_run * alpha + tile_rsum;
-    // The partial output P_{j-1} V_{j-1} was relative to the old reference.
-    if (HAS_PV && resc) {
+    // The sums so far, and the partial output up to P_{j-1} V_{j-1}, were relative to the
+    // old reference: scale them by 2^(m_old - m_new) before adding this tile.
+    if (resc) {
+      const float alpha = __builtin_amdgcn_exp2f(m_old - m_run);
+      l_run *= alpha;
+      lr_run *= alpha;
+      if (HAS_PV) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+        for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      }
+      m_thr = m_run + kRescaleSlack;
     }
+    l_run += tile_sum;
+    lr_run += tile_rsum;
     sync_tiles();
   };
 
