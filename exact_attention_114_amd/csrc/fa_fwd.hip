@@ -25,6 +25,10 @@ constexpr int kBlockM = 32 * kWaves;
 // the grid can fill them, while a small grid does better with the longer step (fewer barriers).
 constexpr int64_t kOneBlockMinGrid = 2 * 256;
 
+// Largest N*d accepted (2^30 - 2^16): a head plane of 2-byte values plus the 64 KiB the last
+// prefetches may reach beyond it stays below 2^31 bytes.
+constexpr int64_t kMaxPlaneElems = ((int64_t)1 << 30) - ((int64_t)1 << 16);
+
 int key_blocks(int64_t d, int64_t grid) { return d == 128 && grid > kOneBlockMinGrid ? 1 : 2; }
 
 template <bool BF16, int D, bool CAUSAL, bool OUT_F32, int KB>
@@ -71,7 +75,9 @@ fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
-  if (N >= lim / d) return FA_ERR_SHAPE;                 // row offsets within a head stay 32-bit
+  // The kernel sizes its tile loads in 32-bit byte offsets from the start of a K/V head
+  // plane, which can reach a few tiles past its end: N*d*2 bytes plus that margin stay below 2^31.
+  if (N * d > kMaxPlaneElems) return FA_ERR_SHAPE;
   if (B >= lim / Hq || B * Hq >= lim / N) return FA_ERR_SHAPE;  // LSE index / head planes
   const int64_t nq = (N + kBlockM - 1) / kBlockM;
   if (B * Hq >= lim / nq) return FA_ERR_SHAPE;           // grid size

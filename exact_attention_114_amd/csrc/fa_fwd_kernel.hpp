@@ -71,7 +71,9 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr float kRescaleSlack = 8.0f;  // log2 units the row max may grow before rescaling
+// A lane's sum of one tile's exponentials above this (2^8) triggers a rescale; below it every
+// exponential of the tile is at most 2^8.
+constexpr float kSumLimit = 256.0f;
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -269,9 +271,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   auto load_tile = [&](const char* base, int j, lds_char* dst, const int voffs) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-      const int64_t first = (int64_t)j * TILE_BYTES + n * NW * 1024;  // this instruction's part
-      const int64_t left = (int64_t)N * ROWB - first;                 // < 2^32 (N*d < 2^31)
-      const int bytes = (int)(unsigned)(left > 0 ? left : 0);         // the hardware reads it unsigned
+      // 32-bit: the host keeps N*ROWB plus the few tiles a prefetch reaches past it below 2^31
+      const int first = j * TILE_BYTES + n * NW * 1024;  // this instruction's part
+      const int left = N * ROWB - first;
+      const int bytes = left > 0 ? left : 0;
       void* bp = (void*)(base + first);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(bp, (short)0, bytes, kBufferWord3);
       lds_void* ldst = (lds_void*)(dst + (n * NW + wave) * 1024);
@@ -359,7 +362,6 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
   float m_run = -__builtin_inff();  // reference max (scaled, log2 units), one per row
-  float m_thr = -__builtin_inff();  // m_run + slack: a tile max above it triggers a rescale
   float l_run = 0.f;   // this lane's partial row sum of the exponentials (its 16 keys of each block)
   float lr_run = 0.f;  // the same sum over the rounded values that enter P V
 
@@ -393,26 +395,23 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     constexpr int NSLOT = NM > 0 ? NM : 1;
     const lds_char* kread = PAR ? K0 : K1;  // K_{j+1}
     const lds_char* vread = PAR ? V0 : V1;  // V_{j-1}
-    // Loads for the next step go into the buffers this step does not read: V_j where V_{j-2}
-    // was, K_{j+2} where K_j was.
-    load_v(j, PAR ? V1 : V0);
-    if (HAS_S) load_k(j + 2, PAR ? K1 : K0);
 
     // ---- mask S_j: keys after the query (causal) or past the sequence end. In the S^T layout
     // element i of block kb holds key kbase + 32kb + 8(i/4) + 4h + i%4: one per-lane threshold
     // on the constant part covers both conditions.
     const int kbase = j * BN;
     const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
-    if (need_mask) {
+    auto mask = [&](f32x16(&st)[KB]) {
       const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;  // hide if part > lim
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int part = 32 * kb + 8 * (i >> 2) + (i & 3);
-          scur[kb][i] = part > lim ? -__builtin_inff() : scur[kb][i];
+          st[kb][i] = part > lim ? -__builtin_inff() : st[kb][i];
         }
-    }
+    };
+    if (need_mask) mask(scur);
 
     // ---- the MFMA stream: P V first (its operands are ready), then S_{j+1}
     u32x4 opnd[NM > 0 ? NM : 1];
@@ -433,29 +432,30 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
       }
     };
 
-    // ---- the VALU work, as small items spread over the slots: 2*KB partial row maxima of 8
-    // scores, then the wave row max with the rescale decision; then one item per score
-    // (exponential, and for odd scores the pack and the pair sum); then the lane's total.
-    constexpr int NMAXI = 2 * KB + 1, NITEM = NMAXI + 16 * KB + 1;
+    // ---- the VALU work, as small items spread over the slots. The first tile sets the
+    // reference from its row max (2*KB partial maxima of 8 scores, then the wave row max). Later
+    // tiles are exponentiated against the current reference straight away and checked after
+    // the slots. Then one item per score (exponential, and for odd scores the pack and the pair
+    // sums); then the lane's totals.
+    constexpr bool MAXFIRST = !HAS_PV;
+    constexpr int NMAXI = MAXFIRST ? 2 * KB + 1 : 0, NITEM = NMAXI + 16 * KB + 1;
     float pm[2 * KB], ex[16 * KB], part[2], tile_sum = 0.f, tile_rsum = 0.f;
-    float m_old = m_run;
-    bool resc = false;
+    auto row_max = [&](const float(&pmx)[2 * KB]) -> float {
+      float mx;
+      if constexpr (KB == 1)
+        mx = fmaxf(pmx[0], pmx[1]);
+      else
+        mx = fmaxf(fmaxf(fmaxf(pmx[0], pmx[1]), pmx[2]), pmx[3]);
+      return wave_half_max(mx) * c;
+    };
     auto item = [&](auto itc) {
       constexpr int it = decltype(itc)::value;
-      if constexpr (it < 2 * KB) {
+      if constexpr (it < NMAXI - 1) {
         pm[it] = max8(scur[it >> 1], 8 * (it & 1));
-      } else if constexpr (it == 2 * KB) {
-        float mx;
-        if constexpr (KB == 1)
-          mx = fmaxf(pm[0], pm[1]);
-        else
-          mx = fmaxf(fmaxf(fmaxf(pm[0], pm[1]), pm[2]), pm[3]);
-        const float mt = wave_half_max(mx) * c;
-        // A wave-uniform decision. The exponentials below need the new reference, so it is
-        // chosen here branch free (the step stays one basic block); the rescale of what was
-        // accumulated against the old one is rare and runs after the step's MFMAs.
-        resc = __builtin_amdgcn_ballot_w64(mt > m_thr) != 0;
-        m_run = resc ? fmaxf(m_run, mt) : m_run;
+      } else if constexpr (it == NMAXI - 1) {
+        // Nothing has been accumulated yet: the reference is simply this tile's row max
+        // (finite: key 0 is visible to every row).
+        m_run = row_max(pm);
       } else if constexpr (it < NITEM - 1) {
         // P = 2^(S*c - m): fp32 for the row sum (the LSE needs it unrounded), packed to the
         // input type (round to nearest even) as the B operand of P V, one u32x4 per 16 keys
@@ -492,6 +492,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     static_for<0, NSLOT>([&](auto slc) {
       constexpr int sl = decltype(slc)::value;
       if constexpr (sl + 2 < NM) fetch(IC<sl + 2>{});
+      // Loads for the next step go into the buffers this step does not read: V_j where V_{j-2}
+      // was, K_{j+2} where K_j was. They are issued once the first MFMA runs, so their scalar
+      // address and size arithmetic issues in its shadow rather than ahead of it.
+      if constexpr (sl == (NM > 1 ? 1 : 0)) {
+        load_v(j, PAR ? V1 : V0);
+        if (HAS_S) load_k(j + 2, PAR ? K1 : K0);
+      }
       // items [lo, hi) of this slot: phase 1 spreads [0, I1) over slots [0, S1), phase 2
       // spreads [I1, NITEM) over slots [S1, NSLOT)
       constexpr int D1 = S1 > 0 ? S1 : 1, D2 = NSLOT - S1 > 0 ? NSLOT - S1 : 1;
@@ -502,17 +509,49 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    // The sums so far, and the partial output up to P_{j-1} V_{j-1}, were relative to the
-    // old reference: scale them by 2^(m_old - m_new) before adding this tile.
-    if (resc) {
-      const float alpha = __builtin_amdgcn_exp2f(m_old - m_run);
-      l_run *= alpha;
-      lr_run *= alpha;
-      if (HAS_PV) {
+    // The exponentials were taken against the current reference. While the reference is no
+    // more than 8 (log2 units) below the true running max, each is at most 2^8 and a lane's sum
+    // of them stays under kSumLimit, so the tile is accepted as it is. A larger sum (or an
+    // overflow) is rare: the reference moves to the exact running max, the tile's exponentials
+    // are taken again (all then at most 1), and the sums and the partial output up to
+    // P_{j-1} V_{j-1}, relative to the old reference, are scaled by 2^(m_old - m_new). The
+    // scores are gone by then (their registers were reused and the K_j buffer is being
+    // refilled), so S_j is formed again with K_j read straight from global memory.
+    if constexpr (!MAXFIRST) {
+      if (__builtin_amdgcn_ballot_w64(tile_sum > kSumLimit) != 0) {
+        f32x16 st[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int krow = min(kbase + 32 * kb + l32, N - 1);  // rows past N are masked below
+          const u32x4* src = (const u32x4*)(Kp + (int64_t)krow * ROWB) + h;
+          st[kb] = (f32x16){};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) st[kb] = E::mfma(src[2 * ks], qreg[ks], st[kb]);
+        }
+        if (need_mask) mask(st);
+#pragma unroll
+        for (int i = 0; i < 2 * KB; ++i) pm[i] = max8(st[i >> 1], 8 * (i & 1));
+        const float m_new = fmaxf(m_run, row_max(pm));
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        float prt = 0.f, rs = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8 * KB; ++q) {
+          const int kb = q >> 3, i = 2 * (q & 7);
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i], c, -m_run));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i + 1], c, -m_run));
+          const unsigned w = E::pack2(e0, e1);
+          pcur[q >> 2][q & 3] = w;
+          prt += e0 + e1;
+          rs = E::sum2(w, rs);
+        }
+        tile_sum = prt;
+        tile_rsum = rs;
+        l_run *= alpha;
+        lr_run *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
       }
-      m_thr = m_run + kRescaleSlack;
     }
     l_run += tile_sum;
     lr_run += tile_rsum;

@@ -75,7 +75,8 @@ typedef enum {
  *   o         device pointer, [B][Hq][N][d] of out_dtype
  *   lse       device pointer, [B][Hq][N] float32
  *   B, Hq, Hkv, N, d   sizes; Hq % Hkv == 0; d in {64, 128}; N >= 1 (any N,
- *             tails are masked); B*Hq*ceil(N/128) and N*d below 2^31
+ *             tails are masked); B*Hq*ceil(N/128) below 2^31; N*d at most
+ *             2^30 - 2^16 (a K/V head plane under 2 GiB)
  *   scale     multiplies Q.K^T (commonly 1/sqrt(d)); finite and > 0
  *   causal    0: every key visible; 1: key j visible to query i iff j <= i
  *   in_dtype  FA_F16 or FA_BF16

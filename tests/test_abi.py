@@ -63,7 +63,8 @@ def test_null_pointers(which):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0), dict(Hkv=0), dict(N=0), dict(d=0), dict(B=-1),
-                                dict(Hq=3, Hkv=2), dict(N=(1 << 31) // 64), dict(B=1 << 20, Hq=1 << 12),
+                                dict(Hq=3, Hkv=2), dict(N=(1 << 31) // 64), dict(N=((1 << 30) - (1 << 16)) // 64 + 1),
+                                dict(N=((1 << 30) - (1 << 16)) // 128 + 1, d=128), dict(B=1 << 20, Hq=1 << 12),
                                 dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=0.0),
                                 dict(scale=-0.125), dict(causal=2)])
 def test_shape_errors(kw):
@@ -93,6 +94,11 @@ def test_tile_query():
     assert bnd.tile(4, 48, 48, 8192, 64, True, bnd.FA_F16)[1] == 64
     bm, bn, grid = bnd.tile(1, 1, 1, 1, 64, False, bnd.FA_F16)
     assert grid == 1
+    # the largest accepted sequence: N*d = 2^30 - 2^16
+    n_max = ((1 << 30) - (1 << 16)) // 128
+    assert bnd.tile(1, 1, 1, n_max, 128, True, bnd.FA_BF16)[2] == (n_max + bm - 1) // bm
+    with pytest.raises(bnd.FaError):
+        bnd.tile(1, 1, 1, n_max + 1, 128, True, bnd.FA_BF16)
     with pytest.raises(bnd.FaError):
         bnd.tile(1, 3, 2, 64, 64, False, bnd.FA_F16)
     lib = bnd.load_library()
