@@ -16,6 +16,9 @@ Contents
                normalisation deferred), used only to check the definition.
   brute.py     the same definition in pure-Python loops (math.exp,
                math.fsum) for tiny shapes.
+  backward.py  the gradients dQ, dK, dV of that definition (the chain rule
+               written out in fp64, P recomputed from the saved LSE), summed
+               over each K/V head's query-head group.
   pool.py      a process pool over (batch, head) units for big shapes.
 
 Every function cites the passage of the pages it follows. Where the pages
@@ -27,3 +30,4 @@ from .softmax import safe_softmax, online_softmax, logsumexp  # noqa: F401
 from .attention import (attention_fp64, head_attention_fp64, attention_probs_fp64,  # noqa: F401
                         tiled_kv_outer_normalised, tiled_q_outer_deferred, kv_head_of)
 from .brute import attention_brute  # noqa: F401
+from .backward import attention_bwd_fp64, head_attention_bwd_fp64  # noqa: F401

@@ -1,0 +1,95 @@
+"""Gradients of exact attention in fp64 -- TEST INFRASTRUCTURE (see the package doc).
+
+What the pages say about the backward pass. The forward keeps only Q, K, V and the softmax
+statistics, and the backward recomputes the attention matrix from them instead of storing
+it. The pages give the trade as about 30% more compute for about 90% less memory:
+  * "FlashAttention算法原理与性能优化实战" (intelliparadigm), section 1.2.3, recomputation;
+  * "Flash Attention是怎么做到又快又省显存的？" (cnblogs), 总结: recomputation as a
+    tiling-based form of gradient checkpointing;
+  * the Triton FA2 walkthrough: the forward's logsumexp L exists for the backward pass, whose
+    benchmark it shows at B=4, H=48, d=64, causal.
+The pages print no gradient formulas. The gradients of O = softmax(s*Q K^T [+ causal
+mask]) V with respect to Q, K and V are plain calculus. Here they are written out for one
+(batch, head) in fp64 on the exactly upcast inputs, with dO the gradient arriving at O:
+  S   = s * Q K^T, hidden entries -inf (causal: key j visible to query i iff j <= i)
+  P   = exp(S - LSE)            recomputed from the forward's saved LSE (the pages' point)
+  dV  = P^T dO
+  dP  = dO V^T
+  D_i = sum_j P_ij dP_ij        (equal to sum_c dO_ic O_ic, the form the GPU path uses)
+  dS  = P o (dP - D)            (o: elementwise; the softmax Jacobian applied row by row)
+  dQ  = s * dS K ;  dK = s * dS^T Q
+Grouped-query attention (intelliparadigm page, section 1.3): query head hq reads K/V head
+floor(hq / G). A K/V head's gradients are therefore the sums over the G query heads that
+read it.
+
+The formula is pinned by tests that do not retype it. Central finite differences of the
+forward definition (and of its pure-Python brute force) check it, and so do torch's float64
+autograd through scaled_dot_product_attention and the invariants sum_j dK_j = 0 and
+sum_j dV_j = sum_i dO_i.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+from .attention import head_attention_fp64, kv_head_of
+
+ROW_BLOCK = 1024  # query rows per block (bounds memory only)
+
+
+def head_attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                            scale: float, causal: bool, lse: Optional[np.ndarray] = None
+                            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of one (batch, head): q, do [n,d] at rows 0..n-1; k, v [N,d].
+
+    Returns (dQ [n,d], dK [N,d], dV [N,d]) in float64. ``lse`` is the forward's natural-log
+    LSE of each row; it is recomputed from the definition when not given.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, N = q.shape[0], k.shape[0]
+    if lse is None:
+        _, lse = head_attention_fp64(q, k, v, scale, causal)
+    lse = np.asarray(lse, dtype=np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, n, ROW_BLOCK):
+        r1 = min(n, r0 + ROW_BLOCK)
+        kend = N if not causal else min(N, r1)
+        S = scale * (q[r0:r1] @ k[:kend].T)
+        if causal:
+            hidden = np.arange(kend)[None, :] > np.arange(r0, r1)[:, None]
+            S = np.where(hidden, -np.inf, S)
+        P = np.exp(S - lse[r0:r1, None])            # recomputed probabilities
+        dv[:kend] += P.T @ do[r0:r1]
+        dP = do[r0:r1] @ v[:kend].T
+        D = np.sum(P * dP, axis=1)
+        dS = P * (dP - D[:, None])
+        dq[r0:r1] = scale * (dS @ k[:kend])
+        dk[:kend] += scale * (dS.T @ q[r0:r1])
+    return dq, dk, dv
+
+
+def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                       causal: bool) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients over [B,Hq,N,d] queries and [B,Hkv,N,d] keys/values (float64).
+
+    Returns (dQ [B,Hq,N,d], dK [B,Hkv,N,d], dV [B,Hkv,N,d]).
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = kv_head_of(hq, Hq, Hkv)
+            g_q, g_k, g_v = head_attention_bwd_fp64(q[b, hq], k[b, hk], v[b, hk], do[b, hq], scale, causal)
+            dq[b, hq] = g_q
+            dk[b, hk] += g_k
+            dv[b, hk] += g_v
+    return dq, dk, dv
