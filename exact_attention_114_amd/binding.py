@@ -1,9 +1,10 @@
-"""ctypes binding over the C ABI of libfa_fwd.so (declared in include/fa.h).
+"""ctypes binding over the C ABI of libfa.so (declared in include/fa.h).
 
 Argument marshalling only: tensors are checked for device, dtype, layout and
-shape, outputs are allocated when the caller does not pass them, and every
-step of the computation runs in the HIP kernels behind ``fa_fwd``. There is
-no fallback: when the library is missing the first call raises.
+shape, outputs (and the backward's workspace) are allocated when the caller
+does not pass them, and every step of the computation runs in the HIP
+kernels behind ``fa_fwd`` and ``fa_bwd``. There is no fallback: when the
+library is missing the first call raises.
 """
 from __future__ import annotations
 
@@ -12,7 +13,7 @@ import math
 import os
 from typing import Optional, Tuple
 
-LIB_NAME = "libfa_fwd.so"
+LIB_NAME = "libfa.so"
 
 FA_F16, FA_BF16, FA_F32 = 0, 1, 2
 FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_HIP = range(6)
@@ -27,6 +28,9 @@ SIGNATURES = {
                                                           ctypes.POINTER(ctypes.c_int),
                                                           ctypes.POINTER(ctypes.c_int),
                                                           ctypes.POINTER(ctypes.c_int64)]),
+    "fa_bwd": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5
+               + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 4),
 }
 
 _lib = None
@@ -45,7 +49,7 @@ def library_path() -> str:
 
 
 def load_library() -> ctypes.CDLL:
-    """Open libfa_fwd.so next to this file (raises FaError if it was never built)."""
+    """Open libfa.so next to this file (raises FaError if it was never built)."""
     global _lib
     if _lib is None:
         path = library_path()
@@ -139,3 +143,67 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out_dty
     _check(fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                    B, Hq, Hkv, N, d, scale, int(bool(causal)), in_code, out_code, stream.cuda_stream))
     return out, lse
+
+
+def bwd_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, ws: int,
+            B: int, Hq: int, Hkv: int, N: int, d: int, scale: float, causal: bool, in_dtype: int,
+            o_dtype: int, stream: int = 0) -> int:
+    """Call fa_bwd with raw device addresses; returns the fa_status code."""
+    return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, N, d, float(scale),
+                                 int(causal), in_dtype, o_dtype, stream)
+
+
+def bwd_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
+    """Bytes of workspace fa_bwd needs (0 for sizes it rejects)."""
+    return int(load_library().fa_bwd_workspace_bytes(B, Hq, N, d))
+
+
+def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False,
+        workspace=None, stream=None):
+    """Gradients (dQ, dK, dV) of exact attention on the GPU, all float32.
+
+    q, k, v as for ``fwd``; o and lse as ``fwd`` returned them (o float32 or
+    the input dtype); dout: the gradient at o, [B, Hq, N, d] in the input
+    dtype. The workspace (a uint8 CUDA tensor of at least
+    ``bwd_workspace_bytes`` bytes) is allocated when not given. Runs on
+    ``stream`` or torch's current stream.
+    """
+    import torch
+
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must be float16 or bfloat16")
+    if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise FaError(FA_ERR_UNSUPPORTED, "q, k, v and dout must share one dtype")
+    if o.dtype not in (torch.float32, q.dtype) or lse.dtype != torch.float32:
+        raise FaError(FA_ERR_UNSUPPORTED, "o must be float32 or the input dtype; lse float32")
+    ts = (q, k, v, o, lse, dout)
+    if any(not t.is_cuda for t in ts) or any(t.device != q.device for t in ts):
+        raise FaError(FA_ERR_UNSUPPORTED, "all tensors must be on one GPU")
+    if any(not t.is_contiguous() for t in ts):
+        raise FaError(FA_ERR_SHAPE, "all tensors must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FaError(FA_ERR_SHAPE, "q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise FaError(FA_ERR_SHAPE, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, N):
+        raise FaError(FA_ERR_SHAPE, "o and dout must match q; lse must be [B, Hq, N]")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    in_code = FA_F16 if q.dtype == torch.float16 else FA_BF16
+    o_code = FA_F32 if o.dtype == torch.float32 else in_code
+    need = bwd_workspace_bytes(B, Hq, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or workspace.numel() * workspace.element_size() < need:
+        raise FaError(FA_ERR_SHAPE, f"workspace must hold {need} bytes on the inputs' device")
+    dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d,
+                   scale, int(bool(causal)), in_code, o_code, stream.cuda_stream))
+    return dq, dk, dv

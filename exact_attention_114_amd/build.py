@@ -1,4 +1,4 @@
-"""Builds libfa_fwd.so (gfx950 code object inside a host shared library) in-tree with hipcc."""
+"""Builds libfa.so (gfx950 code objects inside a host shared library) in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -6,10 +6,11 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip")]
-DEPENDS = [os.path.join(HERE, "csrc", "fa_fwd_kernel.hpp"),
+SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip")]
+DEPENDS = [os.path.join(HERE, "csrc", "fa_fwd_kernel.hpp"), os.path.join(HERE, "csrc", "fa_bwd_kernel.hpp"),
+           os.path.join(HERE, "csrc", "fa_status.hpp"),
            os.path.join(os.path.dirname(HERE), "include", "fa.h")]
-OUTPUT = os.path.join(HERE, "libfa_fwd.so")
+OUTPUT = os.path.join(HERE, "libfa.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -28,7 +29,7 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source into libfa_fwd.so (always recompiles)."""
+    """Compile every HIP source into libfa.so (always recompiles)."""
     tmp = OUTPUT + ".tmp"
     cmd = [hipcc()] + HIPCC_FLAGS + SOURCES + ["-o", tmp]
     if verbose:

@@ -1,0 +1,449 @@
+// fa_bwd_kernel.hpp — exact-attention backward kernels for gfx950 (CDNA4, MI355X).
+//
+// The backward pass recomputes the attention matrix from Q, K, V and the forward's saved
+// statistics instead of storing it (intelliparadigm page, section 1.2.3, recomputation; the
+// cnblogs page's summary; the Triton FA2 walkthrough keeps logsumexp L for it). Per head, with
+// s the scale and dO the gradient arriving at O:
+//   P = exp(s Q K^T - LSE)      (masked entries 0)
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,  dS = P o (dP - D)
+//   dQ = s dS K,  dK = s dS^T Q  (K/V-head gradients summed over the head's query group)
+// Three kernels:
+//   1. prep: per query row, D = rowsum(dO o O) and the LSE in log2 units, into a workspace laid
+//      out per 32-row block as [32 LSE*log2(e) | 32 D] (rows past N hold zeros).
+//   2. dK/dV: a work-group owns 32*NW keys of one (batch, K/V head); each wave keeps its 32 keys'
+//      K and V rows as MFMA operands and its dK, dV accumulators in registers, and sweeps every
+//      32-row query block of every query head of the group. Q and dO blocks stream through LDS
+//      (LDS-DMA, double-buffered). S = Q K^T and dP = dO V^T come out with one key per lane, so
+//      P and dS pack straight into the A operand of dV += P^T dO and dK += dS^T Q, whose
+//      B operands are Q and dO read transposed from LDS (ds_read_b64_tr_b16). No atomics.
+//   3. dQ: a work-group owns 32*NW query rows of one (batch, query head), like the forward;
+//      K and V tiles stream through LDS. S^T = K Q^T and dP^T = V dO^T put one query per lane, so
+//      dS packs into the A operand of dQ += dS K, whose B operand is K read transposed.
+// dQ is kept out of the dK/dV kernel: forming it there would need dS transposed and a
+// cross-work-group sum over key tiles (atomics). Re-forming S and dP in a second kernel costs
+// two more products per tile instead, with no atomics.
+#pragma once
+
+#include "fa_fwd_kernel.hpp"
+
+namespace fa {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* ws;     // per (b, hq) and 32-row block: 32 floats LSE*log2(e), then 32 floats D
+  int B, Hq, Hkv, N;
+  int group;     // Hq / Hkv
+  int n_blk32;   // ceil(N / 32): query blocks the dK/dV kernel sweeps
+  int ws_blk;    // 32-row blocks per head in the workspace: 4 * ceil(N / 128), so that every
+                 // wave of a dQ work-group finds its block (rows past N hold zeros)
+  int n_tiles;   // work-group tiles along the sequence (keys for dK/dV, queries for dQ)
+  int total_wg;
+  float c;       // scale * log2(e)
+  float scale;
+};
+
+// One LDS swizzle for tiles that are read both as rows (ds_read_b128: 16 consecutive rows at one
+// logical 16-byte chunk must hit 16 different bank slots) and transposed (ds_read_b64_tr_b16: an
+// aligned group of 4 rows at one 64-byte segment must hit 4 different 64-byte bank quarters).
+// The chunk index is XORed with a bijection of the row's low bits whose two high result bits come
+// from the row's two lowest bits.
+template <int D>
+__device__ inline int swz_u(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+__device__ inline float half_lo(unsigned w, bool bf16) {
+  return bf16 ? __builtin_bit_cast(float, w << 16) : (float)__builtin_bit_cast(f16x2, w)[0];
+}
+__device__ inline float half_hi(unsigned w, bool bf16) {
+  return bf16 ? __builtin_bit_cast(float, w & 0xffff0000u) : (float)__builtin_bit_cast(f16x2, w)[1];
+}
+
+// ---- 1. prep: D = rowsum(dO o O) and LSE*log2(e), one row per D/8 lanes ----------------------
+template <bool BF16, int D, bool O_F32>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const BwdParams p) {
+  constexpr int TPR = D / 8;       // lanes per row, 8 elements each
+  constexpr int RPB = 256 / TPR;   // rows per work-group
+  const int64_t rows_per_head = (int64_t)p.ws_blk * 32;
+  const int64_t rows = (int64_t)p.B * p.Hq * rows_per_head;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int ch = threadIdx.x % TPR;
+  const int64_t head = row / rows_per_head;
+  const int i = (int)(row - head * rows_per_head);
+  float acc = 0.f, lse2 = 0.f;
+  if (row < rows && i < p.N) {
+    const int64_t e = (head * p.N + i) * D + ch * 8;
+    const u32x4 g = *(const u32x4*)((const unsigned short*)p.dout + e);
+    float o[8];
+    if (O_F32) {
+      const f32x4 a = *(const f32x4*)((const float*)p.o + e);
+      const f32x4 b = *(const f32x4*)((const float*)p.o + e + 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        o[t] = a[t];
+        o[t + 4] = b[t];
+      }
+    } else {
+      const u32x4 w = *(const u32x4*)((const unsigned short*)p.o + e);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        o[2 * t] = half_lo(w[t], BF16);
+        o[2 * t + 1] = half_hi(w[t], BF16);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc += half_lo(g[t], BF16) * o[2 * t] + half_hi(g[t], BF16) * o[2 * t + 1];
+    if (ch == 0) lse2 = p.lse[head * p.N + i] * 1.44269504088896340736f;
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && ch == 0) {
+    float* w = p.ws + (head * p.ws_blk + i / 32) * 64;
+    w[i % 32] = lse2;
+    w[32 + i % 32] = acc;
+  }
+}
+
+// Work-group id -> logical work, each XCD taking a contiguous range (work-group i runs on
+// XCD i % 8), so neighbouring logical work shares that XCD's L2.
+__device__ inline int xcd_remap(int wg, int total) {
+  const int xcd = wg & 7, local = wg >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd * per + min(xcd, rem) + local;
+}
+
+// LDS-DMA of rows [r0, r0 + 32) of a [N][D] plane into a 32-row tile. Instruction n of wave w
+// fills tile bytes [(n*NW + w)*1024, +1024); lane offsets are loop invariant (the swizzle repeats
+// every 16 rows), the instruction's first byte goes into the descriptor base and rows past N
+// read as zero.
+template <int D, int NW>
+__device__ inline void dma_rows(const char* plane, int N, int r0, lds_char* dst, int wave, int voff) {
+  constexpr int ROWB = D * 2, TB = 32 * ROWB, NLD = TB / (NW * 1024);
+  static_assert(NLD >= 1 && TB % (NW * 1024) == 0, "whole 1 KiB DMA instructions per wave");
+#pragma unroll
+  for (int n = 0; n < NLD; ++n) {
+    const int first = r0 * ROWB + n * NW * 1024;
+    const int left = N * ROWB - first;
+    const int bytes = left > 0 ? left : 0;
+    void* bp = (void*)(plane + first);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(bp, (short)0, bytes, kBufferWord3);
+    lds_void* ldst = (lds_void*)(dst + (n * NW + wave) * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ldst, 16, voff, 0, 0, 0);
+  }
+}
+
+// Lane offsets of a tile read as an MFMA operand. Rows: lane holds row l32, chunk 2ks + h.
+template <int D>
+__device__ inline int row_off(int l32, int h, int ks) {
+  return l32 * D * 2 + (((2 * ks + h) ^ swz_u<D>(l32)) << 4);
+}
+// Transposed: lane reads rows 16t + 8u + 4h + i16/4 (t adds an immediate; u changes the swizzle),
+// columns 32db + 16dh + 4(i16%4) .. +3.
+template <int D>
+__device__ inline int tr_off(int lane, int u, int db) {
+  const int h = lane >> 5, i16 = lane & 15, dh = (lane >> 4) & 1;
+  const int row = 8 * u + 4 * h + (i16 >> 2);
+  return row * D * 2 + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ swz_u<D>(row)) << 4) + ((i16 & 1) << 3);
+}
+__device__ inline u32x4 tr_operand(const lds_char* tile, int rowb, int t2, int off0, int off1) {
+  u32x4 a;
+  const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 16 * t2 * rowb + off0)));
+  const u32x2 y = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 16 * t2 * rowb + off1)));
+  a[0] = x[0];
+  a[1] = x[1];
+  a[2] = y[0];
+  a[3] = y[1];
+  return a;
+}
+
+constexpr int bwd_waves_per_simd(int d) { return d == 128 ? 1 : 2; }
+
+// ---- 2. dK/dV ---------------------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
+  using E = Elt<BF16>;
+  constexpr int ROWB = D * 2, KCH = D / 8, TB = 32 * ROWB;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char sQ0[TB];
+  __shared__ __attribute__((aligned(1024))) char sQ1[TB];
+  __shared__ __attribute__((aligned(1024))) char sG0[TB];
+  __shared__ __attribute__((aligned(1024))) char sG1[TB];
+  __shared__ __attribute__((aligned(256))) float sW0[64];
+  __shared__ __attribute__((aligned(256))) float sW1[64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int N = p.N, G = p.group;
+
+  const int L = xcd_remap(blockIdx.x, p.total_wg);
+  const int bk = L / p.n_tiles;  // b * Hkv + hkv
+  const int kt = L - bk * p.n_tiles;
+  const int b = bk / p.Hkv, hkv = bk - b * p.Hkv;
+  const int k0 = kt * 32 * NW, k0w = k0 + 32 * wave;
+
+  using T = unsigned short;
+  const T* Kp = (const T*)p.k + (int64_t)bk * N * D;
+  const T* Vp = (const T*)p.v + (int64_t)bk * N * D;
+  // this wave's 32 keys as the B operands of S = Q K^T and dP = dO V^T: lane holds key l32,
+  // d = 16ks + 8h .. +7 (keys past N repeat row N-1; their gradients are never stored)
+  u32x4 kreg[NKS], vreg[NKS];
+  {
+    const int kr = min(k0w + l32, N - 1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kreg[ks] = *(const u32x4*)(Kp + (int64_t)kr * D + 16 * ks + 8 * h);
+      vreg[ks] = *(const u32x4*)(Vp + (int64_t)kr * D + 16 * ks + 8 * h);
+    }
+  }
+
+  int ld_off;
+  {
+    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
+    ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
+  }
+  int aoff[NKS], toff[2][NDB];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) aoff[ks] = row_off<D>(l32, h, ks);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) toff[u][db] = tr_off<D>(lane, u, db);
+
+  // query blocks: causal work-groups start at the block holding query k0 (earlier queries see
+  // none of these keys)
+  const int qb0 = CAUSAL ? k0 / 32 : 0;
+  const int nqb = p.n_blk32 - qb0;
+  const int n_it = G * nqb;
+
+  auto issue_loads = [&](int it, lds_char* dq_, lds_char* dg_, float* dw_) {
+    const int g = it / nqb, qb = qb0 + (it - g * nqb);
+    const int64_t head = (int64_t)b * p.Hq + hkv * G + g;
+    dma_rows<D, NW>((const char*)((const T*)p.q + head * N * D), N, qb * 32, dq_, wave, ld_off);
+    dma_rows<D, NW>((const char*)((const T*)p.dout + head * N * D), N, qb * 32, dg_, wave, ld_off);
+    if (wave == 0) {
+      void* wp = (void*)(p.ws + (head * p.ws_blk + qb) * 64);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(wp, (short)0, 256, kBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dw_, 4, lane * 4, 0, 0, 0);
+    }
+  };
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = (f32x16){};
+    dv[db] = (f32x16){};
+  }
+  const float c = p.c;
+
+  if (n_it > 0) issue_loads(0, (lds_char*)sQ0, (lds_char*)sG0, sW0);
+  for (int it = 0; it < n_it; ++it) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const bool odd = it & 1;
+    const lds_char* tq = (const lds_char*)(odd ? sQ1 : sQ0);
+    const lds_char* tg = (const lds_char*)(odd ? sG1 : sG0);
+    const float* tw = odd ? sW1 : sW0;
+    if (it + 1 < n_it) issue_loads(it + 1, (lds_char*)(odd ? sQ0 : sQ1), (lds_char*)(odd ? sG0 : sG1), odd ? sW0 : sW1);
+    const int qb = qb0 + (it % nqb);
+    const int q0 = qb * 32;
+
+    // S = Q K^T, dP = dO V^T: lane holds key l32 (column), queries 8(i/4) + 4h + i%4 (rows)
+    f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s = E::mfma(*(const lds_u32x4*)(tq + aoff[ks]), kreg[ks], s);
+      dp = E::mfma(*(const lds_u32x4*)(tg + aoff[ks]), vreg[ks], dp);
+    }
+    // the lane's rows' statistics: 4 groups of 4 consecutive queries
+    float lse2[16], dlt[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 a = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + (8 * g4 + 4 * h) * 4);
+      const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + 128 + (8 * g4 + 4 * h) * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        lse2[4 * g4 + r] = a[r];
+        dlt[4 * g4 + r] = d4[r];
+      }
+    }
+    // causal: key k0w + l32 is hidden from query q0 + part + 4h when it is later
+    if (CAUSAL && q0 < k0w + 31) {
+      const int t = k0w + l32 - q0 - 4 * h;  // hide if part < t
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int part = 8 * (i >> 2) + (i & 3);
+        s[i] = part < t ? -__builtin_inff() : s[i];
+      }
+    }
+    u32x4 pw[2], sw[2];
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2) {
+      const int i = 2 * q2;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2[i]));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -lse2[i + 1]));
+      const float d0 = p0 * (dp[i] - dlt[i]);
+      const float d1 = p1 * (dp[i + 1] - dlt[i + 1]);
+      pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1);
+      sw[q2 >> 2][q2 & 3] = E::pack2(d0, d1);
+    }
+    // dV += P^T dO, dK += dS^T Q: B operands are dO and Q read transposed
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = E::mfma(pw[t2], tr_operand(tg, ROWB, t2, toff[0][db], toff[1][db]), dv[db]);
+        dk[db] = E::mfma(sw[t2], tr_operand(tq, ROWB, t2, toff[0][db], toff[1][db]), dk[db]);
+      }
+  }
+
+  // element i of block db: key k0w + 8(i/4) + 4h + i%4, column 32db + l32
+  float* dkp = p.dk + (int64_t)bk * N * D;
+  float* dvp = p.dv + (int64_t)bk * N * D;
+  const float sc = p.scale;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = k0w + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (key < N) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dkp[(int64_t)key * D + 32 * db + l32] = dk[db][i] * sc;
+        dvp[(int64_t)key * D + 32 * db + l32] = dv[db][i];
+      }
+    }
+  }
+}
+
+// ---- 3. dQ ------------------------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p) {
+  using E = Elt<BF16>;
+  constexpr int ROWB = D * 2, KCH = D / 8, TB = 32 * ROWB, BM = 32 * NW;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char sK0[TB];
+  __shared__ __attribute__((aligned(1024))) char sK1[TB];
+  __shared__ __attribute__((aligned(1024))) char sV0[TB];
+  __shared__ __attribute__((aligned(1024))) char sV1[TB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int N = p.N, G = p.group;
+
+  // (b, hkv) groups with the G sibling query heads side by side, longest Q-tiles first
+  const int L = xcd_remap(blockIdx.x, p.total_wg);
+  const int per_kv = p.n_tiles * G;
+  const int bk = L / per_kv;
+  const int r0 = L - bk * per_kv;
+  const int t_ord = r0 / G, g = r0 - t_ord * G;
+  const int t = CAUSAL ? (p.n_tiles - 1 - t_ord) : t_ord;
+  const int b = bk / p.Hkv, hkv = bk - b * p.Hkv, hq = hkv * G + g;
+  const int64_t head = (int64_t)b * p.Hq + hq;
+  const int q0 = t * BM, q0w = q0 + 32 * wave, qrow = q0w + l32;
+
+  using T = unsigned short;
+  const char* Kp = (const char*)((const T*)p.k + (int64_t)bk * N * D);
+  const char* Vp = (const char*)((const T*)p.v + (int64_t)bk * N * D);
+  // this wave's queries as B operands of S^T = K Q^T and dP^T = V dO^T
+  u32x4 qreg[NKS], greg[NKS];
+  {
+    const int qr = min(qrow, N - 1);
+    const T* qs = (const T*)p.q + (head * N + qr) * D + 8 * h;
+    const T* gs = (const T*)p.dout + (head * N + qr) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qreg[ks] = *(const u32x4*)(qs + 16 * ks);
+      greg[ks] = *(const u32x4*)(gs + 16 * ks);
+    }
+  }
+  // the lane's query's statistics (rows past N hold zeros)
+  const float* w = p.ws + (head * p.ws_blk + q0w / 32) * 64;
+  const float lse2 = w[l32], dlt = w[32 + l32];
+
+  int ld_off;
+  {
+    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
+    ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
+  }
+  int aoff[NKS], toff[2][NDB];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) aoff[ks] = row_off<D>(l32, h, ks);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) toff[u][db] = tr_off<D>(lane, u, db);
+
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kv_end + 31) / 32;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
+  const float c = p.c;
+
+  dma_rows<D, NW>(Kp, N, 0, (lds_char*)sK0, wave, ld_off);
+  dma_rows<D, NW>(Vp, N, 0, (lds_char*)sV0, wave, ld_off);
+  for (int j = 0; j < nt; ++j) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const bool odd = j & 1;
+    const lds_char* tk = (const lds_char*)(odd ? sK1 : sK0);
+    const lds_char* tv = (const lds_char*)(odd ? sV1 : sV0);
+    if (j + 1 < nt) {
+      dma_rows<D, NW>(Kp, N, (j + 1) * 32, (lds_char*)(odd ? sK0 : sK1), wave, ld_off);
+      dma_rows<D, NW>(Vp, N, (j + 1) * 32, (lds_char*)(odd ? sV0 : sV1), wave, ld_off);
+    }
+    // S^T = K Q^T, dP^T = V dO^T: lane holds query l32, keys 32j + 8(i/4) + 4h + i%4
+    f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s = E::mfma(*(const lds_u32x4*)(tk + aoff[ks]), qreg[ks], s);
+      dp = E::mfma(*(const lds_u32x4*)(tv + aoff[ks]), greg[ks], dp);
+    }
+    const int kbase = 32 * j;
+    if ((CAUSAL && kbase + 31 > q0w) || kbase + 32 > N) {
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;  // hide if part > lim
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int part = 8 * (i >> 2) + (i & 3);
+        s[i] = part > lim ? -__builtin_inff() : s[i];
+      }
+    }
+    u32x4 sw[2];
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2) {
+      const int i = 2 * q2;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -lse2));
+      sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
+    }
+    // dQ += dS K: B operand is K read transposed
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = E::mfma(sw[t2], tr_operand(tk, ROWB, t2, toff[0][db], toff[1][db]), acc[db]);
+  }
+
+  // element i of block db: query q0w + 8(i/4) + 4h + i%4, column 32db + l32
+  float* dqp = p.dq + head * N * D;
+  const float sc = p.scale;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int q = q0w + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (q < N) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dqp[(int64_t)q * D + 32 * db + l32] = acc[db][i] * sc;
+    }
+  }
+}
+
+}  // namespace fa

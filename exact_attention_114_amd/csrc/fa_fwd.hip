@@ -12,10 +12,9 @@
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_status.hpp"
 
 namespace {
-
-thread_local int g_last_hip_error = 0;
 
 // Waves per work-group: 4, 32 query rows each, so a work-group takes BM = 128 rows.
 constexpr int kWaves = 4;
@@ -38,7 +37,7 @@ fa_status launch(const fa::Params& p, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
+    fa::last_hip_error = (int)e;
     return FA_ERR_HIP;
   }
   return FA_OK;
@@ -150,6 +149,6 @@ const char* fa_status_str(fa_status s) {
   return "unknown fa_status";
 }
 
-int fa_last_hip_error(void) { return g_last_hip_error; }
+int fa_last_hip_error(void) { return fa::last_hip_error; }
 
 }  // extern "C"

@@ -143,6 +143,13 @@ def draw_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
     return QKV(to_bits(q, dtype), to_bits(k, dtype), to_bits(v, dtype), dtype)
 
 
+def draw_dout(B: int, Hq: int, N: int, d: int, dtype: str, seed: int) -> np.ndarray:
+    """The gradient arriving at O for the backward pass: [B,Hq,N,d] standard normal from its
+    own PCG64 stream (seed), rounded to the storage type; returns the bit pattern."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return to_bits(g.standard_normal((B, Hq, N, d), dtype=np.float32), dtype)
+
+
 def workload_qkv(w: Workload) -> QKV:
     return draw_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.k_mult)
 

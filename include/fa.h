@@ -1,5 +1,6 @@
 /*
- * fa.h — C ABI of the MI355X (gfx950) exact-attention forward library, libfa_fwd.so.
+ * fa.h — C ABI of the MI355X (gfx950) exact-attention library, libfa.so: the forward pass
+ * (fa_fwd) and its gradients (fa_bwd).
  *
  * The operation (FlashAttention forward) is the standard scaled-dot-product
  * attention the pages start from — "PyTorch Transformer Flash Attention机制：
@@ -42,9 +43,10 @@
  * Errors: arguments are checked on the host before any HIP call; on any
  * error nothing is launched and the outputs are left untouched.
  */
-#ifndef FA_FWD_H_
-#define FA_FWD_H_
+#ifndef FA_H_
+#define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -107,8 +109,52 @@ int fa_last_hip_error(void);
 fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
                       fa_dtype in_dtype, int* block_m, int* block_n, int64_t* grid);
 
+/*
+ * fa_bwd — gradients of the attention fa_fwd computes, with respect to q, k
+ * and v, given dout, the gradient arriving at its output o. The backward
+ * pass recomputes the probabilities from q, k and the forward's lse rather
+ * than storing them (intelliparadigm page, section 1.2.3, recomputation;
+ * cnblogs page, summary; the Triton FA2 walkthrough keeps logsumexp L for
+ * the backward pass). Per (batch, query head), with P the probabilities fa_fwd
+ * applied and s = scale:
+ *
+ *   dV = P^T dO    dP = dO V^T    D_i = sum_c dO[i,c] O[i,c]
+ *   dS = P o (dP - D)    (o: elementwise, D subtracted from row i)
+ *   dQ = s dS K    dK = s dS^T Q
+ *
+ * and each K/V head's dK and dV are the sums over its G query heads.
+ *
+ *   q, k, v   as given to fa_fwd
+ *   o, lse    as fa_fwd produced them; o of o_dtype (FA_F32 or in_dtype)
+ *   dout      device pointer, [B][Hq][N][d] of in_dtype: the gradient at o
+ *   dq        device pointer, [B][Hq][N][d] float32, written
+ *   dk, dv    device pointers, [B][Hkv][N][d] float32, written
+ *   workspace device pointer to fa_bwd_workspace_bytes(B, Hq, N, d) bytes
+ *             of scratch, owned by the caller. Its contents on entry do not
+ *             matter; afterwards it holds per-row statistics. Calls that
+ *             share a workspace must not run concurrently.
+ *   sizes, scale, causal, in_dtype, stream: as for fa_fwd
+ *
+ * The outputs must not overlap any input, the workspace or each other. The
+ * call enqueues three kernels on `stream` (row statistics, dK/dV, dQ) and
+ * allocates nothing. Results are deterministic (no atomics). Errors are
+ * reported as for fa_fwd, and every argument is checked before any HIP call.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, float* dq, float* dk, float* dv, float* workspace,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 float scale, int causal, fa_dtype in_dtype, fa_dtype o_dtype,
+                 void* stream);
+
+/*
+ * fa_bwd_workspace_bytes — size in bytes of the workspace fa_bwd needs for
+ * these sizes (two floats per query row, rows padded to a multiple of 128),
+ * or 0 when the sizes are invalid for fa_bwd. Makes no HIP call.
+ */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d);
+
 #ifdef __cplusplus
 }
 #endif
 
-#endif /* FA_FWD_H_ */
+#endif /* FA_H_ */

@@ -93,3 +93,57 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
             dk[b, hk] += g_k
             dv[b, hk] += g_v
     return dq, dk, dv
+
+
+def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                                  o_used: np.ndarray, scale: float, causal: bool, u: float,
+                                  e32: float = 2.0 ** -24
+                                  ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """First-order elementwise error bounds (Bq [n,d], Bk [N,d], Bv [N,d]) for one head's
+    gradients computed the way a tiled kernel does: S, dP and D accumulated in fp32 (unit
+    roundoff ``e32``), D formed from ``o_used`` (the O it is given, e.g. stored in fp32 or in
+    16 bits), P = exp(S - LSE) in fp32, P and dS rounded to a 16-bit type of unit roundoff ``u``
+    before the products that consume them, and those products accumulated in fp32. The test
+    suite sizes its parity bar from these; they are not part of the result.
+
+    With d the head dimension, n the rows and N the keys, per element:
+      rho_ij = d e32 s (|Q||K|^T)_ij + 4 e32              relative error of P (S, fma, exp)
+      eta_ij = d e32 ((|dO||V|^T)_ij + sum_c |dO_ic O_ic|) + |sum_c dO_ic (O_used - O)_ic|
+                                                           absolute error of dP - D
+      Bv = sum_i (u + rho_ij + n e32) P_ij |dO_ic|
+      Bq = s sum_j [(u + rho_ij + N e32) |dS_ij| + P_ij eta_ij] |K_jc|
+      Bk = s sum_i [(u + rho_ij + n e32) |dS_ij| + P_ij eta_ij] |Q_ic|
+    (a product sum_k a_k b_k whose factor a_k carries a relative error e moves by at most
+    e sum_k |a_k b_k|; an fp32 sum of m terms by at most m e32 times the sum of magnitudes).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o_used = np.asarray(o_used, dtype=np.float64)
+    n, N = q.shape[0], k.shape[0]
+    d = q.shape[1]
+    O, lse = head_attention_fp64(q, k, v, scale, causal)
+    d_dev = np.abs(np.sum(do * (o_used - O), axis=1))
+    d_mag = np.sum(np.abs(do * O), axis=1)
+    bq = np.zeros(q.shape)
+    bk = np.zeros(k.shape)
+    bv = np.zeros(v.shape)
+    g_d = d * e32
+    for r0 in range(0, n, ROW_BLOCK):
+        r1 = min(n, r0 + ROW_BLOCK)
+        kend = N if not causal else min(N, r1)
+        S = scale * (q[r0:r1] @ k[:kend].T)
+        if causal:
+            hidden = np.arange(kend)[None, :] > np.arange(r0, r1)[:, None]
+            S = np.where(hidden, -np.inf, S)
+        P = np.exp(S - lse[r0:r1, None])
+        dP = do[r0:r1] @ v[:kend].T
+        D = np.sum(P * dP, axis=1)
+        dS = np.abs(P * (dP - D[:, None]))
+        rho = g_d * scale * (np.abs(q[r0:r1]) @ np.abs(k[:kend]).T) + 4 * e32
+        eta = g_d * (np.abs(do[r0:r1]) @ np.abs(v[:kend]).T + d_mag[r0:r1, None]) + d_dev[r0:r1, None]
+        bv[:kend] += ((u + rho + n * e32) * P).T @ np.abs(do[r0:r1])
+        bq[r0:r1] = scale * (((u + rho + N * e32) * dS + P * eta) @ np.abs(k[:kend]))
+        bk[:kend] += scale * (((u + rho + n * e32) * dS + P * eta).T @ np.abs(q[r0:r1]))
+    return bq, bk, bv

@@ -114,3 +114,57 @@ def test_binding_has_no_cpu_path():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(bnd.FaError):
         bnd.fwd(q, q, q)
+
+
+# ---------------------------------------------------------------- fa_bwd host validation
+
+def call_bwd(**kw):
+    args = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, dout=BAD, dq=BAD, dk=BAD, dv=BAD, ws=BAD, B=1, Hq=2, Hkv=1,
+                N=64, d=64, scale=0.125, causal=0, in_dtype=bnd.FA_F16, o_dtype=bnd.FA_F32)
+    args.update(kw)
+    a = args
+    return bnd.bwd_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["ws"],
+                       a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["in_dtype"],
+                       a["o_dtype"], 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"])
+def test_bwd_null_pointers(which):
+    assert call_bwd(**{which: 0}) == bnd.FA_ERR_NULLPTR
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0), dict(Hkv=0), dict(N=0), dict(d=0), dict(Hq=3, Hkv=2),
+                                dict(N=((1 << 30) - (1 << 16)) // 64 + 1), dict(B=1 << 20, Hq=1 << 12),
+                                dict(scale=float("nan")), dict(scale=0.0), dict(scale=-1.0), dict(causal=2)])
+def test_bwd_shape_errors(kw):
+    assert call_bwd(**kw) == bnd.FA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=256), dict(in_dtype=bnd.FA_F32), dict(in_dtype=9),
+                                dict(o_dtype=bnd.FA_BF16), dict(in_dtype=bnd.FA_BF16, o_dtype=bnd.FA_F16)])
+def test_bwd_unsupported(kw):
+    assert call_bwd(**kw) == bnd.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_alignment_is_checked_last():
+    assert call_bwd() == bnd.FA_ERR_ALIGN
+    assert call_bwd(in_dtype=bnd.FA_BF16, o_dtype=bnd.FA_BF16, d=128, causal=1, Hq=8, Hkv=2, N=1) == bnd.FA_ERR_ALIGN
+
+
+def test_bwd_workspace_bytes():
+    # two floats per query row, rows padded to whole 128-row tiles
+    assert bnd.bwd_workspace_bytes(2, 3, 1, 64) == 2 * 3 * 128 * 2 * 4
+    assert bnd.bwd_workspace_bytes(1, 1, 129, 128) == 256 * 2 * 4
+    assert bnd.bwd_workspace_bytes(4, 32, 8192, 128) == 4 * 32 * 8192 * 2 * 4
+    assert bnd.bwd_workspace_bytes(1, 1, 64, 96) == 0
+    assert bnd.bwd_workspace_bytes(0, 1, 64, 64) == 0
+
+
+def test_bwd_binding_has_no_cpu_path():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    o = torch.zeros(1, 1, 8, 64, dtype=torch.float32)
+    lse = torch.zeros(1, 1, 8, dtype=torch.float32)
+    with pytest.raises(bnd.FaError):
+        bnd.bwd(q, q, q, o, lse, q)
