@@ -10,6 +10,8 @@ in HBM when the timed region starts. Prints ONE JSON line.
                   [--no-cpu-baseline] [--calibrate-copy] [--sweep]
 
 --sweep additionally prints one line per workload (for tables; not the bench line).
+--bwd measures the backward pass (fa_bwd) on the workload instead and prints its own line:
+one step = one fa_bwd call (row statistics, dK/dV and dQ kernels) with O and LSE from fa_fwd.
 --calibrate-copy runs, after the timed region, one elementwise copy kernel of a known
 size, used to scale the FETCH_SIZE / WRITE_SIZE hardware counters into bytes.
 
@@ -112,6 +114,79 @@ def time_gpu(w, steps: int, warmup: int):
     ev_ms = ev0.elapsed_time(ev1)
     assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
     return wall, ev_ms / steps
+
+
+BWD_METRIC = "attention bwd TFLOP/s (10·B·H·N²·d, causal halved) and % of MFMA peak, 1 GPU"
+
+
+def time_gpu_bwd(w, steps: int, warmup: int):
+    """Seconds of wall time for `steps` fa_bwd calls, and the HIP-event average per call."""
+    import torch
+
+    import exact_attention_114_amd as fa
+    from exact_attention_114_amd import binding
+    from exact_attention_114_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    qkv = I.workload_qkv(w)
+    q, k, v = (to_device(x, w.dtype, dev) for x in (qkv.q, qkv.k, qkv.v))
+    del qkv
+    dout = to_device(I.draw_dout(w.B, w.Hq, w.N, w.d, w.dtype, w.seed + 1000), w.dtype, dev)
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    ws = torch.empty(binding.bwd_workspace_bytes(w.B, w.Hq, w.N, w.d), dtype=torch.uint8, device=dev)
+    grads = (torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.Hkv, w.N, w.d), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.Hkv, w.N, w.d), dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        fa.bwd(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, workspace=ws, grads=grads, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert all(torch.isfinite(g).all().item() for g in grads), "non-finite gradient"
+    return wall, ev0.elapsed_time(ev1) / steps
+
+
+def bwd_algorithmic_bytes(w) -> float:
+    """Unique HBM bytes of one fa_bwd call: Q, K, V, dO, LSE and O (fp32) read once; dQ, dK, dV
+    (fp32) written once."""
+    rd = w.B * w.Hq * w.N * w.d * (2 + 2 + 4) + 2 * w.B * w.Hkv * w.N * w.d * 2 + w.B * w.Hq * w.N * 4
+    wr = (w.B * w.Hq + 2 * w.B * w.Hkv) * w.N * w.d * 4
+    return float(rd + wr)
+
+
+def bwd_line(w, args):
+    wall, ms = time_gpu_bwd(w, args.steps, args.warmup)
+    flops = 2.5 * w.flops  # five products of the forward's size: S, dP, dV, dK, dQ
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {
+        "metric": BWD_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and dO; PCG64)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "in_dtype": w.dtype, "grad_dtype": "f32", "o_dtype": "f32",
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_hbm_bytes": bwd_algorithmic_bytes(w), "call_ms": round(ms, 5),
+                     "note": "achieved = algorithmic FLOP / HIP-event time of the whole fa_bwd call "
+                             "(its three kernels); per-kernel times are in the rocprofv3 summary"},
+    }
 
 
 COPY_BYTES = 64 * 1024 * 1024 * 4  # the calibration copy reads and writes this many bytes
@@ -227,6 +302,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--bwd", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="")
     args = ap.parse_args()
@@ -252,6 +328,16 @@ def main():
     binding.load_library()  # fails loudly if the HIP library is missing
 
     w = I.WORKLOADS[args.workload]
+    if args.bwd:
+        if args.sweep:
+            for name in I.WORKLOADS:
+                wk = I.WORKLOADS[name]
+                _, ms = time_gpu_bwd(wk, max(3, min(50, int(5e12 / wk.flops))), 2)
+                tf = 2.5 * wk.flops / (ms * 1e-3) / 1e12
+                print(json.dumps({"sweep_bwd": name, "ms": round(ms, 5), "tflops": round(tf, 2),
+                                  "pct_peak": round(100 * tf / PEAK_TFLOPS[wk.dtype], 2)}), flush=True)
+        print(json.dumps(bwd_line(w, args)), flush=True)
+        return
     if args.sweep:
         for name in I.WORKLOADS:
             wk = I.WORKLOADS[name]

@@ -159,14 +159,15 @@ def bwd_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
 
 
 def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False,
-        workspace=None, stream=None):
+        workspace=None, grads=None, stream=None):
     """Gradients (dQ, dK, dV) of exact attention on the GPU, all float32.
 
     q, k, v as for ``fwd``; o and lse as ``fwd`` returned them (o float32 or
     the input dtype); dout: the gradient at o, [B, Hq, N, d] in the input
     dtype. The workspace (a uint8 CUDA tensor of at least
-    ``bwd_workspace_bytes`` bytes) is allocated when not given. Runs on
-    ``stream`` or torch's current stream.
+    ``bwd_workspace_bytes`` bytes) and the outputs (``grads``: contiguous
+    float32 dq [B, Hq, N, d], dk and dv [B, Hkv, N, d]) are allocated when not
+    given. Runs on ``stream`` or torch's current stream.
     """
     import torch
 
@@ -198,9 +199,14 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if workspace.device != q.device or workspace.numel() * workspace.element_size() < need:
         raise FaError(FA_ERR_SHAPE, f"workspace must hold {need} bytes on the inputs' device")
-    dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
-    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
-    dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    if grads is None:
+        grads = (torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device),
+                 torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device),
+                 torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device))
+    dq, dk, dv = grads
+    for t, shp in ((dq, (B, Hq, N, d)), (dk, (B, Hkv, N, d)), (dv, (B, Hkv, N, d))):
+        if t.shape != shp or t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
+            raise FaError(FA_ERR_SHAPE, "grads must be contiguous float32 dq [B,Hq,N,d], dk and dv [B,Hkv,N,d]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),

@@ -164,7 +164,10 @@ __device__ inline u32x4 tr_operand(const lds_char* tile, int rowb, int t2, int o
   return a;
 }
 
-constexpr int bwd_waves_per_simd(int d) { return d == 128 ? 1 : 2; }
+// At d = 128 the dK/dV kernel keeps V's rows in LDS rather than registers, which brings it
+// under the 256 VGPRs two waves per SIMD allow.
+constexpr bool bwd_v_in_lds(int d) { return d == 128; }
+constexpr int bwd_waves_per_simd(int d) { return 2; }
 
 // ---- 2. dK/dV ---------------------------------------------------------------------------------
 template <bool BF16, int D, bool CAUSAL, int NW>
@@ -179,6 +182,8 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   __shared__ __attribute__((aligned(1024))) char sG1[TB];
   __shared__ __attribute__((aligned(256))) float sW0[64];
   __shared__ __attribute__((aligned(256))) float sW1[64];
+  constexpr bool VL = bwd_v_in_lds(D);
+  __shared__ __attribute__((aligned(1024))) char sV[VL ? NW * TB : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -194,22 +199,27 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   using T = unsigned short;
   const T* Kp = (const T*)p.k + (int64_t)bk * N * D;
   const T* Vp = (const T*)p.v + (int64_t)bk * N * D;
+  int ld_off;
+  {
+    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
+    ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
+  }
   // this wave's 32 keys as the B operands of S = Q K^T and dP = dO V^T: lane holds key l32,
-  // d = 16ks + 8h .. +7 (keys past N repeat row N-1; their gradients are never stored)
-  u32x4 kreg[NKS], vreg[NKS];
+  // d = 16ks + 8h .. +7 (keys past N repeat row N-1, or read as zero from LDS; their gradients
+  // are never stored). V's rows go to LDS when registers are short: 32 rows per wave, read with
+  // the same lane offsets as a Q tile.
+  u32x4 kreg[NKS], vreg[VL ? 1 : NKS];
   {
     const int kr = min(k0w + l32, N - 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kreg[ks] = *(const u32x4*)(Kp + (int64_t)kr * D + 16 * ks + 8 * h);
-      vreg[ks] = *(const u32x4*)(Vp + (int64_t)kr * D + 16 * ks + 8 * h);
+      if constexpr (!VL) vreg[ks] = *(const u32x4*)(Vp + (int64_t)kr * D + 16 * ks + 8 * h);
     }
-  }
-
-  int ld_off;
-  {
-    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
-    ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
+    if constexpr (VL) {
+#pragma unroll
+      for (int m = 0; m < NW; ++m) dma_rows<D, NW>((const char*)Vp, N, k0 + 32 * m, (lds_char*)sV + m * TB, wave, ld_off);
+    }
   }
   int aoff[NKS], toff[2][NDB];
 #pragma unroll
@@ -262,39 +272,40 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       s = E::mfma(*(const lds_u32x4*)(tq + aoff[ks]), kreg[ks], s);
-      dp = E::mfma(*(const lds_u32x4*)(tg + aoff[ks]), vreg[ks], dp);
+      u32x4 vb;
+      if constexpr (VL)
+        vb = *(const lds_u32x4*)((const lds_char*)sV + wave * TB + aoff[ks]);
+      else
+        vb = vreg[ks];
+      dp = E::mfma(*(const lds_u32x4*)(tg + aoff[ks]), vb, dp);
     }
-    // the lane's rows' statistics: 4 groups of 4 consecutive queries
-    float lse2[16], dlt[16];
+    // causal: key k0w + l32 is hidden from query q0 + part + 4h when it is later
+    const bool diag = CAUSAL && q0 < k0w + 31;
+    const int t_hide = k0w + l32 - q0 - 4 * h;  // hide if part < t_hide
+    // P and dS, four rows at a time: the lane's rows' statistics are 4 groups of 4 consecutive
+    // queries, read from LDS just before use
+    u32x4 pw[2], sw[2];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 a = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + (8 * g4 + 4 * h) * 4);
       const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + 128 + (8 * g4 + 4 * h) * 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        lse2[4 * g4 + r] = a[r];
-        dlt[4 * g4 + r] = d4[r];
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const int i = 4 * g4 + 2 * r2;
+        float s0 = s[i], s1 = s[i + 1];
+        if (diag) {
+          s0 = 8 * g4 + 2 * r2 < t_hide ? -__builtin_inff() : s0;
+          s1 = 8 * g4 + 2 * r2 + 1 < t_hide ? -__builtin_inff() : s1;
+        }
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a[2 * r2]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -a[2 * r2 + 1]));
+        const float d0 = p0 * (dp[i] - d4[2 * r2]);
+        const float d1 = p1 * (dp[i + 1] - d4[2 * r2 + 1]);
+        const int q2 = i >> 1;
+        pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1);
+        sw[q2 >> 2][q2 & 3] = E::pack2(d0, d1);
       }
-    }
-    // causal: key k0w + l32 is hidden from query q0 + part + 4h when it is later
-    if (CAUSAL && q0 < k0w + 31) {
-      const int t = k0w + l32 - q0 - 4 * h;  // hide if part < t
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int part = 8 * (i >> 2) + (i & 3);
-        s[i] = part < t ? -__builtin_inff() : s[i];
-      }
-    }
-    u32x4 pw[2], sw[2];
-#pragma unroll
-    for (int q2 = 0; q2 < 8; ++q2) {
-      const int i = 2 * q2;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2[i]));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -lse2[i + 1]));
-      const float d0 = p0 * (dp[i] - dlt[i]);
-      const float d1 = p1 * (dp[i + 1] - dlt[i + 1]);
-      pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1);
-      sw[q2 >> 2][q2 & 3] = E::pack2(d0, d1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // dV += P^T dO, dK += dS^T Q: B operands are dO and Q read transposed
 #pragma unroll
