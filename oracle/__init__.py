@@ -19,6 +19,8 @@ Contents
   backward.py  the gradients dQ, dK, dV of that definition (the chain rule
                written out in fp64, P recomputed from the saved LSE), summed
                over each K/V head's query-head group.
+  attention.py and backward.py also hold the banded forms: a sliding window
+               (left and right edges) with separate query and key lengths.
   pool.py      a process pool over (batch, head) units for big shapes.
 
 Every function cites the passage of the pages it follows. Where the pages
@@ -28,6 +30,8 @@ invariants, library routines, brute force); none is "parity unpinned".
 """
 from .softmax import safe_softmax, online_softmax, logsumexp  # noqa: F401
 from .attention import (attention_fp64, head_attention_fp64, attention_probs_fp64,  # noqa: F401
-                        tiled_kv_outer_normalised, tiled_q_outer_deferred, kv_head_of)
+                        tiled_kv_outer_normalised, tiled_q_outer_deferred, kv_head_of,
+                        band_visible, head_attention_band_fp64, attention_band_fp64)
 from .brute import attention_brute  # noqa: F401
-from .backward import attention_bwd_fp64, head_attention_bwd_fp64  # noqa: F401
+from .backward import (attention_bwd_fp64, head_attention_bwd_fp64,  # noqa: F401
+                       attention_bwd_band_fp64, head_attention_bwd_band_fp64)

@@ -191,3 +191,75 @@ def tiled_q_outer_deferred(q, k, v, scale: float, causal: bool, block_q: int, bl
         O[i0:i1] = acc / l[:, None]
         LSE[i0:i1] = m + np.log(l)
     return O, LSE
+
+
+def band_visible(q_pos: np.ndarray, k_pos: np.ndarray, left: Optional[int], right: Optional[int],
+                 off: int) -> np.ndarray:
+    """visible[i, j]: whether key ``k_pos[j]`` is visible to the query at ``q_pos[i]``.
+
+    The Ascend operator on the intelliparadigm page (section 2.2) bounds a sliding window
+    with pre_tokens (left edge) and next_tokens (right edge), both unlimited by default; its
+    tiling (section 2.3) takes separate query and key lengths. The reading taken: the query
+    at row i sits at key position i + off with off = Nk - Nq (its diagonal aligned to the end
+    of the key sequence), and sees key j iff i + off - left <= j <= i + off + right, an
+    unlimited edge (None) imposing nothing. Causal attention with Nq = Nk is left = None,
+    right = 0.
+    """
+    rel = np.asarray(k_pos, np.int64)[None, :] - (np.asarray(q_pos, np.int64)[:, None] + off)
+    vis = np.ones(rel.shape, dtype=bool)
+    if left is not None:
+        vis &= rel >= -left
+    if right is not None:
+        vis &= rel <= right
+    return vis
+
+
+def head_attention_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                             left: Optional[int], right: Optional[int], off: int = 0,
+                             q_pos: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of one (batch, head) under the band of ``band_visible``.
+
+    Same definition as ``head_attention_fp64`` over each row's visible keys. A row that sees
+    no key has an empty softmax; the reading taken is O = 0 and LSE = -inf (the log of an
+    empty sum).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, N = q.shape[0], k.shape[0]
+    if q_pos is None:
+        q_pos = np.arange(n)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    O = np.zeros((n, v.shape[1]), dtype=np.float64)
+    LSE = np.full((n,), -np.inf, dtype=np.float64)
+    for r0 in range(0, n, ROW_BLOCK):
+        r1 = min(n, r0 + ROW_BLOCK)
+        vis = band_visible(q_pos[r0:r1], np.arange(N), left, right, off)
+        S = np.where(vis, _scores(q[r0:r1], k, scale), -np.inf)
+        seen = vis.any(axis=1)
+        if not seen.any():
+            continue
+        S = S[seen]
+        m = np.max(S, axis=1)
+        e = np.exp(S - m[:, None])
+        l = np.sum(e, axis=1)
+        rows = np.arange(r0, r1)[seen]
+        O[rows] = (e / l[:, None]) @ v
+        LSE[rows] = m + np.log(l)
+    return O, LSE
+
+
+def attention_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                        left: Optional[int], right: Optional[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Banded attention over [B,Hq,Nq,d] queries and [B,Hkv,Nk,d] keys/values (float64),
+    with the diagonal offset off = Nk - Nq. Returns (O [B,Hq,Nq,d], LSE [B,Hq,Nq])."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    O = np.empty(q.shape, dtype=np.float64)
+    LSE = np.empty((B, Hq, Nq), dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = kv_head_of(hq, Hq, Hkv)
+            O[b, hq], LSE[b, hq] = head_attention_band_fp64(q[b, hq], k[b, hk], v[b, hk], scale, left, right,
+                                                            off=Nk - Nq)
+    return O, LSE

@@ -33,7 +33,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .attention import head_attention_fp64, kv_head_of
+from .attention import band_visible, head_attention_band_fp64, head_attention_fp64, kv_head_of
 
 ROW_BLOCK = 1024  # query rows per block (bounds memory only)
 
@@ -147,3 +147,53 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
         bq[r0:r1] = scale * (((u + rho + N * e32) * dS + P * eta) @ np.abs(k[:kend]))
         bk[:kend] += scale * (((u + rho + n * e32) * dS + P * eta).T @ np.abs(q[r0:r1]))
     return bq, bk, bv
+
+
+
+def head_attention_bwd_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                                 left: Optional[int], right: Optional[int], off: int = 0
+                                 ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of one head under the band of ``attention.band_visible`` (the same chain rule
+    as ``head_attention_bwd_fp64``; hidden entries and rows that see no key have P = 0)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, N = q.shape[0], k.shape[0]
+    _, lse = head_attention_band_fp64(q, k, v, scale, left, right, off)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, n, ROW_BLOCK):
+        r1 = min(n, r0 + ROW_BLOCK)
+        vis = band_visible(np.arange(r0, r1), np.arange(N), left, right, off)
+        seen = np.isfinite(lse[r0:r1])
+        S = scale * (q[r0:r1] @ k.T)
+        P = np.where(vis & seen[:, None], np.exp(np.where(vis, S, 0.0) - np.where(seen, lse[r0:r1], 0.0)[:, None]), 0.0)
+        dv += P.T @ do[r0:r1]
+        dP = do[r0:r1] @ v.T
+        D = np.sum(P * dP, axis=1)
+        dS = P * (dP - D[:, None])
+        dq[r0:r1] = scale * (dS @ k)
+        dk += scale * (dS.T @ q[r0:r1])
+    return dq, dk, dv
+
+
+def attention_bwd_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                            left: Optional[int], right: Optional[int]
+                            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Banded gradients over [B,Hq,Nq,d] queries and [B,Hkv,Nk,d] keys/values, off = Nk - Nq."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = kv_head_of(hq, Hq, Hkv)
+            g_q, g_k, g_v = head_attention_bwd_band_fp64(q[b, hq], k[b, hk], v[b, hk], do[b, hq], scale, left, right,
+                                                         off=Nk - Nq)
+            dq[b, hq] = g_q
+            dk[b, hk] += g_k
+            dv[b, hk] += g_v
+    return dq, dk, dv
