@@ -31,6 +31,10 @@ SIGNATURES = {
     "fa_bwd": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5
                + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 4),
+    "fa_fwd_ex": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
+                  + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_bwd_ex": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [ctypes.c_float]
+                  + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -84,6 +88,23 @@ def fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: int, Hkv: int,
                                  in_dtype, out_dtype, stream)
 
 
+def fwd_ex_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+               scale: float, left: int, right: int, in_dtype: int, out_dtype: int, stream: int = 0) -> int:
+    """Call fa_fwd_ex with raw device addresses; returns the fa_status code."""
+    return load_library().fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right,
+                                    in_dtype, out_dtype, stream)
+
+
+def _edges(causal: bool, window) -> Tuple[int, int]:
+    """(left, right) band edges for the C ABI, -1 meaning unlimited."""
+    if window is None:
+        return -1, (0 if causal else -1)
+    if causal:
+        raise FaError(FA_ERR_SHAPE, "pass either causal=True or window=(left, right), not both")
+    left, right = window
+    return (-1 if left is None else int(left)), (-1 if right is None else int(right))
+
+
 def tile(B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool, in_dtype: int) -> Tuple[int, int, int]:
     """(query rows per work-group, keys per tile, work-group count) fa_fwd uses."""
     bm, bn, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
@@ -92,14 +113,16 @@ def tile(B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool, in_dtype: int)
     return bm.value, bn.value, grid.value
 
 
-def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out_dtype=None,
+def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=None, out_dtype=None,
         out=None, lse=None, stream=None):
     """Exact attention forward on the GPU: returns (O, LSE).
 
-    q: [B, Hq, N, d], k and v: [B, Hkv, N, d], contiguous fp16 or bf16 CUDA
+    q: [B, Hq, Nq, d], k and v: [B, Hkv, Nk, d], contiguous fp16 or bf16 CUDA
     tensors (on ROCm, HIP device tensors). scale defaults to 1/sqrt(d);
-    out_dtype defaults to float32 (or pass q.dtype); LSE is float32 [B, Hq, N].
-    Runs on ``stream`` (a torch stream) or torch's current stream.
+    out_dtype defaults to float32 (or pass q.dtype); LSE is float32 [B, Hq, Nq].
+    causal=True, or window=(left, right) (None for an unlimited edge), bands the
+    keys as fa_fwd_ex does: query row i sees keys i + Nk - Nq - left ..
+    i + Nk - Nq + right. Runs on ``stream`` (a torch stream) or torch's current stream.
     """
     import torch
 
@@ -114,9 +137,10 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out_dty
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise FaError(FA_ERR_SHAPE, "q, k, v must be contiguous")
     B, Hq, N, d = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise FaError(FA_ERR_SHAPE, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
-    Hkv = k.shape[1]
+    Hkv, Nk = k.shape[1], k.shape[2]
+    left, right = _edges(causal, window)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out_dtype is None:
@@ -140,8 +164,8 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, out_dty
         raise FaError(FA_ERR_SHAPE, "all tensors must be on one device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    _check(fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                   B, Hq, Hkv, N, d, scale, int(bool(causal)), in_code, out_code, stream.cuda_stream))
+    _check(fwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, Hq, Hkv, N, Nk, d, scale, left, right, in_code, out_code, stream.cuda_stream))
     return out, lse
 
 
@@ -158,13 +182,22 @@ def bwd_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_bytes(B, Hq, N, d))
 
 
-def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False,
+def bwd_ex_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, ws: int,
+               B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, scale: float, left: int, right: int,
+               in_dtype: int, o_dtype: int, stream: int = 0) -> int:
+    """Call fa_bwd_ex with raw device addresses; returns the fa_status code."""
+    return load_library().fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                    left, right, in_dtype, o_dtype, stream)
+
+
+def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False, window=None,
         workspace=None, grads=None, stream=None):
     """Gradients (dQ, dK, dV) of exact attention on the GPU, all float32.
 
     q, k, v as for ``fwd``; o and lse as ``fwd`` returned them (o float32 or
     the input dtype); dout: the gradient at o, [B, Hq, N, d] in the input
-    dtype. The workspace (a uint8 CUDA tensor of at least
+    dtype. causal and window as for ``fwd`` (k and v may have their own
+    sequence length). The workspace (a uint8 CUDA tensor of at least
     ``bwd_workspace_bytes`` bytes) and the outputs (``grads``: contiguous
     float32 dq [B, Hq, N, d], dk and dv [B, Hkv, N, d]) are allocated when not
     given. Runs on ``stream`` or torch's current stream.
@@ -185,11 +218,12 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise FaError(FA_ERR_SHAPE, "q, k, v must be 4-D [batch, heads, seq, head_dim]")
     B, Hq, N, d = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise FaError(FA_ERR_SHAPE, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     if o.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, N):
         raise FaError(FA_ERR_SHAPE, "o and dout must match q; lse must be [B, Hq, N]")
-    Hkv = k.shape[1]
+    Hkv, Nk = k.shape[1], k.shape[2]
+    left, right = _edges(causal, window)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     in_code = FA_F16 if q.dtype == torch.float16 else FA_BF16
@@ -201,15 +235,15 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
         raise FaError(FA_ERR_SHAPE, f"workspace must hold {need} bytes on the inputs' device")
     if grads is None:
         grads = (torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device),
-                 torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device),
-                 torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device))
+                 torch.empty((B, Hkv, Nk, d), dtype=torch.float32, device=q.device),
+                 torch.empty((B, Hkv, Nk, d), dtype=torch.float32, device=q.device))
     dq, dk, dv = grads
-    for t, shp in ((dq, (B, Hq, N, d)), (dk, (B, Hkv, N, d)), (dv, (B, Hkv, N, d))):
+    for t, shp in ((dq, (B, Hq, N, d)), (dk, (B, Hkv, Nk, d)), (dv, (B, Hkv, Nk, d))):
         if t.shape != shp or t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
-            raise FaError(FA_ERR_SHAPE, "grads must be contiguous float32 dq [B,Hq,N,d], dk and dv [B,Hkv,N,d]")
+            raise FaError(FA_ERR_SHAPE, "grads must be contiguous float32 dq [B,Hq,Nq,d], dk and dv [B,Hkv,Nk,d]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    _check(bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d,
-                   scale, int(bool(causal)), in_code, o_code, stream.cuda_stream))
+    _check(bwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, Nk, d,
+                      scale, left, right, in_code, o_code, stream.cuda_stream))
     return dq, dk, dv

@@ -18,6 +18,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTile = 32 * kWaves;                                       // keys or queries per work-group
 constexpr int64_t kMaxPlaneElems = ((int64_t)1 << 30) - ((int64_t)1 << 16);  // as the forward
+constexpr int kUnlimited = 1 << 30;                                       // an unlimited band edge
 
 fa_status launched() {
   const hipError_t e = hipGetLastError();
@@ -28,7 +29,7 @@ fa_status launched() {
   return FA_OK;
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool BAND>
 fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t grid_kv, int64_t grid_q,
                      hipStream_t s) {
   constexpr int RPB = 256 / (D / 8);
@@ -39,35 +40,38 @@ fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t gri
     hipLaunchKernelGGL((fa::fa_bwd_prep_kernel<BF16, D, false>), dim3(prep_grid), dim3(256), 0, s, p);
   fa_status st = launched();
   if (st != FA_OK) return st;
-  p.n_tiles = (int)((p.N + kTile - 1) / kTile);
+  p.n_tiles = (int)((p.Nk + kTile - 1) / kTile);
   p.total_wg = (int)grid_kv;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, CAUSAL, kWaves>), dim3((unsigned)grid_kv), dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves>), dim3((unsigned)grid_kv), dim3(kWaves * 64), 0, s, p);
   st = launched();
   if (st != FA_OK) return st;
+  p.n_tiles = (int)((p.Nq + kTile - 1) / kTile);
   p.total_wg = (int)grid_q;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, CAUSAL, kWaves>), dim3((unsigned)grid_q), dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves>), dim3((unsigned)grid_q), dim3(kWaves * 64), 0, s, p);
   return launched();
 }
 
 template <bool BF16, int D>
-fa_status dispatch_causal(const fa::BwdParams& p, bool causal, bool o_f32, int64_t pr, int64_t gkv, int64_t gq,
-                          hipStream_t s) {
-  return causal ? launch_all<BF16, D, true>(p, o_f32, pr, gkv, gq, s) : launch_all<BF16, D, false>(p, o_f32, pr, gkv, gq, s);
+fa_status dispatch_band(const fa::BwdParams& p, bool band, bool o_f32, int64_t pr, int64_t gkv, int64_t gq,
+                        hipStream_t s) {
+  return band ? launch_all<BF16, D, true>(p, o_f32, pr, gkv, gq, s) : launch_all<BF16, D, false>(p, o_f32, pr, gkv, gq, s);
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Shape checks shared by fa_bwd and fa_bwd_workspace_bytes; fills the derived sizes.
-fa_status check_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t* ws_blk, int64_t* tiles) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_SHAPE;
+// Shape checks shared by fa_bwd_ex and fa_bwd_workspace_bytes; fills the derived sizes.
+fa_status check_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int64_t* ws_blk,
+                    int64_t* tq, int64_t* tk) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (N * d > kMaxPlaneElems) return FA_ERR_SHAPE;
+  if (Nq * d > kMaxPlaneElems || Nk * d > kMaxPlaneElems) return FA_ERR_SHAPE;
   const int64_t lim = (int64_t)1 << 31;
-  const int64_t t = (N + kTile - 1) / kTile;
-  if (B >= lim / Hq || B * Hq >= lim / (4 * t) || B * Hq * 4 * t >= lim / 64) return FA_ERR_SHAPE;
+  const int64_t t = (Nq + kTile - 1) / kTile, u = (Nk + kTile - 1) / kTile;
+  if (B >= lim / Hq || B * Hq >= lim / (4 * t) || B * Hq * 4 * t >= lim / 64 || B * Hq >= lim / u) return FA_ERR_SHAPE;
   *ws_blk = 4 * t;
-  *tiles = t;
+  *tq = t;
+  *tk = u;
   return FA_OK;
 }
 
@@ -76,19 +80,18 @@ fa_status check_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, in
 extern "C" {
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d) {
-  int64_t wb = 0, t = 0;
-  if (check_bwd(B, Hq, 1, N, d, &wb, &t) != FA_OK) return 0;
+  int64_t wb = 0, t = 0, u = 0;
+  if (check_bwd(B, Hq, 1, N, 1, d, &wb, &t, &u) != FA_OK) return 0;
   return (size_t)(B * Hq * wb * 64 * (int64_t)sizeof(float));
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                 float* dq, float* dk, float* dv, float* workspace, int64_t B, int64_t Hq, int64_t Hkv,
-                 int64_t N, int64_t d, float scale, int causal, fa_dtype in_dtype, fa_dtype o_dtype,
-                 void* stream) {
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, float* dq, float* dk, float* dv, float* workspace, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                    int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
-  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
-  int64_t ws_blk = 0, tiles = 0;
-  const fa_status st = check_bwd(B, Hq, Hkv, N, d, &ws_blk, &tiles);
+  int64_t ws_blk = 0, tq = 0, tk = 0;
+  const fa_status st = check_bwd(B, Hq, Hkv, Nq, Nk, d, &ws_blk, &tq, &tk);
   if (st != FA_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
   if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
@@ -111,25 +114,40 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   p.B = (int)B;
   p.Hq = (int)Hq;
   p.Hkv = (int)Hkv;
-  p.N = (int)N;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.off = (int)(Nk - Nq);
+  p.left = window_left < 0 || window_left >= kUnlimited ? kUnlimited : (int)window_left;
+  p.right = window_right < 0 || window_right >= kUnlimited ? kUnlimited : (int)window_right;
   p.group = (int)(Hq / Hkv);
-  p.n_blk32 = (int)((N + 31) / 32);
+  p.n_blk32 = (int)((Nq + 31) / 32);
   p.ws_blk = (int)ws_blk;
-  p.n_tiles = (int)tiles;
+  p.n_tiles = 0;
   p.total_wg = 0;
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   p.scale = scale;
 
+  const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const int64_t prep_rows = B * Hq * ws_blk * 32;
-  const int64_t grid_kv = B * Hkv * tiles;
-  const int64_t grid_q = B * Hq * tiles;
+  const int64_t grid_kv = B * Hkv * tk;
+  const int64_t grid_q = B * Hq * tq;
   const bool bf16 = in_dtype == FA_BF16, o_f32 = o_dtype == FA_F32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (bf16)
-    return d == 64 ? dispatch_causal<true, 64>(p, causal != 0, o_f32, prep_rows, grid_kv, grid_q, s)
-                   : dispatch_causal<true, 128>(p, causal != 0, o_f32, prep_rows, grid_kv, grid_q, s);
-  return d == 64 ? dispatch_causal<false, 64>(p, causal != 0, o_f32, prep_rows, grid_kv, grid_q, s)
-                 : dispatch_causal<false, 128>(p, causal != 0, o_f32, prep_rows, grid_kv, grid_q, s);
+    return d == 64 ? dispatch_band<true, 64>(p, band, o_f32, prep_rows, grid_kv, grid_q, s)
+                   : dispatch_band<true, 128>(p, band, o_f32, prep_rows, grid_kv, grid_q, s);
+  return d == 64 ? dispatch_band<false, 64>(p, band, o_f32, prep_rows, grid_kv, grid_q, s)
+                 : dispatch_band<false, 128>(p, band, o_f32, prep_rows, grid_kv, grid_q, s);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 float* dq, float* dk, float* dv, float* workspace, int64_t B, int64_t Hq, int64_t Hkv,
+                 int64_t N, int64_t d, float scale, int causal, fa_dtype in_dtype, fa_dtype o_dtype,
+                 void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, N, d, scale, -1, causal ? 0 : -1,
+                   in_dtype, o_dtype, stream);
 }
 
 }  // extern "C"

@@ -9,7 +9,10 @@
 //   dQ = s dS K,  dK = s dS^T Q  (K/V-head gradients summed over the head's query group)
 // Three kernels:
 //   1. prep: per query row, D = rowsum(dO o O) and the LSE in log2 units, into a workspace laid
-//      out per 32-row block as [32 LSE*log2(e) | 32 D] (rows past N hold zeros).
+//      out per 32-row block as [32 LSE*log2(e) | 32 D] (rows past Nq hold zeros; a row that
+//      sees no key holds +inf, which makes its P zero).
+// Masks are the forward's band (causal is left unlimited, right 0; query row i sits at key
+// position i + Nk - Nq); each kernel visits only the tiles a band touches.
 //   2. dK/dV: a work-group owns 32*NW keys of one (batch, K/V head); each wave keeps its 32 keys'
 //      K and V rows as MFMA operands and its dK, dV accumulators in registers, and sweeps every
 //      32-row query block of every query head of the group. Q and dO blocks stream through LDS
@@ -39,12 +42,15 @@ struct BwdParams {
   float* dk;
   float* dv;
   float* ws;     // per (b, hq) and 32-row block: 32 floats LSE*log2(e), then 32 floats D
-  int B, Hq, Hkv, N;
+  int B, Hq, Hkv;
+  int Nq, Nk;    // query and key rows per head
+  int off;       // Nk - Nq: key position of query row 0
+  int left, right;  // band edges (1 << 30: unlimited), as in the forward
   int group;     // Hq / Hkv
-  int n_blk32;   // ceil(N / 32): query blocks the dK/dV kernel sweeps
-  int ws_blk;    // 32-row blocks per head in the workspace: 4 * ceil(N / 128), so that every
-                 // wave of a dQ work-group finds its block (rows past N hold zeros)
-  int n_tiles;   // work-group tiles along the sequence (keys for dK/dV, queries for dQ)
+  int n_blk32;   // ceil(Nq / 32): query blocks the dK/dV kernel sweeps
+  int ws_blk;    // 32-row blocks per head in the workspace: 4 * ceil(Nq / 128), so that every
+                 // wave of a dQ work-group finds its block (rows past Nq hold zeros)
+  int n_tiles;   // work-group tiles along the sequence: ceil(Nk / 128) for dK/dV, ceil(Nq / 128) for dQ
   int total_wg;
   float c;       // scale * log2(e)
   float scale;
@@ -79,8 +85,8 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const BwdParams p) {
   const int64_t head = row / rows_per_head;
   const int i = (int)(row - head * rows_per_head);
   float acc = 0.f, lse2 = 0.f;
-  if (row < rows && i < p.N) {
-    const int64_t e = (head * p.N + i) * D + ch * 8;
+  if (row < rows && i < p.Nq) {
+    const int64_t e = (head * p.Nq + i) * D + ch * 8;
     const u32x4 g = *(const u32x4*)((const unsigned short*)p.dout + e);
     float o[8];
     if (O_F32) {
@@ -101,7 +107,11 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const BwdParams p) {
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc += half_lo(g[t], BF16) * o[2 * t] + half_hi(g[t], BF16) * o[2 * t + 1];
-    if (ch == 0) lse2 = p.lse[head * p.N + i] * 1.44269504088896340736f;
+    // a row that sees no key (LSE = -inf) gets +inf, so that every P of the row is 0
+    if (ch == 0) {
+      const float l = p.lse[head * p.Nq + i];
+      lse2 = l == -__builtin_inff() ? __builtin_inff() : l * 1.44269504088896340736f;
+    }
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
@@ -145,18 +155,27 @@ template <int D>
 __device__ inline int row_off(int l32, int h, int ks) {
   return l32 * D * 2 + (((2 * ks + h) ^ swz_u<D>(l32)) << 4);
 }
-// Transposed: lane reads rows 16t + 8u + 4h + i16/4 (t adds an immediate; u changes the swizzle),
-// columns 32db + 16dh + 4(i16%4) .. +3.
+// Transposed: lane reads rows 16t + 8u + 4h + i16/4 (t adds an immediate; u changes the swizzle,
+// see tr_half1), columns 32db + 16dh + 4(i16%4) .. +3.
 template <int D>
 __device__ inline int tr_off(int lane, int u, int db) {
   const int h = lane >> 5, i16 = lane & 15, dh = (lane >> 4) & 1;
   const int row = 8 * u + 4 * h + (i16 >> 2);
   return row * D * 2 + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ swz_u<D>(row)) << 4) + ((i16 & 1) << 3);
 }
-__device__ inline u32x4 tr_operand(const lds_char* tile, int rowb, int t2, int off0, int off1) {
+// The second half (rows + 8) has the swizzle's bit 1 flipped for every lane (rows 8u + 4h + r
+// give (row >> 2) & 3 = 2u + h), so its offset is (off0 ^ 32) + 8 rows: one VGPR per d-block,
+// with the XOR re-done inside the loop (x1 = off0 ^ 32, pinned there) instead of a second
+// loop-invariant register.
+__device__ inline int tr_half1(int off0) {
+  int x = off0 ^ 32;
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ inline u32x4 tr_operand(const lds_char* tile, int rowb, int t2, int off0, int x1) {
   u32x4 a;
   const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 16 * t2 * rowb + off0)));
-  const u32x2 y = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 16 * t2 * rowb + off1)));
+  const u32x2 y = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (16 * t2 + 8) * rowb + x1)));
   a[0] = x[0];
   a[1] = x[1];
   a[2] = y[0];
@@ -169,8 +188,17 @@ __device__ inline u32x4 tr_operand(const lds_char* tile, int rowb, int t2, int o
 constexpr bool bwd_v_in_lds(int d) { return d == 128; }
 constexpr int bwd_waves_per_simd(int d) { return 2; }
 
+// 4 * (lane id), formed from scratch where it is used: as an opaque instruction sequence it
+// cannot be hoisted out of a loop, so it holds no register across the loop (the dK/dV kernel
+// at d = 128 has none to spare).
+__device__ inline int lane_bytes4() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 2, %0" : "=v"(v));
+  return v;
+}
+
 // ---- 2. dK/dV ---------------------------------------------------------------------------------
-template <bool BF16, int D, bool CAUSAL, int NW>
+template <bool BF16, int D, bool BAND, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -188,7 +216,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int N = p.N, G = p.group;
+  const int Nq = p.Nq, Nk = p.Nk, G = p.group;
 
   const int L = xcd_remap(blockIdx.x, p.total_wg);
   const int bk = L / p.n_tiles;  // b * Hkv + hkv
@@ -197,20 +225,20 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   const int k0 = kt * 32 * NW, k0w = k0 + 32 * wave;
 
   using T = unsigned short;
-  const T* Kp = (const T*)p.k + (int64_t)bk * N * D;
-  const T* Vp = (const T*)p.v + (int64_t)bk * N * D;
+  const T* Kp = (const T*)p.k + (int64_t)bk * Nk * D;
+  const T* Vp = (const T*)p.v + (int64_t)bk * Nk * D;
   int ld_off;
   {
     const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
     ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
   }
   // this wave's 32 keys as the B operands of S = Q K^T and dP = dO V^T: lane holds key l32,
-  // d = 16ks + 8h .. +7 (keys past N repeat row N-1, or read as zero from LDS; their gradients
+  // d = 16ks + 8h .. +7 (keys past Nk repeat row Nk-1, or read as zero from LDS; their gradients
   // are never stored). V's rows go to LDS when registers are short: 32 rows per wave, read with
   // the same lane offsets as a Q tile.
   u32x4 kreg[NKS], vreg[VL ? 1 : NKS];
   {
-    const int kr = min(k0w + l32, N - 1);
+    const int kr = min(k0w + l32, Nk - 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kreg[ks] = *(const u32x4*)(Kp + (int64_t)kr * D + 16 * ks + 8 * h);
@@ -218,32 +246,32 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     }
     if constexpr (VL) {
 #pragma unroll
-      for (int m = 0; m < NW; ++m) dma_rows<D, NW>((const char*)Vp, N, k0 + 32 * m, (lds_char*)sV + m * TB, wave, ld_off);
+      for (int m = 0; m < NW; ++m) dma_rows<D, NW>((const char*)Vp, Nk, k0 + 32 * m, (lds_char*)sV + m * TB, wave, ld_off);
     }
   }
-  int aoff[NKS], toff[2][NDB];
+  int aoff[NKS], toff[NDB];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) aoff[ks] = row_off<D>(l32, h, ks);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) toff[u][db] = tr_off<D>(lane, u, db);
+  for (int db = 0; db < NDB; ++db) toff[db] = tr_off<D>(lane, 0, db);
 
-  // query blocks: causal work-groups start at the block holding query k0 (earlier queries see
-  // none of these keys)
-  const int qb0 = CAUSAL ? k0 / 32 : 0;
-  const int nqb = p.n_blk32 - qb0;
+  // query blocks whose band reaches keys [k0, k0 + 32*NW): rows i with
+  // i + off - left <= k0 + 32*NW - 1 and i + off + right >= k0
+  const int q_lo = BAND ? max(0, k0 - p.off - p.right) : 0;
+  const int q_hi = BAND ? min(Nq - 1, k0 + 32 * NW - 1 - p.off + p.left) : Nq - 1;
+  const int qb0 = q_lo / 32;
+  const int nqb = q_hi >= q_lo ? q_hi / 32 - qb0 + 1 : 0;
   const int n_it = G * nqb;
 
   auto issue_loads = [&](int it, lds_char* dq_, lds_char* dg_, float* dw_) {
     const int g = it / nqb, qb = qb0 + (it - g * nqb);
     const int64_t head = (int64_t)b * p.Hq + hkv * G + g;
-    dma_rows<D, NW>((const char*)((const T*)p.q + head * N * D), N, qb * 32, dq_, wave, ld_off);
-    dma_rows<D, NW>((const char*)((const T*)p.dout + head * N * D), N, qb * 32, dg_, wave, ld_off);
+    dma_rows<D, NW>((const char*)((const T*)p.q + head * Nq * D), Nq, qb * 32, dq_, wave, ld_off);
+    dma_rows<D, NW>((const char*)((const T*)p.dout + head * Nq * D), Nq, qb * 32, dg_, wave, ld_off);
     if (wave == 0) {
       void* wp = (void*)(p.ws + (head * p.ws_blk + qb) * 64);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(wp, (short)0, 256, kBufferWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dw_, 4, lane * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dw_, 4, lane_bytes4(), 0, 0, 0);
     }
   };
 
@@ -279,9 +307,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
         vb = vreg[ks];
       dp = E::mfma(*(const lds_u32x4*)(tg + aoff[ks]), vb, dp);
     }
-    // causal: key k0w + l32 is hidden from query q0 + part + 4h when it is later
-    const bool diag = CAUSAL && q0 < k0w + 31;
-    const int t_hide = k0w + l32 - q0 - 4 * h;  // hide if part < t_hide
+    // band: key k0w + l32 is hidden from query q0 + part + 4h when it lies after the query's
+    // right edge (part < t_lo) or before its left edge (part > t_hi)
+    const bool diag = BAND && (k0w + 31 > q0 + p.off + p.right || k0w < q0 + 31 + p.off - p.left);
+    // visible iff t - right <= part <= t + left (t = key - q0 - 4h - off): one unsigned range
+    // check of part - (t - right) against left + right
+    const int vlo = k0w + l32 - q0 - 4 * h - p.off - p.right;
+    const unsigned width = (unsigned)p.left + (unsigned)p.right;
     // P and dS, four rows at a time: the lane's rows' statistics are 4 groups of 4 consecutive
     // queries, read from LDS just before use
     u32x4 pw[2], sw[2];
@@ -294,8 +326,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
         const int i = 4 * g4 + 2 * r2;
         float s0 = s[i], s1 = s[i + 1];
         if (diag) {
-          s0 = 8 * g4 + 2 * r2 < t_hide ? -__builtin_inff() : s0;
-          s1 = 8 * g4 + 2 * r2 + 1 < t_hide ? -__builtin_inff() : s1;
+          const int pa = 8 * g4 + 2 * r2, pb = pa + 1;
+          s0 = (unsigned)(pa - vlo) > width ? -__builtin_inff() : s0;
+          s1 = (unsigned)(pb - vlo) > width ? -__builtin_inff() : s1;
         }
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a[2 * r2]));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -a[2 * r2 + 1]));
@@ -308,23 +341,28 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
       __builtin_amdgcn_sched_barrier(0);
     }
     // dV += P^T dO, dK += dS^T Q: B operands are dO and Q read transposed
+    int x1[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) x1[db] = tr_half1(toff[db]);
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dv[db] = E::mfma(pw[t2], tr_operand(tg, ROWB, t2, toff[0][db], toff[1][db]), dv[db]);
-        dk[db] = E::mfma(sw[t2], tr_operand(tq, ROWB, t2, toff[0][db], toff[1][db]), dk[db]);
+        dv[db] = E::mfma(pw[t2], tr_operand(tg, ROWB, t2, toff[db], x1[db]), dv[db]);
+        dk[db] = E::mfma(sw[t2], tr_operand(tq, ROWB, t2, toff[db], x1[db]), dk[db]);
       }
   }
 
+  // no LDS-DMA may still be in flight when the work-group ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // element i of block db: key k0w + 8(i/4) + 4h + i%4, column 32db + l32
-  float* dkp = p.dk + (int64_t)bk * N * D;
-  float* dvp = p.dv + (int64_t)bk * N * D;
+  float* dkp = p.dk + (int64_t)bk * Nk * D;
+  float* dvp = p.dv + (int64_t)bk * Nk * D;
   const float sc = p.scale;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int key = k0w + 8 * (i >> 2) + 4 * h + (i & 3);
-    if (key < N) {
+    if (key < Nk) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         dkp[(int64_t)key * D + 32 * db + l32] = dk[db][i] * sc;
@@ -335,7 +373,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
 }
 
 // ---- 3. dQ ------------------------------------------------------------------------------------
-template <bool BF16, int D, bool CAUSAL, int NW>
+template <bool BF16, int D, bool BAND, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -349,7 +387,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int N = p.N, G = p.group;
+  const int Nq = p.Nq, Nk = p.Nk, G = p.group;
 
   // (b, hkv) groups with the G sibling query heads side by side, longest Q-tiles first
   const int L = xcd_remap(blockIdx.x, p.total_wg);
@@ -357,27 +395,27 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   const int bk = L / per_kv;
   const int r0 = L - bk * per_kv;
   const int t_ord = r0 / G, g = r0 - t_ord * G;
-  const int t = CAUSAL ? (p.n_tiles - 1 - t_ord) : t_ord;
+  const int t = BAND ? (p.n_tiles - 1 - t_ord) : t_ord;
   const int b = bk / p.Hkv, hkv = bk - b * p.Hkv, hq = hkv * G + g;
   const int64_t head = (int64_t)b * p.Hq + hq;
   const int q0 = t * BM, q0w = q0 + 32 * wave, qrow = q0w + l32;
 
   using T = unsigned short;
-  const char* Kp = (const char*)((const T*)p.k + (int64_t)bk * N * D);
-  const char* Vp = (const char*)((const T*)p.v + (int64_t)bk * N * D);
+  const char* Kp = (const char*)((const T*)p.k + (int64_t)bk * Nk * D);
+  const char* Vp = (const char*)((const T*)p.v + (int64_t)bk * Nk * D);
+  const int qr = min(qrow, Nq - 1);  // rows past Nq behave as the last row (never stored)
   // this wave's queries as B operands of S^T = K Q^T and dP^T = V dO^T
   u32x4 qreg[NKS], greg[NKS];
   {
-    const int qr = min(qrow, N - 1);
-    const T* qs = (const T*)p.q + (head * N + qr) * D + 8 * h;
-    const T* gs = (const T*)p.dout + (head * N + qr) * D + 8 * h;
+    const T* qs = (const T*)p.q + (head * Nq + qr) * D + 8 * h;
+    const T* gs = (const T*)p.dout + (head * Nq + qr) * D + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       qreg[ks] = *(const u32x4*)(qs + 16 * ks);
       greg[ks] = *(const u32x4*)(gs + 16 * ks);
     }
   }
-  // the lane's query's statistics (rows past N hold zeros)
+  // the lane's query's statistics (rows past Nq hold zeros)
   const float* w = p.ws + (head * p.ws_blk + q0w / 32) * 64;
   const float lse2 = w[l32], dlt = w[32 + l32];
 
@@ -386,32 +424,38 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
     const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
     ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
   }
-  int aoff[NKS], toff[2][NDB];
+  int aoff[NKS], toff[NDB];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) aoff[ks] = row_off<D>(l32, h, ks);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) toff[u][db] = tr_off<D>(lane, u, db);
+  for (int db = 0; db < NDB; ++db) toff[db] = tr_off<D>(lane, 0, db);
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kv_end + 31) / 32;
+  // the K/V tiles the Q-tile's band touches: [j_lo, j_lo + nt), and the lane's keys [klo, khi]
+  const int lo_t = BAND ? max(0, q0 + p.off - p.left) : 0;
+  const int hi_t = BAND ? min(Nk - 1, min(q0 + BM, Nq) - 1 + p.off + p.right) : Nk - 1;
+  const int j_lo = lo_t / 32;
+  const int nt = hi_t >= lo_t ? hi_t / 32 - j_lo + 1 : 0;
+  const int khi = BAND ? min(Nk - 1, qr + p.off + p.right) : Nk - 1;
+  const int klo = BAND ? qr + p.off - p.left : 0;
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
   const float c = p.c;
 
-  dma_rows<D, NW>(Kp, N, 0, (lds_char*)sK0, wave, ld_off);
-  dma_rows<D, NW>(Vp, N, 0, (lds_char*)sV0, wave, ld_off);
-  for (int j = 0; j < nt; ++j) {
+  if (nt > 0) {
+    dma_rows<D, NW>(Kp, Nk, j_lo * 32, (lds_char*)sK0, wave, ld_off);
+    dma_rows<D, NW>(Vp, Nk, j_lo * 32, (lds_char*)sV0, wave, ld_off);
+  }
+  for (int r = 0; r < nt; ++r) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const bool odd = j & 1;
+    const bool odd = r & 1;
+    const int j = j_lo + r;
     const lds_char* tk = (const lds_char*)(odd ? sK1 : sK0);
     const lds_char* tv = (const lds_char*)(odd ? sV1 : sV0);
-    if (j + 1 < nt) {
-      dma_rows<D, NW>(Kp, N, (j + 1) * 32, (lds_char*)(odd ? sK0 : sK1), wave, ld_off);
-      dma_rows<D, NW>(Vp, N, (j + 1) * 32, (lds_char*)(odd ? sV0 : sV1), wave, ld_off);
+    if (r + 1 < nt) {
+      dma_rows<D, NW>(Kp, Nk, (j + 1) * 32, (lds_char*)(odd ? sK0 : sK1), wave, ld_off);
+      dma_rows<D, NW>(Vp, Nk, (j + 1) * 32, (lds_char*)(odd ? sV0 : sV1), wave, ld_off);
     }
     // S^T = K Q^T, dP^T = V dO^T: lane holds query l32, keys 32j + 8(i/4) + 4h + i%4
     f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -421,12 +465,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
       dp = E::mfma(*(const lds_u32x4*)(tv + aoff[ks]), greg[ks], dp);
     }
     const int kbase = 32 * j;
-    if ((CAUSAL && kbase + 31 > q0w) || kbase + 32 > N) {
-      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;  // hide if part > lim
+    if ((BAND && (kbase + 31 > min(q0w, Nq - 1) + p.off + p.right || kbase < min(q0w + 31, Nq - 1) + p.off - p.left)) ||
+        kbase + 32 > Nk) {
+      const int hi = khi - kbase - 4 * h, lo = klo - kbase - 4 * h;  // hide if part > hi or part < lo
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int part = 8 * (i >> 2) + (i & 3);
-        s[i] = part > lim ? -__builtin_inff() : s[i];
+        s[i] = (part > hi || (BAND && part < lo)) ? -__builtin_inff() : s[i];
       }
     }
     u32x4 sw[2];
@@ -438,19 +483,22 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
       sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
     }
     // dQ += dS K: B operand is K read transposed
+    int x1[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) x1[db] = tr_half1(toff[db]);
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = E::mfma(sw[t2], tr_operand(tk, ROWB, t2, toff[0][db], toff[1][db]), acc[db]);
+      for (int db = 0; db < NDB; ++db) acc[db] = E::mfma(sw[t2], tr_operand(tk, ROWB, t2, toff[db], x1[db]), acc[db]);
   }
 
   // element i of block db: query q0w + 8(i/4) + 4h + i%4, column 32db + l32
-  float* dqp = p.dq + head * N * D;
+  float* dqp = p.dq + head * Nq * D;
   const float sc = p.scale;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int q = q0w + 8 * (i >> 2) + 4 * h + (i & 3);
-    if (q < N) {
+    if (q < Nq) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dqp[(int64_t)q * D + 32 * db + l32] = acc[db][i] * sc;
     }

@@ -30,10 +30,13 @@ constexpr int64_t kMaxPlaneElems = ((int64_t)1 << 30) - ((int64_t)1 << 16);
 
 int key_blocks(int64_t d, int64_t grid) { return d == 128 && grid > kOneBlockMinGrid ? 1 : 2; }
 
-template <bool BF16, int D, bool CAUSAL, bool OUT_F32, int KB>
+// A band edge of this size or more is unlimited: every in-range index difference is smaller.
+constexpr int kUnlimited = 1 << 30;
+
+template <bool BF16, int D, bool BAND, bool OUT_F32, int KB>
 fa_status launch(const fa::Params& p, hipStream_t stream) {
   // The K/V double buffer is static LDS inside the kernel (4 tiles of 32*KB x D values).
-  auto kern = fa::fa_fwd_kernel<BF16, D, CAUSAL, OUT_F32, kWaves, KB>;
+  auto kern = fa::fa_fwd_kernel<BF16, D, BAND, OUT_F32, kWaves, KB>;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -43,42 +46,42 @@ fa_status launch(const fa::Params& p, hipStream_t stream) {
   return FA_OK;
 }
 
-template <bool BF16, int D, bool CAUSAL, bool OUT_F32>
+template <bool BF16, int D, bool BAND, bool OUT_F32>
 fa_status dispatch_kb(const fa::Params& p, int kb, hipStream_t s) {
   if constexpr (D == 128) {
-    if (kb == 1) return launch<BF16, D, CAUSAL, OUT_F32, 1>(p, s);
+    if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1>(p, s);
   }
-  return launch<BF16, D, CAUSAL, OUT_F32, 2>(p, s);
+  return launch<BF16, D, BAND, OUT_F32, 2>(p, s);
 }
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool BAND>
 fa_status dispatch_out(const fa::Params& p, bool out_f32, int kb, hipStream_t s) {
-  return out_f32 ? dispatch_kb<BF16, D, CAUSAL, true>(p, kb, s) : dispatch_kb<BF16, D, CAUSAL, false>(p, kb, s);
+  return out_f32 ? dispatch_kb<BF16, D, BAND, true>(p, kb, s) : dispatch_kb<BF16, D, BAND, false>(p, kb, s);
 }
 template <bool BF16, int D>
-fa_status dispatch_causal(const fa::Params& p, bool causal, bool out_f32, int kb, hipStream_t s) {
-  return causal ? dispatch_out<BF16, D, true>(p, out_f32, kb, s) : dispatch_out<BF16, D, false>(p, out_f32, kb, s);
+fa_status dispatch_band(const fa::Params& p, bool band, bool out_f32, int kb, hipStream_t s) {
+  return band ? dispatch_out<BF16, D, true>(p, out_f32, kb, s) : dispatch_out<BF16, D, false>(p, out_f32, kb, s);
 }
 template <bool BF16>
-fa_status dispatch_d(const fa::Params& p, int d, bool causal, bool out_f32, int kb, hipStream_t s) {
-  return d == 64 ? dispatch_causal<BF16, 64>(p, causal, out_f32, kb, s)
-                 : dispatch_causal<BF16, 128>(p, causal, out_f32, kb, s);
+fa_status dispatch_d(const fa::Params& p, int d, bool band, bool out_f32, int kb, hipStream_t s) {
+  return d == 64 ? dispatch_band<BF16, 64>(p, band, out_f32, kb, s)
+                 : dispatch_band<BF16, 128>(p, band, out_f32, kb, s);
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // Shared shape/type validation. Returns FA_OK and fills the derived sizes.
-fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype in_dtype,
+fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, fa_dtype in_dtype,
                         int64_t* n_qtiles, int64_t* grid) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_SHAPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
   // The kernel sizes its tile loads in 32-bit byte offsets from the start of a K/V head
   // plane, which can reach a few tiles past its end: N*d*2 bytes plus that margin stay below 2^31.
-  if (N * d > kMaxPlaneElems) return FA_ERR_SHAPE;
-  if (B >= lim / Hq || B * Hq >= lim / N) return FA_ERR_SHAPE;  // LSE index / head planes
-  const int64_t nq = (N + kBlockM - 1) / kBlockM;
+  if (Nq * d > kMaxPlaneElems || Nk * d > kMaxPlaneElems) return FA_ERR_SHAPE;
+  if (B >= lim / Hq || B * Hq >= lim / Nq) return FA_ERR_SHAPE;  // LSE index / head planes
+  const int64_t nq = (Nq + kBlockM - 1) / kBlockM;
   if (B * Hq >= lim / nq) return FA_ERR_SHAPE;           // grid size
   *n_qtiles = nq;
   *grid = B * Hq * nq;
@@ -89,13 +92,12 @@ fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d
 
 extern "C" {
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
-                 int64_t Hkv, int64_t N, int64_t d, float scale, int causal, fa_dtype in_dtype,
-                 fa_dtype out_dtype, void* stream) {
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                    int64_t window_right, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
-  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   int64_t nq = 0, grid = 0;
-  const fa_status st = check_problem(B, Hq, Hkv, N, d, in_dtype, &nq, &grid);
+  const fa_status st = check_problem(B, Hq, Hkv, Nq, Nk, d, in_dtype, &nq, &grid);
   if (st != FA_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
   if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
@@ -110,18 +112,31 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.B = (int)B;
   p.Hq = (int)Hq;
   p.Hkv = (int)Hkv;
-  p.N = (int)N;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.off = (int)(Nk - Nq);
+  p.left = window_left < 0 || window_left >= kUnlimited ? kUnlimited : (int)window_left;
+  p.right = window_right < 0 || window_right >= kUnlimited ? kUnlimited : (int)window_right;
   p.group = (int)(Hq / Hkv);
   p.n_qtiles = (int)nq;
   p.total_wg = (int)grid;
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
 
+  // With both edges unlimited every key is visible and no band is applied.
+  const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const bool bf16 = in_dtype == FA_BF16;
   const bool out_f32 = out_dtype == FA_F32;
   const int kb = key_blocks(d, grid);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return bf16 ? dispatch_d<true>(p, (int)d, causal != 0, out_f32, kb, s)
-              : dispatch_d<false>(p, (int)d, causal != 0, out_f32, kb, s);
+  return bf16 ? dispatch_d<true>(p, (int)d, band, out_f32, kb, s) : dispatch_d<false>(p, (int)d, band, out_f32, kb, s);
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                 int64_t Hkv, int64_t N, int64_t d, float scale, int causal, fa_dtype in_dtype,
+                 fa_dtype out_dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, -1, causal ? 0 : -1, in_dtype, out_dtype, stream);
 }
 
 fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, fa_dtype in_dtype,
@@ -129,7 +144,7 @@ fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
   if (!block_m || !block_n || !grid) return FA_ERR_NULLPTR;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   int64_t nq = 0, g = 0;
-  const fa_status st = check_problem(B, Hq, Hkv, N, d, in_dtype, &nq, &g);
+  const fa_status st = check_problem(B, Hq, Hkv, N, N, d, in_dtype, &nq, &g);
   if (st != FA_OK) return st;
   *block_m = kBlockM;
   *block_n = 32 * key_blocks(d, g);

@@ -38,9 +38,14 @@
 //      l~ of the rounded values that enter the MFMA (one v_dot2 per packed pair), which
 //      normalises O. The weights that multiply V then sum to one, so the rounding of a
 //      dominant weight (up to 2^-8 relative in bf16) cancels rather than scaling the row.
-//   5. Causal (intelliparadigm page, section 1.3: skip the masked half): tiles
-//      past a work-group's last row are never loaded or computed, and only tiles
-//      straddling the diagonal (or the ragged end of the sequence) are masked.
+//   5. Masks. Causal attention (intelliparadigm page, section 1.3: skip the masked half) is one
+//      case of a band: the operator on that page bounds a sliding window by pre_tokens and
+//      next_tokens (section 2.2), and its tiling takes separate query and key lengths (2.3).
+//      Query row i sits at key position i + off, off = Nk - Nq, and sees keys j with
+//      i + off - left <= j <= i + off + right; causal is left = unlimited, right = 0. Only the
+//      K/V tiles a Q-tile's band touches are loaded and computed, and only tiles crossing a
+//      band edge (or the ragged end of the keys) are masked. A row that sees no key gets
+//      O = 0 and LSE = -inf.
 //
 // Software pipeline. A wave's softmax is VALU work and its two products are MFMA
 // work; on gfx950 an MFMA leaves the issue port free for about four VALU
@@ -74,6 +79,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // A lane's sum of one tile's exponentials above this (2^8) triggers a rescale; below it every
 // exponential of the tile is at most 2^8.
 constexpr float kSumLimit = 256.0f;
+// Floor of the running reference (log2 units): a row whose first tiles hold no visible key
+// keeps a finite reference, so the next visible score overflows the check and moves it.
+constexpr float kRefFloor = -1.0e30f;
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -83,9 +91,12 @@ struct Params {
   const void* v;
   void* o;
   float* lse;
-  int B, Hq, Hkv, N;
+  int B, Hq, Hkv;
+  int Nq, Nk;    // query and key rows per head
+  int off;       // Nk - Nq: key position of query row 0
+  int left, right;  // band edges (the host passes 1 << 30 for an unlimited edge)
   int group;     // Hq / Hkv
-  int n_qtiles;  // ceil(N / BM)
+  int n_qtiles;  // ceil(Nq / BM)
   int total_wg;  // B * Hq * n_qtiles
   float c;       // scale * log2(e)
 };
@@ -195,7 +206,7 @@ constexpr int waves_per_simd(int d, int kb) { return d == 128 && kb == 1 ? 3 : 2
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
 // pipeline step takes KB blocks of 32 keys.
-template <bool BF16, int D, bool CAUSAL, bool OUT_F32, int NW, int KB>
+template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
@@ -241,16 +252,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const int r0 = L - bk * per_kv;
   const int t_ord = r0 / G;
   const int g = r0 - t_ord * G;
-  const int t = CAUSAL ? (p.n_qtiles - 1 - t_ord) : t_ord;
+  const int t = BAND ? (p.n_qtiles - 1 - t_ord) : t_ord;
   const int b = bk / p.Hkv;
   const int hkv = bk - b * p.Hkv;
   const int hq = hkv * G + g;
-  const int N = p.N;
+  const int Nq = p.Nq, Nk = p.Nk;
 
   using T = unsigned short;
-  const T* __restrict__ Qp = (const T*)p.q + ((int64_t)(b * p.Hq + hq)) * N * D;
-  const char* __restrict__ Kp = (const char*)((const T*)p.k + ((int64_t)bk) * N * D);
-  const char* __restrict__ Vp = (const char*)((const T*)p.v + ((int64_t)bk) * N * D);
+  const T* __restrict__ Qp = (const T*)p.q + ((int64_t)(b * p.Hq + hq)) * Nq * D;
+  const char* __restrict__ Kp = (const char*)((const T*)p.k + ((int64_t)bk) * Nk * D);
+  const char* __restrict__ Vp = (const char*)((const T*)p.v + ((int64_t)bk) * Nk * D);
 
   // ---- tile loads: instruction n of this wave fills LDS bytes [ii*1024, ii*1024 + 1024) of a
   // tile (ii = n*NW + wave); lane l writes physical chunk ii*64 + l, which holds logical chunk
@@ -271,10 +282,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   auto load_tile = [&](const char* base, int j, lds_char* dst, const int voffs) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-      // 32-bit: the host keeps N*ROWB plus the few tiles a prefetch reaches past it below 2^31
+      // 32-bit: the host keeps Nk*ROWB plus the few tiles a prefetch reaches past it below 2^31
       const int first = j * TILE_BYTES + n * NW * 1024;  // this instruction's part
-      const int left = N * ROWB - first;
-      const int bytes = left > 0 ? left : 0;
+      const int rest = Nk * ROWB - first;
+      const int bytes = rest > 0 ? rest : 0;
       void* bp = (void*)(base + first);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(bp, (short)0, bytes, kBufferWord3);
       lds_void* ldst = (lds_void*)(dst + (n * NW + wave) * 1024);
@@ -303,7 +314,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   // A ragged sequence end leaves tile rows that no load writes (if out-of-range lanes skip
   // the LDS write) or writes as zero: clear the buffers once so they never hold stale bits
   // that could be non-finite.
-  if (N % BN != 0) {
+  if (Nk % BN != 0) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int n = 0; n < TILE_BYTES / (NW * 64 * 16); ++n) {
@@ -343,16 +354,38 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const int q0 = t * BM;
   const int q0w = q0 + wave * 32;
   const int qrow = q0w + l32;  // this lane's query row
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kv_end + BN - 1) / BN;
+  const int qr = min(qrow, Nq - 1);  // rows past Nq behave as the last row (never stored)
+  // the K/V tiles the Q-tile's band touches: [j_lo, j_lo + nt)
+  const int lo_t = BAND ? max(0, q0 + p.off - p.left) : 0;
+  const int hi_t = BAND ? min(Nk - 1, min(q0 + BM, Nq) - 1 + p.off + p.right) : Nk - 1;
+  const int j_lo = lo_t / BN;
+  const int nt = hi_t >= lo_t ? hi_t / BN - j_lo + 1 : 0;
+  // the lane's visible keys: [klo, khi]
+  const int khi = BAND ? min(Nk - 1, qr + p.off + p.right) : Nk - 1;
+  const int klo = BAND ? qr + p.off - p.left : 0;
+  if (nt == 0) {
+    // no row of this Q-tile sees a key: O = 0, LSE = -inf
+    if (qrow < Nq) {
+      const int64_t obase = ((int64_t)(b * p.Hq + hq) * Nq + qrow) * D;
+#pragma unroll
+      for (int c8 = 0; c8 < D / 2; c8 += 4) {
+        const int dcol = 2 * c8 + 4 * h;  // lanes h = 0, 1 cover alternate groups of 4
+        if (OUT_F32)
+          *(f32x4*)((float*)p.o + obase + dcol) = (f32x4){0.f, 0.f, 0.f, 0.f};
+        else
+          *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){0u, 0u};
+      }
+      if (h == 0) p.lse[(int64_t)(b * p.Hq + hq) * Nq + qrow] = -__builtin_inff();
+    }
+    return;
+  }
 
   // ---- prologue: K_0, K_1 into LDS; Q tile -> registers as the MFMA B operand (Q^T):
   // lane l: query l%32, d = 16ks + 8h + 0..7
-  load_k(0, K0);
-  load_k(1, K1);
+  load_k(j_lo, K0);
+  load_k(j_lo + 1, K1);
   u32x4 qreg[NKS];
   {
-    const int qr = min(qrow, N - 1);
     const u32x4* src = (const u32x4*)(Qp + (int64_t)qr * D + 8 * h);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qreg[ks] = src[2 * ks];
@@ -384,8 +417,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   // is laid out as slots of one MFMA each; a slot also issues the LDS reads of the MFMA two
   // slots ahead and an even share of the softmax's VALU work, and scheduling barriers keep that
   // order, so the MFMA pipe stays fed while the VALU work issues in its shadow.
-  auto step = [&](const int j, auto par, auto has_s, auto has_pv, f32x16 (&scur)[KB], f32x16 (&snext)[KB],
+  auto step = [&](const int r, auto par, auto has_s, auto has_pv, f32x16 (&scur)[KB], f32x16 (&snext)[KB],
                   const u32x4 (&pprev)[2 * KB], u32x4 (&pcur)[2 * KB]) {
+    const int j = j_lo + r;  // the K/V tile (buffers alternate with r)
     constexpr int PAR = decltype(par)::value;
     constexpr bool HAS_S = decltype(has_s)::value;
     constexpr bool HAS_PV = decltype(has_pv)::value;
@@ -396,19 +430,24 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     const lds_char* kread = PAR ? K0 : K1;  // K_{j+1}
     const lds_char* vread = PAR ? V0 : V1;  // V_{j-1}
 
-    // ---- mask S_j: keys after the query (causal) or past the sequence end. In the S^T layout
-    // element i of block kb holds key kbase + 32kb + 8(i/4) + 4h + i%4: one per-lane threshold
-    // on the constant part covers both conditions.
+    // ---- mask S_j: keys outside the lane's band [klo, khi] (khi also stops at the last key).
+    // In the S^T layout element i of block kb holds key kbase + 32kb + 8(i/4) + 4h + i%4: two
+    // per-lane thresholds on the constant part. A tile needs masking when it crosses the wave's
+    // band edges or the end of the keys.
     const int kbase = j * BN;
-    const bool need_mask = (CAUSAL && kbase + BN - 1 > q0w) || (kbase + BN > N);
+    const bool need_mask = (BAND && (kbase + BN - 1 > min(q0w, Nq - 1) + p.off + p.right ||
+                                     kbase < min(q0w + 31, Nq - 1) + p.off - p.left)) ||
+                           (kbase + BN > Nk);
     auto mask = [&](f32x16(&st)[KB]) {
-      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;  // hide if part > lim
+      const int hi = khi - kbase - 4 * h;  // hide if part > hi
+      const int lo = klo - kbase - 4 * h;  // hide if part < lo
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int part = 32 * kb + 8 * (i >> 2) + (i & 3);
-          st[kb][i] = part > lim ? -__builtin_inff() : st[kb][i];
+          const bool hide = BAND ? (part > hi || part < lo) : part > hi;
+          st[kb][i] = hide ? -__builtin_inff() : st[kb][i];
         }
     };
     if (need_mask) mask(scur);
@@ -453,9 +492,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
       if constexpr (it < NMAXI - 1) {
         pm[it] = max8(scur[it >> 1], 8 * (it & 1));
       } else if constexpr (it == NMAXI - 1) {
-        // Nothing has been accumulated yet: the reference is simply this tile's row max
-        // (finite: key 0 is visible to every row).
-        m_run = row_max(pm);
+        // Nothing has been accumulated yet: the reference is simply this tile's row max,
+        // floored so that a row with no visible key here keeps a finite reference.
+        m_run = fmaxf(row_max(pm), kRefFloor);
       } else if constexpr (it < NITEM - 1) {
         // P = 2^(S*c - m): fp32 for the row sum (the LSE needs it unrounded), packed to the
         // input type (round to nearest even) as the B operand of P V, one u32x4 per 16 keys
@@ -522,7 +561,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
         f32x16 st[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const int krow = min(kbase + 32 * kb + l32, N - 1);  // rows past N are masked below
+          const int krow = min(kbase + 32 * kb + l32, Nk - 1);  // rows past Nk are masked below
           const u32x4* src = (const u32x4*)(Kp + (int64_t)krow * ROWB) + h;
           st[kb] = (f32x16){};
 #pragma unroll
@@ -569,20 +608,21 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const IC<true> Y;
   const IC<false> Nn;
   step(0, E0, Y, Nn, sA, sB, pB, pA);
-  for (int j = 1; j <= nt; j += 2) {
-    step(j, E1, Y, Y, sB, sA, pA, pB);
-    step(j + 1, E0, Y, Y, sA, sB, pB, pA);
+  for (int r = 1; r <= nt; r += 2) {
+    step(r, E1, Y, Y, sB, sA, pA, pB);
+    step(r + 1, E0, Y, Y, sA, sB, pB, pA);
   }
 
   // ---- epilogue: O = acc / lr, LSE = ln2 * (m + log2 l). O is divided by the sum of the very
   // values P V was formed with, so the weights that multiply V sum to one: the rounding of a
   // dominant weight to the input type then cancels instead of scaling the whole row. The LSE
-  // keeps the unrounded sum.
+  // keeps the unrounded sum. A row that saw no key (a band can leave one empty) has both sums
+  // zero: O = 0 and LSE = -inf.
   const float l_tot = wave_half_sum(l_run);
   const float lr_tot = wave_half_sum(lr_run);
-  if (qrow < N) {
-    const float inv = 1.0f / lr_tot;
-    const int64_t obase = ((int64_t)(b * p.Hq + hq) * N + qrow) * D;
+  if (qrow < Nq) {
+    const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+    const int64_t obase = ((int64_t)(b * p.Hq + hq) * Nq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -596,7 +636,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
           *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){E::pack2(o0, o1), E::pack2(o2, o3)};
         }
       }
-    if (h == 0) p.lse[(int64_t)(b * p.Hq + hq) * N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    if (h == 0)
+      p.lse[(int64_t)(b * p.Hq + hq) * Nq + qrow] =
+          l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
   }
 }
 

@@ -92,6 +92,29 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, fa_dtype in_dtype, fa_dtype out_dtype,
                  void* stream);
 
+/*
+ * fa_fwd_ex — fa_fwd with separate query and key lengths and a sliding-window
+ * band. The intelliparadigm page's operator bounds a window with pre_tokens
+ * and next_tokens (section 2.2) and tiles with separate query and key
+ * lengths (section 2.3). Query row i sits at key position i + (Nk - Nq), so
+ * its diagonal is aligned with the end of the key sequence, and it sees key j
+ * iff
+ *
+ *   i + (Nk - Nq) - window_left  <=  j  <=  i + (Nk - Nq) + window_right
+ *
+ * A negative edge is unlimited. fa_fwd(causal = 1) is Nq = Nk with
+ * window_left = -1 and window_right = 0; fa_fwd(causal = 0) has both edges
+ * unlimited. A row that sees no key gets O = 0 and lse = -inf.
+ *
+ *   q, o      [B][Hq][Nq][d];  lse [B][Hq][Nq];  k, v [B][Hkv][Nk][d]
+ *   Nq, Nk    >= 1, each with N*d at most 2^30 - 2^16
+ * Other arguments, errors and execution as fa_fwd.
+ */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                    float scale, int64_t window_left, int64_t window_right,
+                    fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 
@@ -147,9 +170,23 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* stream);
 
 /*
- * fa_bwd_workspace_bytes — size in bytes of the workspace fa_bwd needs for
- * these sizes (two floats per query row, rows padded to a multiple of 128),
- * or 0 when the sizes are invalid for fa_bwd. Makes no HIP call.
+ * fa_bwd_ex — fa_bwd for fa_fwd_ex: separate query and key lengths and the
+ * same band. q, o, dout and dq are [B][Hq][Nq][d], lse [B][Hq][Nq], k, v, dk
+ * and dv [B][Hkv][Nk][d]; the workspace is fa_bwd_workspace_bytes(B, Hq, Nq,
+ * d) bytes. Rows that see no key contribute nothing and get dq = 0; keys no
+ * row sees get dk = dv = 0. Other arguments, errors and execution as fa_bwd.
+ */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, float* dq, float* dk, float* dv, float* workspace,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                    float scale, int64_t window_left, int64_t window_right,
+                    fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes — size in bytes of the workspace fa_bwd (or
+ * fa_bwd_ex, with N = Nq) needs for these sizes (two floats per query row,
+ * rows padded to a multiple of 128), or 0 when the sizes are invalid for
+ * fa_bwd. Makes no HIP call.
  */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d);
 

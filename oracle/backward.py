@@ -97,7 +97,7 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
 
 def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                                   o_used: np.ndarray, scale: float, causal: bool, u: float,
-                                  e32: float = 2.0 ** -24
+                                  e32: float = 2.0 ** -24, band: Optional[Tuple] = None
                                   ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """First-order elementwise error bounds (Bq [n,d], Bk [N,d], Bv [N,d]) for one head's
     gradients computed the way a tiled kernel does: S, dP and D accumulated in fp32 (unit
@@ -115,6 +115,7 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
       Bk = s sum_i [(u + rho_ij + n e32) |dS_ij| + P_ij eta_ij] |Q_ic|
     (a product sum_k a_k b_k whose factor a_k carries a relative error e moves by at most
     e sum_k |a_k b_k|; an fp32 sum of m terms by at most m e32 times the sum of magnitudes).
+    ``band`` = (left, right, off) replaces ``causal`` by the band of ``attention.band_visible``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -123,7 +124,10 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
     o_used = np.asarray(o_used, dtype=np.float64)
     n, N = q.shape[0], k.shape[0]
     d = q.shape[1]
-    O, lse = head_attention_fp64(q, k, v, scale, causal)
+    if band is None:
+        O, lse = head_attention_fp64(q, k, v, scale, causal)
+    else:
+        O, lse = head_attention_band_fp64(q, k, v, scale, *band)
     d_dev = np.abs(np.sum(do * (o_used - O), axis=1))
     d_mag = np.sum(np.abs(do * O), axis=1)
     bq = np.zeros(q.shape)
@@ -132,12 +136,18 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
     g_d = d * e32
     for r0 in range(0, n, ROW_BLOCK):
         r1 = min(n, r0 + ROW_BLOCK)
-        kend = N if not causal else min(N, r1)
+        kend = N if (band is not None or not causal) else min(N, r1)
         S = scale * (q[r0:r1] @ k[:kend].T)
-        if causal:
-            hidden = np.arange(kend)[None, :] > np.arange(r0, r1)[:, None]
-            S = np.where(hidden, -np.inf, S)
-        P = np.exp(S - lse[r0:r1, None])
+        if band is not None:
+            vis = band_visible(np.arange(r0, r1), np.arange(kend), band[0], band[1], band[2])
+            seen = np.isfinite(lse[r0:r1])
+            P = np.where(vis & seen[:, None],
+                         np.exp(np.where(vis, S, 0.0) - np.where(seen, lse[r0:r1], 0.0)[:, None]), 0.0)
+        else:
+            if causal:
+                hidden = np.arange(kend)[None, :] > np.arange(r0, r1)[:, None]
+                S = np.where(hidden, -np.inf, S)
+            P = np.exp(S - lse[r0:r1, None])
         dP = do[r0:r1] @ v[:kend].T
         D = np.sum(P * dP, axis=1)
         dS = np.abs(P * (dP - D[:, None]))

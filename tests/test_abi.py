@@ -168,3 +168,52 @@ def test_bwd_binding_has_no_cpu_path():
     lse = torch.zeros(1, 1, 8, dtype=torch.float32)
     with pytest.raises(bnd.FaError):
         bnd.bwd(q, q, q, o, lse, q)
+
+
+# ---------------------------------------------------------------- banded entry points
+
+def call_fwd_ex(**kw):
+    a = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, B=1, Hq=2, Hkv=1, Nq=64, Nk=80, d=64, scale=0.125, left=-1,
+             right=0, in_dtype=bnd.FA_F16, out_dtype=bnd.FA_F32)
+    a.update(kw)
+    return bnd.fwd_ex_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                          a["d"], a["scale"], a["left"], a["right"], a["in_dtype"], a["out_dtype"], 0)
+
+
+def call_bwd_ex(**kw):
+    a = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, dout=BAD, dq=BAD, dk=BAD, dv=BAD, ws=BAD, B=1, Hq=2, Hkv=1,
+             Nq=64, Nk=80, d=64, scale=0.125, left=16, right=-1, in_dtype=bnd.FA_BF16, o_dtype=bnd.FA_F32)
+    a.update(kw)
+    return bnd.bwd_ex_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["ws"],
+                          a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["left"], a["right"],
+                          a["in_dtype"], a["o_dtype"], 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fwd_ex_null_pointers(which):
+    assert call_fwd_ex(**{which: 0}) == bnd.FA_ERR_NULLPTR
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(Nk=0), dict(Nk=((1 << 30) - (1 << 16)) // 64 + 1),
+                                dict(Hq=3, Hkv=2), dict(scale=0.0)])
+def test_fwd_ex_shape_errors(kw):
+    assert call_fwd_ex(**kw) == bnd.FA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(left=5, right=5), dict(left=-7, right=-1), dict(left=1 << 40, right=0),
+                                dict(Nq=1, Nk=4096)])
+def test_fwd_ex_any_window_passes_validation(kw):
+    # every window value is valid (negative or huge edges mean unlimited): only alignment stops it
+    assert call_fwd_ex(**kw) == bnd.FA_ERR_ALIGN
+
+
+@pytest.mark.parametrize("which", ["q", "dout", "dq", "dk", "ws"])
+def test_bwd_ex_null_pointers(which):
+    assert call_bwd_ex(**{which: 0}) == bnd.FA_ERR_NULLPTR
+
+
+def test_bwd_ex_validation_order():
+    assert call_bwd_ex(Nk=0) == bnd.FA_ERR_SHAPE
+    assert call_bwd_ex(d=96) == bnd.FA_ERR_UNSUPPORTED
+    assert call_bwd_ex(o_dtype=bnd.FA_F16) == bnd.FA_ERR_UNSUPPORTED
+    assert call_bwd_ex() == bnd.FA_ERR_ALIGN
