@@ -100,14 +100,14 @@ def time_gpu(w, steps: int, warmup: int):
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=out, lse=lse, stream=stream)
+        fa.fwd(q, k, v, scale=w.scale, window=w.band, out=out, lse=lse, stream=stream)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
-        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=out, lse=lse, stream=stream)
+        fa.fwd(q, k, v, scale=w.scale, window=w.band, out=out, lse=lse, stream=stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -132,7 +132,7 @@ def time_gpu_bwd(w, steps: int, warmup: int):
     q, k, v = (to_device(x, w.dtype, dev) for x in (qkv.q, qkv.k, qkv.v))
     del qkv
     dout = to_device(I.draw_dout(w.B, w.Hq, w.N, w.d, w.dtype, w.seed + 1000), w.dtype, dev)
-    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    o, lse = fa.fwd(q, k, v, scale=w.scale, window=w.band)
     ws = torch.empty(binding.bwd_workspace_bytes(w.B, w.Hq, w.N, w.d), dtype=torch.uint8, device=dev)
     grads = (torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev),
              torch.empty((w.B, w.Hkv, w.N, w.d), dtype=torch.float32, device=dev),
@@ -140,7 +140,7 @@ def time_gpu_bwd(w, steps: int, warmup: int):
     stream = torch.cuda.current_stream(dev)
 
     def call():
-        fa.bwd(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, workspace=ws, grads=grads, stream=stream)
+        fa.bwd(q, k, v, o, lse, dout, scale=w.scale, window=w.band, workspace=ws, grads=grads, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -178,7 +178,8 @@ def bwd_line(w, args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs and dO; PCG64)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "in_dtype": w.dtype, "grad_dtype": "f32", "o_dtype": "f32",
+                   "causal": w.causal, "window_left": w.window_left, "in_dtype": w.dtype, "grad_dtype": "f32",
+                   "o_dtype": "f32",
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
@@ -217,6 +218,8 @@ def cpu_baseline(w, budget_s: float = 12.0):
     from exact_attention_114_amd import inputs as I
     from oracle.pool import attention_rows_pool, available_cores
 
+    if w.window_left is not None:
+        return None  # the pooled oracle covers the causal and unmasked forms; the bench line is GQA
     qkv = I.workload_qkv(w)
     cores = max(1, min(16, available_cores()))
     rows_per_unit = 1024
@@ -372,7 +375,8 @@ def main():
         "data": "synthetic (seeded N(0,1), K x2; PCG64 seed %d)" % w.seed if w.k_mult != 1.0
         else "synthetic (seeded N(0,1); PCG64 seed %d)" % w.seed,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "in_dtype": w.dtype, "out_dtype": "f32", "scale": w.scale,
+                   "causal": w.causal, "window_left": w.window_left, "in_dtype": w.dtype, "out_dtype": "f32",
+                   "scale": w.scale,
                    "block_m": bm, "block_n": bn, "grid": grid, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",

@@ -49,10 +49,24 @@ class Workload:
     scale: float  # passed to the kernel as a float32
     seed: int
     k_mult: float = 1.0  # exact power-of-two multiplier applied to K before rounding
+    window_left: Optional[int] = None  # causal sliding window: row i sees keys i - window_left .. i
+
+    @property
+    def band(self):
+        """(left, right) edges for the binding: causal, a causal window, or unmasked."""
+        if self.window_left is not None:
+            return (self.window_left, 0)
+        return (None, 0) if self.causal else (None, None)
 
     @property
     def flops(self) -> float:
-        """Algorithmic FLOPs: two N x N x d contractions, halved when causal."""
+        """Algorithmic FLOPs: 4 d per visible (query, key) pair: two N x N x d contractions,
+        halved when causal, over the band when windowed."""
+        if self.window_left is not None:
+            w, n = self.window_left, self.N
+            m = min(w, n)
+            pairs = m * (m + 1) / 2.0 + (n - m) * (w + 1.0)
+            return 4.0 * self.B * self.Hq * self.d * pairs
         f = 4.0 * self.B * self.Hq * self.N * self.N * self.d
         return f / 2.0 if self.causal else f
 
@@ -80,6 +94,10 @@ WORKLOADS: Dict[str, Workload] = {
         _c4(1024), _c4(2048), _c4(4096), _c4(8192), _c4(16384),
         Workload("gqa_causal_b4_hq32_hkv8_n8192_d128_bf16", 4, 32, 8, 8192, 128, BF16, True,
                  1.0 / math.sqrt(128.0), 5, k_mult=2.0),
+        # the walkthrough's benchmark shape under the operator's sliding window
+        # (pre_tokens = 2048, next_tokens = 0; intelliparadigm page, section 2.2)
+        Workload("window_b4_h48_n16384_d64_f16_w2048", 4, 48, 48, 16384, 64, F16, True, 0.125, 46,
+                 window_left=2048),
     ]
 }
 

@@ -129,3 +129,26 @@ def test_bwd_band(Nq, Nk, left, right, d, dt):
         assert np.isfinite(g).all(), f"non-finite {name}"
         ratio = (np.abs(g - r) / np.maximum(2.0 * b, 1e-300)).max()
         assert ratio <= 1.0, f"{name} error reaches {ratio:.3f} of the bar"
+
+
+def test_window_workload_sampled_rows():
+    """The full-size sliding-window workload as the benchmark times it, on rows the oracle
+    computes one by one (rows at the window's edge and spread over the sequence)."""
+    from oracle.attention import head_attention_band_fp64
+
+    w = I.WORKLOADS["window_b4_h48_n16384_d64_f16_w2048"]
+    qkv = I.workload_qkv(w)
+    print(f"[gpu] fa_fwd_ex {w.name}", flush=True)
+    O, L = fa.fwd(*(to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v)), scale=w.scale, window=w.band)
+    torch.cuda.synchronize()
+    O = O.cpu().numpy()
+    L = L.cpu().numpy()
+    rng = np.random.Generator(np.random.PCG64(7))
+    rows = np.unique(np.concatenate([[0, 1, 2047, 2048, 2049, 8191, w.N - 1], rng.integers(0, w.N, 24)]))
+    for b, h in [(0, 0), (1, 17), (3, 47)]:
+        q = I.bits_to_f64(qkv.q[b, h][rows], w.dtype)
+        k = I.bits_to_f64(qkv.k[b, h], w.dtype)
+        v = I.bits_to_f64(qkv.v[b, h], w.dtype)
+        O_ref, L_ref = head_attention_band_fp64(q, k, v, I.scale_f32(w.scale), w.window_left, 0, q_pos=rows)
+        check_fwd(O[b, h][rows].astype(np.float64), L[b, h][rows].astype(np.float64), O_ref, L_ref, w.dtype,
+                  f"{w.name} head ({b},{h})")
