@@ -35,6 +35,9 @@ SIGNATURES = {
                   + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_bwd_ex": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                   + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [ctypes.c_float]
+                     + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
 }
 
 _lib = None
@@ -95,6 +98,19 @@ def fwd_ex_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: int, Hkv: i
                                     in_dtype, out_dtype, stream)
 
 
+def fwd_split_raw(q: int, k: int, v: int, o: int, lse: int, ws: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int,
+                  d: int, scale: float, left: int, right: int, n_splits: int, in_dtype: int, out_dtype: int,
+                  stream: int = 0) -> int:
+    """Call fa_fwd_split with raw device addresses; returns the fa_status code."""
+    return load_library().fa_fwd_split(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right,
+                                       n_splits, in_dtype, out_dtype, stream)
+
+
+def split_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: int) -> int:
+    """Bytes of workspace fa_fwd_split needs (0: it would not split)."""
+    return int(load_library().fa_fwd_split_workspace_bytes(B, Hq, Nq, Nk, d, n_splits))
+
+
 def _edges(causal: bool, window) -> Tuple[int, int]:
     """(left, right) band edges for the C ABI, -1 meaning unlimited."""
     if window is None:
@@ -114,7 +130,7 @@ def tile(B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool, in_dtype: int)
 
 
 def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=None, out_dtype=None,
-        out=None, lse=None, stream=None):
+        out=None, lse=None, splits: Optional[int] = None, workspace=None, stream=None):
     """Exact attention forward on the GPU: returns (O, LSE).
 
     q: [B, Hq, Nq, d], k and v: [B, Hkv, Nk, d], contiguous fp16 or bf16 CUDA
@@ -122,7 +138,9 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
     out_dtype defaults to float32 (or pass q.dtype); LSE is float32 [B, Hq, Nq].
     causal=True, or window=(left, right) (None for an unlimited edge), bands the
     keys as fa_fwd_ex does: query row i sees keys i + Nk - Nq - left ..
-    i + Nk - Nq + right. Runs on ``stream`` (a torch stream) or torch's current stream.
+    i + Nk - Nq + right. splits (0 = automatic, or a chunk count up to 16) cuts each
+    Q-tile's keys into chunks merged afterwards (fa_fwd_split); its workspace is
+    allocated when not given. Runs on ``stream`` (a torch stream) or torch's current stream.
     """
     import torch
 
@@ -164,6 +182,16 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
         raise FaError(FA_ERR_SHAPE, "all tensors must be on one device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if splits is not None:
+        need = split_workspace_bytes(B, Hq, N, Nk, d, int(splits))
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        if workspace.device != q.device or workspace.numel() * workspace.element_size() < need:
+            raise FaError(FA_ERR_SHAPE, f"workspace must hold {need} bytes on the inputs' device")
+        _check(fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             workspace.data_ptr(), B, Hq, Hkv, N, Nk, d, scale, left, right, int(splits), in_code,
+                             out_code, stream.cuda_stream))
+        return out, lse
     _check(fwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, Nk, d, scale, left, right, in_code, out_code, stream.cuda_stream))
     return out, lse

@@ -7,6 +7,7 @@
 // flattened to one dimension so the kernel can remap work-groups onto XCDs.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -32,6 +33,22 @@ int key_blocks(int64_t d, int64_t grid) { return d == 128 && grid > kOneBlockMin
 
 // A band edge of this size or more is unlimited: every in-range index difference is smaller.
 constexpr int kUnlimited = 1 << 30;
+
+// Split keys: at most this many chunks per Q-tile, each a whole number of 64-key tiles and at
+// least two of them; splitting aims at two work-groups per CU.
+constexpr int kMaxSplits = 16;
+constexpr int64_t kSplitTarget = 2 * 256;
+
+// Chunks for a problem (requested: 0 = automatic) and the keys per chunk.
+void split_plan(int64_t grid, int64_t Nk, int requested, int* nsplit, int* kchunk) {
+  const int64_t tiles64 = (Nk + 63) / 64;
+  int64_t s = requested > 0 ? requested : (grid >= kSplitTarget ? 1 : (kSplitTarget + grid - 1) / grid);
+  s = std::min<int64_t>(s, kMaxSplits);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles64 / 2));
+  const int64_t chunk = ((tiles64 + s - 1) / s) * 64;
+  *kchunk = (int)chunk;
+  *nsplit = (int)((Nk + chunk - 1) / chunk);
+}
 
 template <bool BF16, int D, bool BAND, bool OUT_F32, int KB>
 fa_status launch(const fa::Params& p, hipStream_t stream) {
@@ -119,6 +136,8 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   p.right = window_right < 0 || window_right >= kUnlimited ? kUnlimited : (int)window_right;
   p.group = (int)(Hq / Hkv);
   p.n_qtiles = (int)nq;
+  p.nsplit = 1;
+  p.kchunk = (int)(((Nk + 63) / 64) * 64);
   p.total_wg = (int)grid;
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
 
@@ -137,6 +156,86 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, -1, causal ? 0 : -1, in_dtype, out_dtype, stream);
+}
+
+size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int n_splits) {
+  int64_t nq = 0, grid = 0;
+  if (n_splits < 0 || n_splits > kMaxSplits) return 0;
+  if (check_problem(B, Hq, 1, Nq, Nk, d, FA_F16, &nq, &grid) != FA_OK) return 0;
+  int ns = 1, kc = 0;
+  split_plan(grid, Nk, n_splits, &ns, &kc);
+  if (ns == 1) return 0;
+  return (size_t)(ns * B * Hq * Nq * (d + 1) * (int64_t)sizeof(float));
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                       int64_t window_left, int64_t window_right, int n_splits, fa_dtype in_dtype,
+                       fa_dtype out_dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+  if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
+  int64_t nq = 0, grid = 0;
+  fa_status st = check_problem(B, Hq, Hkv, Nq, Nk, d, in_dtype, &nq, &grid);
+  if (st != FA_OK) return st;
+  int ns = 1, kc = 0;
+  split_plan(grid, Nk, n_splits, &ns, &kc);
+  if (ns == 1)
+    return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, in_dtype, out_dtype,
+                     stream);
+  if (!workspace) return FA_ERR_NULLPTR;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
+  if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const int64_t rows = B * Hq * Nq;
+  if (grid * ns >= ((int64_t)1 << 31) || rows * d * ns >= ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+
+  fa::Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = workspace;                      // ns planes of fp32 O [rows][d]
+  p.lse = workspace + ns * rows * d;    // then ns planes of fp32 LSE [rows]
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.off = (int)(Nk - Nq);
+  p.left = window_left < 0 || window_left >= kUnlimited ? kUnlimited : (int)window_left;
+  p.right = window_right < 0 || window_right >= kUnlimited ? kUnlimited : (int)window_right;
+  p.group = (int)(Hq / Hkv);
+  p.n_qtiles = (int)nq;
+  p.nsplit = ns;
+  p.kchunk = kc;
+  p.total_wg = (int)(grid * ns);
+  p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  const bool band = p.left != kUnlimited || p.right != kUnlimited;
+  const bool bf16 = in_dtype == FA_BF16;
+  const int kb = key_blocks(d, grid * ns);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = bf16 ? dispatch_d<true>(p, (int)d, band, true, kb, s) : dispatch_d<false>(p, (int)d, band, true, kb, s);
+  if (st != FA_OK) return st;
+  const int rows_per_wg = 256 / (int)(d / 4);
+  const dim3 mg((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+  const float* ow = workspace;
+  const float* lw = workspace + ns * rows * d;
+  const bool f32 = out_dtype == FA_F32;
+#define FA_MERGE(BF, DD, F32) hipLaunchKernelGGL((fa::fa_merge_kernel<BF, DD, F32>), mg, dim3(256), 0, s, ow, lw, o, lse, rows, ns)
+  if (d == 64) {
+    if (f32) { if (bf16) FA_MERGE(true, 64, true); else FA_MERGE(false, 64, true); }
+    else { if (bf16) FA_MERGE(true, 64, false); else FA_MERGE(false, 64, false); }
+  } else {
+    if (f32) { if (bf16) FA_MERGE(true, 128, true); else FA_MERGE(false, 128, true); }
+    else { if (bf16) FA_MERGE(true, 128, false); else FA_MERGE(false, 128, false); }
+  }
+#undef FA_MERGE
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    fa::last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
 }
 
 fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, fa_dtype in_dtype,

@@ -46,6 +46,10 @@
 //      K/V tiles a Q-tile's band touches are loaded and computed, and only tiles crossing a
 //      band edge (or the ragged end of the keys) are masked. A row that sees no key gets
 //      O = 0 and LSE = -inf.
+//   6. Split keys. When batch x heads x Q-tiles leaves the GPU under-filled, the keys of each
+//      Q-tile can be cut into chunks handled by separate work-groups (the FA2 walkthrough's
+//      point about adding parallelism along the sequence when batch and heads are small); each
+//      writes its chunk's normalised O and LSE, and a merge kernel combines them.
 //
 // Software pipeline. A wave's softmax is VALU work and its two products are MFMA
 // work; on gfx950 an MFMA leaves the issue port free for about four VALU
@@ -97,7 +101,9 @@ struct Params {
   int left, right;  // band edges (the host passes 1 << 30 for an unlimited edge)
   int group;     // Hq / Hkv
   int n_qtiles;  // ceil(Nq / BM)
-  int total_wg;  // B * Hq * n_qtiles
+  int nsplit;    // key chunks per Q-tile (1: none); chunk s covers keys [s*kchunk, (s+1)*kchunk)
+  int kchunk;    // keys per chunk, a multiple of 64 (every key-tile size)
+  int total_wg;  // B * Hq * n_qtiles * nsplit
   float c;       // scale * log2(e)
 };
 
@@ -245,7 +251,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const int wg = blockIdx.x;
   const int xcd = wg & 7, local = wg >> 3;
   const int per = p.total_wg >> 3, rem = p.total_wg & 7;
-  const int L = xcd * per + min(xcd, rem) + local;
+  const int LS = xcd * per + min(xcd, rem) + local;
+  const int split = LS % p.nsplit;  // the key chunk (0 when keys are not split)
+  const int L = LS / p.nsplit;
   const int G = p.group;
   const int per_kv = p.n_qtiles * G;
   const int bk = L / per_kv;  // b * Hkv + hkv
@@ -257,6 +265,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const int hkv = bk - b * p.Hkv;
   const int hq = hkv * G + g;
   const int Nq = p.Nq, Nk = p.Nk;
+
+  // outputs: with split keys, chunk s writes fp32 O and LSE into its own plane (the host
+  // passes the workspace and an fp32 output then)
+  const int64_t rows_all = (int64_t)p.B * p.Hq * Nq;
+  float* const Of = (float*)p.o + (int64_t)split * rows_all * D;
+  float* const Ls = p.lse + (int64_t)split * rows_all;
 
   using T = unsigned short;
   const T* __restrict__ Qp = (const T*)p.q + ((int64_t)(b * p.Hq + hq)) * Nq * D;
@@ -356,12 +370,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const int qrow = q0w + l32;  // this lane's query row
   const int qr = min(qrow, Nq - 1);  // rows past Nq behave as the last row (never stored)
   // the K/V tiles the Q-tile's band touches: [j_lo, j_lo + nt)
-  const int lo_t = BAND ? max(0, q0 + p.off - p.left) : 0;
-  const int hi_t = BAND ? min(Nk - 1, min(q0 + BM, Nq) - 1 + p.off + p.right) : Nk - 1;
+  // keys this work-group may use: its chunk [split*kchunk, kend) (all keys when not split)
+  const int kend = min(Nk, (split + 1) * p.kchunk);
+  const int lo_t = max(split * p.kchunk, BAND ? q0 + p.off - p.left : 0);
+  const int hi_t = min(kend - 1, BAND ? min(q0 + BM, Nq) - 1 + p.off + p.right : Nk - 1);
   const int j_lo = lo_t / BN;
   const int nt = hi_t >= lo_t ? hi_t / BN - j_lo + 1 : 0;
-  // the lane's visible keys: [klo, khi]
-  const int khi = BAND ? min(Nk - 1, qr + p.off + p.right) : Nk - 1;
+  // the lane's visible keys: [klo, khi]. khi also stops at the chunk's end: the steps run past
+  // the last tile (and, with split keys, into the next chunk) must add nothing.
+  const int khi = BAND ? min(kend - 1, qr + p.off + p.right) : kend - 1;
   const int klo = BAND ? qr + p.off - p.left : 0;
   if (nt == 0) {
     // no row of this Q-tile sees a key: O = 0, LSE = -inf
@@ -371,11 +388,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
       for (int c8 = 0; c8 < D / 2; c8 += 4) {
         const int dcol = 2 * c8 + 4 * h;  // lanes h = 0, 1 cover alternate groups of 4
         if (OUT_F32)
-          *(f32x4*)((float*)p.o + obase + dcol) = (f32x4){0.f, 0.f, 0.f, 0.f};
+          *(f32x4*)(Of + obase + dcol) = (f32x4){0.f, 0.f, 0.f, 0.f};
         else
           *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){0u, 0u};
       }
-      if (h == 0) p.lse[(int64_t)(b * p.Hq + hq) * Nq + qrow] = -__builtin_inff();
+      if (h == 0) Ls[(int64_t)(b * p.Hq + hq) * Nq + qrow] = -__builtin_inff();
     }
     return;
   }
@@ -430,14 +447,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     const lds_char* kread = PAR ? K0 : K1;  // K_{j+1}
     const lds_char* vread = PAR ? V0 : V1;  // V_{j-1}
 
-    // ---- mask S_j: keys outside the lane's band [klo, khi] (khi also stops at the last key).
+    // ---- mask S_j: keys outside the lane's band [klo, khi] (khi also stops at the chunk's last key).
     // In the S^T layout element i of block kb holds key kbase + 32kb + 8(i/4) + 4h + i%4: two
     // per-lane thresholds on the constant part. A tile needs masking when it crosses the wave's
     // band edges or the end of the keys.
     const int kbase = j * BN;
     const bool need_mask = (BAND && (kbase + BN - 1 > min(q0w, Nq - 1) + p.off + p.right ||
                                      kbase < min(q0w + 31, Nq - 1) + p.off - p.left)) ||
-                           (kbase + BN > Nk);
+                           (kbase + BN > kend);
     auto mask = [&](f32x16(&st)[KB]) {
       const int hi = khi - kbase - 4 * h;  // hide if part > hi
       const int lo = klo - kbase - 4 * h;  // hide if part < lo
@@ -631,15 +648,47 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
         const float o0 = acc_o[db][4 * g4 + 0] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
         const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;
         if (OUT_F32) {
-          *(f32x4*)((float*)p.o + obase + dcol) = (f32x4){o0, o1, o2, o3};
+          *(f32x4*)(Of + obase + dcol) = (f32x4){o0, o1, o2, o3};
         } else {
           *(u32x2*)((unsigned short*)p.o + obase + dcol) = (u32x2){E::pack2(o0, o1), E::pack2(o2, o3)};
         }
       }
     if (h == 0)
-      p.lse[(int64_t)(b * p.Hq + hq) * Nq + qrow] =
+      Ls[(int64_t)(b * p.Hq + hq) * Nq + qrow] =
           l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
   }
+}
+
+// Merge of split-key partials (the online-softmax combination of partial results: the cnblogs
+// page's running maximum and denominator, applied to whole chunks). For a row with chunk
+// results (O_s, LSE_s): LSE = ln sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s; chunks whose
+// keys the row cannot see carry LSE_s = -inf and weigh nothing, and a row that sees no key
+// keeps O = 0 and LSE = -inf. D/4 lanes per row, 4 columns each.
+template <bool BF16, int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ ow, const float* __restrict__ lw,
+                                                       void* o, float* lse, int64_t rows, int nsplit) {
+  using E = Elt<BF16>;
+  constexpr int TPR = D / 4;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c4 = (threadIdx.x % TPR) * 4;
+  if (row >= rows) return;
+  float m = -__builtin_inff();
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lw[s * rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (m != -__builtin_inff()) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float wgt = __expf(lw[s * rows + row] - m);
+      den += wgt;
+      acc += wgt * *(const f32x4*)(ow + (s * rows + row) * D + c4);
+    }
+    acc *= 1.0f / den;
+  }
+  if (OUT_F32)
+    *(f32x4*)((float*)o + row * D + c4) = acc;
+  else
+    *(u32x2*)((unsigned short*)o + row * D + c4) = (u32x2){E::pack2(acc[0], acc[1]), E::pack2(acc[2], acc[3])};
+  if (c4 == 0) lse[row] = m == -__builtin_inff() ? m : m + __logf(den);
 }
 
 }  // namespace fa

@@ -115,6 +115,40 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int64_t window_left, int64_t window_right,
                     fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
 
+/*
+ * fa_fwd_split — fa_fwd_ex with the keys of every Q-tile cut into chunks that
+ * separate work-groups process, for problems whose batch x heads x Q-tiles
+ * leaves the GPU under-filled (the FA2 walkthrough: parallelism along the
+ * sequence when batch and heads are small; the intelliparadigm page's
+ * hierarchical tiling of long sequences, section 6.1). Each chunk's
+ * normalised O and LSE go to the workspace, and a merge kernel combines them
+ * with the online-softmax rule: LSE = ln sum_s exp(LSE_s) and
+ * O = sum_s exp(LSE_s - LSE) O_s.
+ *
+ *   n_splits   0: automatic (aims at two work-groups per CU); otherwise the
+ *              number of chunks wanted, at most 16. Chunks are whole 64-key
+ *              tiles, at least two, so fewer may be used.
+ *   workspace  device pointer to fa_fwd_split_workspace_bytes(...) bytes,
+ *              16-byte aligned, owned by the caller. It may be NULL when that
+ *              size is 0, which means no split: the call is then fa_fwd_ex.
+ * Other arguments, errors and execution as fa_fwd_ex. The result equals
+ * fa_fwd_ex's up to rounding order. Calls that share a workspace must not
+ * run concurrently.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       float* workspace, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                       int64_t Nk, int64_t d, float scale, int64_t window_left,
+                       int64_t window_right, int n_splits, fa_dtype in_dtype,
+                       fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_fwd_split_workspace_bytes — bytes of workspace fa_fwd_split needs
+ * (chunks x rows x (d + 1) floats), 0 when it would not split (or the
+ * arguments are invalid). Makes no HIP call.
+ */
+size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d,
+                                    int n_splits);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 

@@ -217,3 +217,39 @@ def test_bwd_ex_validation_order():
     assert call_bwd_ex(d=96) == bnd.FA_ERR_UNSUPPORTED
     assert call_bwd_ex(o_dtype=bnd.FA_F16) == bnd.FA_ERR_UNSUPPORTED
     assert call_bwd_ex() == bnd.FA_ERR_ALIGN
+
+
+# ---------------------------------------------------------------- split keys
+
+def test_split_workspace_bytes():
+    # automatic: a grid of 16 Q-tiles (1 x 16 heads x 1 tile) wants 512 / 16 = 32 chunks, capped at
+    # 16 and at half the 64-key tiles (2048 keys: 32 tiles -> 16): 16 chunks of 128 keys
+    assert bnd.split_workspace_bytes(1, 16, 100, 2048, 128, 0) == 16 * 16 * 100 * 129 * 4
+    assert bnd.split_workspace_bytes(1, 16, 100, 2048, 128, 3) == 3 * 16 * 100 * 129 * 4
+    # a full grid does not split; a short key range cannot
+    assert bnd.split_workspace_bytes(4, 32, 8192, 8192, 128, 0) == 0
+    assert bnd.split_workspace_bytes(1, 1, 64, 100, 64, 0) == 0
+    # requested splits are bounded by the 64-key tiles: 256 keys -> 4 tiles -> 2 chunks
+    assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 8) == 2 * 1 * 10 * 65 * 4
+    assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 17) == 0
+    assert bnd.split_workspace_bytes(1, 1, 10, 256, 96, 2) == 0
+
+
+def test_split_validation():
+    lib = bnd.load_library()
+    args = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, ws=BAD, B=1, Hq=2, Hkv=1, Nq=64, Nk=4096, d=64, scale=0.125,
+                left=-1, right=0, ns=4, i=bnd.FA_F16, o_=bnd.FA_F32)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return bnd.fwd_split_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["B"], a["Hq"], a["Hkv"],
+                                 a["Nq"], a["Nk"], a["d"], a["scale"], a["left"], a["right"], a["ns"], a["i"],
+                                 a["o_"], 0)
+    assert call(q=0) == bnd.FA_ERR_NULLPTR
+    assert call(ws=0) == bnd.FA_ERR_NULLPTR          # a split needs its workspace
+    assert call(ns=-1) == bnd.FA_ERR_SHAPE
+    assert call(ns=17) == bnd.FA_ERR_SHAPE
+    assert call(d=96) == bnd.FA_ERR_UNSUPPORTED
+    assert call() == bnd.FA_ERR_ALIGN
+    assert call(ws=0, Nk=64) == bnd.FA_ERR_ALIGN     # no split possible: the workspace is not needed
