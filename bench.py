@@ -6,10 +6,14 @@ the hot path: work decomposition, K/V streaming, Q K^T, masked online softmax,
 P V, epilogue with O and LSE). Inputs are seeded synthetic data already resident
 in HBM when the timed region starts. Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits S]
                   [--no-cpu-baseline] [--calibrate-copy] [--sweep]
 
---sweep additionally prints one line per workload (for tables; not the bench line).
+--splits S cuts each Q-tile's keys into S chunks merged by their LSEs (fa_fwd_split; the
+merge kernel is then part of the step); 0, the default, lets the library choose, which keeps
+one chunk on grids that already fill the chip; 1 never splits.
+--sweep additionally prints one line per workload (for tables; not the bench line), and for
+workloads the library splits, a second line without the split.
 --bwd measures the backward pass (fa_bwd) on the workload instead and prints its own line:
 one step = one fa_bwd call (row statistics, dK/dV and dQ kernels) with O and LSE from fa_fwd.
 --calibrate-copy runs, after the timed region, one elementwise copy kernel of a known
@@ -80,16 +84,25 @@ def to_device(bits, dtype_name, dev):
 def algorithmic_bytes(w) -> float:
     """Unique HBM bytes of one launch: Q, K, V read once, O (fp32) and LSE written once."""
     q = w.B * w.Hq * w.N * w.d * 2
-    kv = 2 * w.B * w.Hkv * w.N * w.d * 2
+    kv = 2 * w.B * w.Hkv * w.nk * w.d * 2
     o = w.B * w.Hq * w.N * w.d * 4
     lse = w.B * w.Hq * w.N * 4
     return float(q + kv + o + lse)
 
 
-def time_gpu(w, steps: int, warmup: int):
+def planned_splits(w, splits: int) -> int:
+    """The key-chunk count fa_fwd_split runs with for this request (1: no split)."""
+    from exact_attention_114_amd import binding
+
+    ws = binding.split_workspace_bytes(w.B, w.Hq, w.N, w.nk, w.d, splits)
+    return ws // (w.B * w.Hq * w.N * (w.d + 1) * 4) if ws else 1
+
+
+def time_gpu(w, steps: int, warmup: int, splits: int = 0):
     import torch
 
     import exact_attention_114_amd as fa
+    from exact_attention_114_amd import binding
     from exact_attention_114_amd import inputs as I
 
     dev = torch.device("cuda:0")
@@ -98,16 +111,23 @@ def time_gpu(w, steps: int, warmup: int):
     del qkv
     out = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    ws_bytes = binding.split_workspace_bytes(w.B, w.Hq, w.N, w.nk, w.d, splits)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+
+    def call():
+        fa.fwd(q, k, v, scale=w.scale, window=w.band, out=out, lse=lse, splits=splits, workspace=ws,
+               stream=stream)
+
     for _ in range(warmup):
-        fa.fwd(q, k, v, scale=w.scale, window=w.band, out=out, lse=lse, stream=stream)
+        call()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
-        fa.fwd(q, k, v, scale=w.scale, window=w.band, out=out, lse=lse, stream=stream)
+        call()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -135,8 +155,8 @@ def time_gpu_bwd(w, steps: int, warmup: int):
     o, lse = fa.fwd(q, k, v, scale=w.scale, window=w.band)
     ws = torch.empty(binding.bwd_workspace_bytes(w.B, w.Hq, w.N, w.d), dtype=torch.uint8, device=dev)
     grads = (torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev),
-             torch.empty((w.B, w.Hkv, w.N, w.d), dtype=torch.float32, device=dev),
-             torch.empty((w.B, w.Hkv, w.N, w.d), dtype=torch.float32, device=dev))
+             torch.empty((w.B, w.Hkv, w.nk, w.d), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.Hkv, w.nk, w.d), dtype=torch.float32, device=dev))
     stream = torch.cuda.current_stream(dev)
 
     def call():
@@ -161,8 +181,8 @@ def time_gpu_bwd(w, steps: int, warmup: int):
 def bwd_algorithmic_bytes(w) -> float:
     """Unique HBM bytes of one fa_bwd call: Q, K, V, dO, LSE and O (fp32) read once; dQ, dK, dV
     (fp32) written once."""
-    rd = w.B * w.Hq * w.N * w.d * (2 + 2 + 4) + 2 * w.B * w.Hkv * w.N * w.d * 2 + w.B * w.Hq * w.N * 4
-    wr = (w.B * w.Hq + 2 * w.B * w.Hkv) * w.N * w.d * 4
+    rd = w.B * w.Hq * w.N * w.d * (2 + 2 + 4) + 2 * w.B * w.Hkv * w.nk * w.d * 2 + w.B * w.Hq * w.N * 4
+    wr = (w.B * w.Hq * w.N + 2 * w.B * w.Hkv * w.nk) * w.d * 4
     return float(rd + wr)
 
 
@@ -177,7 +197,7 @@ def bwd_line(w, args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs and dO; PCG64)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "Nk": w.nk, "d": w.d,
                    "causal": w.causal, "window_left": w.window_left, "in_dtype": w.dtype, "grad_dtype": "f32",
                    "o_dtype": "f32",
                    "parallelism": "single GPU"},
@@ -218,8 +238,8 @@ def cpu_baseline(w, budget_s: float = 12.0):
     from exact_attention_114_amd import inputs as I
     from oracle.pool import attention_rows_pool, available_cores
 
-    if w.window_left is not None:
-        return None  # the pooled oracle covers the causal and unmasked forms; the bench line is GQA
+    if w.window_left is not None or w.nk != w.N:
+        return None  # the pooled oracle covers the causal and unmasked square forms; the bench line is GQA
     qkv = I.workload_qkv(w)
     cores = max(1, min(16, available_cores()))
     rows_per_unit = 1024
@@ -306,6 +326,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--bwd", action="store_true")
+    ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="")
     args = ap.parse_args()
@@ -345,20 +366,25 @@ def main():
         for name in I.WORKLOADS:
             wk = I.WORKLOADS[name]
             steps = max(5, min(200, int(2e13 / wk.flops)))
-            _, ms = time_gpu(wk, steps, 3)
-            tf = wk.flops / (ms * 1e-3) / 1e12
-            print(json.dumps({"sweep": name, "ms": round(ms, 5), "tflops": round(tf, 2),
-                              "pct_peak": round(100 * tf / PEAK_TFLOPS[wk.dtype], 2)}), flush=True)
+            tries = [args.splits] + ([1] if planned_splits(wk, args.splits) > 1 else [])
+            for s in tries:
+                _, ms = time_gpu(wk, steps, 3, s)
+                tf = wk.flops / (ms * 1e-3) / 1e12
+                print(json.dumps({"sweep": name, "splits": planned_splits(wk, s), "ms": round(ms, 5),
+                                  "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_TFLOPS[wk.dtype], 2)}),
+                      flush=True)
 
     torch.cuda.synchronize()
-    wall, ms_launch = time_gpu(w, args.steps, args.warmup)
+    wall, ms_launch = time_gpu(w, args.steps, args.warmup, args.splits)
     flops = w.flops
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ms_launch * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     if args.calibrate_copy:
         calibrate_copy()
-    bm, bn, grid = binding.tile(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal,
+    ns = planned_splits(w, args.splits)
+    # with split keys the attention kernel runs ns times the grid (tiles chosen for that grid)
+    bm, bn, grid = binding.tile(w.B * ns, w.Hq, w.Hkv, w.N, w.d, w.causal,
                                 binding.FA_F16 if w.dtype == "f16" else binding.FA_BF16)
     line = {
         "metric": METRIC,
@@ -374,9 +400,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1), K x2; PCG64 seed %d)" % w.seed if w.k_mult != 1.0
         else "synthetic (seeded N(0,1); PCG64 seed %d)" % w.seed,
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "Nk": w.nk, "d": w.d,
                    "causal": w.causal, "window_left": w.window_left, "in_dtype": w.dtype, "out_dtype": "f32",
-                   "scale": w.scale,
+                   "scale": w.scale, "key_splits": ns,
                    "block_m": bm, "block_n": bn, "grid": grid, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
@@ -384,6 +410,9 @@ def main():
                      "algorithmic_hbm_bytes": algorithmic_bytes(w),
                      "kernel_ms": round(ms_launch, 5)},
     }
+    if ns > 1:
+        line["roofline"]["note"] = ("split keys: kernel_ms and achieved cover the attention kernel and the "
+                                    "merge kernel together (HIP events around the whole call)")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

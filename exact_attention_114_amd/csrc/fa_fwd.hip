@@ -35,16 +35,28 @@ int key_blocks(int64_t d, int64_t grid) { return d == 128 && grid > kOneBlockMin
 constexpr int kUnlimited = 1 << 30;
 
 // Split keys: at most this many chunks per Q-tile, each a whole number of 64-key tiles and at
-// least two of them; splitting aims at two work-groups per CU.
+// least two of them.
 constexpr int kMaxSplits = 16;
+// The automatic choice aims at two work-groups per CU (256 CUs), but only cuts chunks of at
+// least kMinChunkKeys(grid) keys: a chunk's fixed cost (loading its Q-tile, writing an fp32
+// partial O, the merge) must stay small against its keys. Measured on MI355X over grids of
+// 16..384 work-groups and 1k..32k keys: splitting a grid that already has a work-group on
+// every CU pays only for long key ranges; small grids gain from chunks of 512 keys up.
 constexpr int64_t kSplitTarget = 2 * 256;
+int64_t min_chunk_keys(int64_t grid) { return grid <= 32 ? 512 : grid < 256 ? 1024 : 4096; }
 
 // Chunks for a problem (requested: 0 = automatic) and the keys per chunk.
 void split_plan(int64_t grid, int64_t Nk, int requested, int* nsplit, int* kchunk) {
   const int64_t tiles64 = (Nk + 63) / 64;
-  int64_t s = requested > 0 ? requested : (grid >= kSplitTarget ? 1 : (kSplitTarget + grid - 1) / grid);
+  int64_t s;
+  if (requested > 0)
+    s = requested;
+  else if (grid >= kSplitTarget)
+    s = 1;
+  else
+    s = std::min<int64_t>((kSplitTarget + grid - 1) / grid, Nk / min_chunk_keys(grid));
   s = std::min<int64_t>(s, kMaxSplits);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles64 / 2));
+  s = std::max<int64_t>(1, std::min<int64_t>(s, tiles64 / 2));
   const int64_t chunk = ((tiles64 + s - 1) / s) * 64;
   *kchunk = (int)chunk;
   *nsplit = (int)((Nk + chunk - 1) / chunk);

@@ -42,7 +42,7 @@ class Workload:
     B: int
     Hq: int
     Hkv: int
-    N: int
+    N: int  # query rows per head (and key rows, unless n_keys is given)
     d: int
     dtype: str  # F16 or BF16: storage type of Q, K, V
     causal: bool
@@ -50,6 +50,11 @@ class Workload:
     seed: int
     k_mult: float = 1.0  # exact power-of-two multiplier applied to K before rounding
     window_left: Optional[int] = None  # causal sliding window: row i sees keys i - window_left .. i
+    n_keys: Optional[int] = None  # key rows per head when they differ from the query rows
+
+    @property
+    def nk(self) -> int:
+        return self.N if self.n_keys is None else self.n_keys
 
     @property
     def band(self):
@@ -61,7 +66,14 @@ class Workload:
     @property
     def flops(self) -> float:
         """Algorithmic FLOPs: 4 d per visible (query, key) pair: two N x N x d contractions,
-        halved when causal, over the band when windowed."""
+        halved when causal, over the band when windowed. With separate key rows, query row i
+        sits at key position i + nk - N and sees the keys up to it when causal."""
+        if self.nk != self.N:
+            assert self.window_left is None
+            n, off = self.N, self.nk - self.N
+            pairs = float(n) * self.nk if not self.causal else \
+                sum(max(0, min(self.nk, i + off + 1)) for i in range(n))
+            return 4.0 * self.B * self.Hq * self.d * pairs
         if self.window_left is not None:
             w, n = self.window_left, self.N
             m = min(w, n)
@@ -74,7 +86,7 @@ class Workload:
         return (self.B, self.Hq, self.N, self.d)
 
     def kv_shape(self):
-        return (self.B, self.Hkv, self.N, self.d)
+        return (self.B, self.Hkv, self.nk, self.d)
 
 
 def _c4(n: int) -> Workload:
@@ -83,7 +95,8 @@ def _c4(n: int) -> Workload:
 
 
 # The five workloads: single-head, GPT-2 shaped, long head dim, the causal
-# sweep, and GQA causal long sequence with K scaled by 2.
+# sweep, and GQA causal long sequence with K scaled by 2; then two for the
+# widened path: a causal sliding window and a query block against long keys.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
@@ -98,6 +111,11 @@ WORKLOADS: Dict[str, Workload] = {
         # (pre_tokens = 2048, next_tokens = 0; intelliparadigm page, section 2.2)
         Workload("window_b4_h48_n16384_d64_f16_w2048", 4, 48, 48, 16384, 64, F16, True, 0.125, 46,
                  window_left=2048),
+        # a short block of new queries against a long key sequence (the last 512 rows of a
+        # causal 32768-token sequence), GQA heads as above: a grid too small to fill the chip
+        # unless the keys are split
+        Workload("chunk_causal_b1_hq32_hkv8_nq512_nk32768_d128_bf16", 1, 32, 8, 512, 128, BF16, True,
+                 1.0 / math.sqrt(128.0), 47, n_keys=32768),
     ]
 }
 
@@ -107,9 +125,16 @@ CAUSAL_SWEEP: List[str] = [_c4(n).name for n in (1024, 2048, 4096, 8192, 16384)]
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (round to nearest, ties to even); uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = x.view(np.uint32)
+    # 32-bit arithmetic cannot overflow for finite values: the largest finite pattern,
+    # 0xFF7FFFFF, plus 0x8000 stays below 2^32
+    if not np.isfinite(x).all():
+        raise ValueError("bf16 rounding expects finite values")
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
@@ -150,12 +175,13 @@ class QKV:
 
 
 def draw_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
-             k_mult: float = 1.0) -> QKV:
-    """Draw Q [B,Hq,N,d], K and V [B,Hkv,N,d] per the recipe in the module doc."""
+             k_mult: float = 1.0, Nk: Optional[int] = None) -> QKV:
+    """Draw Q [B,Hq,N,d], K and V [B,Hkv,Nk,d] (Nk defaults to N) per the recipe in the module doc."""
+    Nk = N if Nk is None else Nk
     g = np.random.Generator(np.random.PCG64(seed))
     q = g.standard_normal((B, Hq, N, d), dtype=np.float32)
-    k = g.standard_normal((B, Hkv, N, d), dtype=np.float32)
-    v = g.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    k = g.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = g.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
     if k_mult != 1.0:
         k = k * np.float32(k_mult)
     return QKV(to_bits(q, dtype), to_bits(k, dtype), to_bits(v, dtype), dtype)
@@ -169,7 +195,7 @@ def draw_dout(B: int, Hq: int, N: int, d: int, dtype: str, seed: int) -> np.ndar
 
 
 def workload_qkv(w: Workload) -> QKV:
-    return draw_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.k_mult)
+    return draw_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.k_mult, w.nk)
 
 
 def scale_f32(scale: float) -> float:

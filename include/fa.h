@@ -125,9 +125,12 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
  * with the online-softmax rule: LSE = ln sum_s exp(LSE_s) and
  * O = sum_s exp(LSE_s - LSE) O_s.
  *
- *   n_splits   0: automatic (aims at two work-groups per CU); otherwise the
- *              number of chunks wanted, at most 16. Chunks are whole 64-key
- *              tiles, at least two, so fewer may be used.
+ *   n_splits   0: automatic: no split when batch x heads x Q-tiles reaches 512
+ *              work-groups, else about 512 / that count chunks, but no chunk
+ *              shorter than 512 keys (grids up to 32 work-groups), 1024 keys
+ *              (up to 255) or 4096 keys (256..511); otherwise the number of
+ *              chunks wanted, at most 16. Chunks are whole 64-key tiles, at
+ *              least two, so fewer may be used.
  *   workspace  device pointer to fa_fwd_split_workspace_bytes(...) bytes,
  *              16-byte aligned, owned by the caller. It may be NULL when that
  *              size is 0, which means no split: the call is then fa_fwd_ex.

@@ -222,13 +222,22 @@ def test_bwd_ex_validation_order():
 # ---------------------------------------------------------------- split keys
 
 def test_split_workspace_bytes():
-    # automatic: a grid of 16 Q-tiles (1 x 16 heads x 1 tile) wants 512 / 16 = 32 chunks, capped at
-    # 16 and at half the 64-key tiles (2048 keys: 32 tiles -> 16): 16 chunks of 128 keys
-    assert bnd.split_workspace_bytes(1, 16, 100, 2048, 128, 0) == 16 * 16 * 100 * 129 * 4
+    # automatic: a grid of 16 Q-tiles (1 x 16 heads x 1 tile) wants 512 / 16 = 32 chunks, capped by
+    # chunks of at least 512 keys (grids up to 32): 2048 keys -> 4 chunks; 32768 keys -> 64, capped at 16
+    assert bnd.split_workspace_bytes(1, 16, 100, 2048, 128, 0) == 4 * 16 * 100 * 129 * 4
+    assert bnd.split_workspace_bytes(1, 16, 100, 32768, 128, 0) == 16 * 16 * 100 * 129 * 4
     assert bnd.split_workspace_bytes(1, 16, 100, 2048, 128, 3) == 3 * 16 * 100 * 129 * 4
+    # grids of 33..255 work-groups: chunks of at least 1024 keys (128 tiles: 512/128 = 4 wanted)
+    assert bnd.split_workspace_bytes(1, 32, 512, 2048, 128, 0) == 2 * 32 * 512 * 129 * 4
+    assert bnd.split_workspace_bytes(1, 32, 512, 32768, 128, 0) == 4 * 32 * 512 * 129 * 4
+    assert bnd.split_workspace_bytes(1, 32, 512, 1024, 128, 0) == 0
+    # 256..511 work-groups: chunks of at least 4096 keys
+    assert bnd.split_workspace_bytes(1, 64, 512, 4096, 128, 0) == 0
+    assert bnd.split_workspace_bytes(1, 64, 512, 8192, 128, 0) == 2 * 64 * 512 * 129 * 4
     # a full grid does not split; a short key range cannot
     assert bnd.split_workspace_bytes(4, 32, 8192, 8192, 128, 0) == 0
     assert bnd.split_workspace_bytes(1, 1, 64, 100, 64, 0) == 0
+    assert bnd.split_workspace_bytes(1, 1, 256, 256, 64, 0) == 0
     # requested splits are bounded by the 64-key tiles: 256 keys -> 4 tiles -> 2 chunks
     assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 8) == 2 * 1 * 10 * 65 * 4
     assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 17) == 0
