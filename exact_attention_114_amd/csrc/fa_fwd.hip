@@ -92,8 +92,12 @@ fa_status dispatch_band(const fa::Params& p, bool band, bool out_f32, int kb, hi
 }
 template <bool BF16>
 fa_status dispatch_d(const fa::Params& p, int d, bool band, bool out_f32, int kb, hipStream_t s) {
-  return d == 64 ? dispatch_band<BF16, 64>(p, band, out_f32, kb, s)
-                 : dispatch_band<BF16, 128>(p, band, out_f32, kb, s);
+  switch (d) {
+    case 32: return dispatch_band<BF16, 32>(p, band, out_f32, kb, s);
+    case 64: return dispatch_band<BF16, 64>(p, band, out_f32, kb, s);
+    case 96: return dispatch_band<BF16, 96>(p, band, out_f32, kb, s);
+    default: return dispatch_band<BF16, 128>(p, band, out_f32, kb, s);
+  }
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -103,7 +107,7 @@ fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t 
                         int64_t* n_qtiles, int64_t* grid) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
   // The kernel sizes its tile loads in 32-bit byte offsets from the start of a K/V head
@@ -228,19 +232,22 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = bf16 ? dispatch_d<true>(p, (int)d, band, true, kb, s) : dispatch_d<false>(p, (int)d, band, true, kb, s);
   if (st != FA_OK) return st;
-  const int rows_per_wg = 256 / (int)(d / 4);
+  const int rows_per_wg = 256 / (int)(d / 4);  // the merge kernel's rows per work-group
   const dim3 mg((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
   const float* ow = workspace;
   const float* lw = workspace + ns * rows * d;
   const bool f32 = out_dtype == FA_F32;
 #define FA_MERGE(BF, DD, F32) hipLaunchKernelGGL((fa::fa_merge_kernel<BF, DD, F32>), mg, dim3(256), 0, s, ow, lw, o, lse, rows, ns)
-  if (d == 64) {
-    if (f32) { if (bf16) FA_MERGE(true, 64, true); else FA_MERGE(false, 64, true); }
-    else { if (bf16) FA_MERGE(true, 64, false); else FA_MERGE(false, 64, false); }
-  } else {
-    if (f32) { if (bf16) FA_MERGE(true, 128, true); else FA_MERGE(false, 128, true); }
-    else { if (bf16) FA_MERGE(true, 128, false); else FA_MERGE(false, 128, false); }
+#define FA_MERGE_D(DD)                                                                  \
+  if (f32) { if (bf16) FA_MERGE(true, DD, true); else FA_MERGE(false, DD, true); }      \
+  else { if (bf16) FA_MERGE(true, DD, false); else FA_MERGE(false, DD, false); }
+  switch (d) {
+    case 32: FA_MERGE_D(32); break;
+    case 64: FA_MERGE_D(64); break;
+    case 96: FA_MERGE_D(96); break;
+    default: FA_MERGE_D(128); break;
   }
+#undef FA_MERGE_D
 #undef FA_MERGE
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -268,7 +275,7 @@ const char* fa_status_str(fa_status s) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: a pointer argument is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes, head grouping, scale or causal flag";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128, inputs fp16/bf16, output fp32 or the input type";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 32, 64, 96 or 128 (64 or 128 for the backward), inputs fp16/bf16, output fp32 or the input type";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error (see fa_last_hip_error)";
   }

@@ -88,6 +88,14 @@ constexpr float kSumLimit = 256.0f;
 constexpr float kRefFloor = -1.0e30f;
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
+// A buffer offset past every descriptor's size (sizes stay below 2^31 - 2^17): a load from it
+// returns zeros without touching memory. Lanes that fill the padding of an LDS row use it.
+constexpr int kPadOffset = 0x7FFF0000;
+
+// LDS row pitch (elements) for a head dimension: rows are stored at a power-of-two pitch so
+// the XOR swizzles below stay inside a row; a head dimension of 32 or 96 leaves padding
+// chunks at the end of each row that are loaded as zeros and never read.
+constexpr int lds_pitch(int d) { return d <= 64 ? 64 : 128; }
 
 struct Params {
   const void* q;
@@ -139,18 +147,18 @@ struct Elt<true> {
   }
 };
 
-// ---- LDS swizzles (16-byte chunk index XOR, per row) ----------------------------------------
+// ---- LDS swizzles (16-byte chunk index XOR, per row), by LDS row pitch DP -----------------
 // LDS has 64 banks x 4 B. K is read with ds_read_b128 by 16 lanes at a time, one row each,
 // same logical chunk: 16 consecutive rows must land in 16 different 16-byte bank slots.
 // V is read with ds_read_b64_tr_b16: 32 lanes read 4 consecutive rows x 64 contiguous bytes;
 // the 4 row segments must land in 4 different 64-byte bank quarters.
-template <int D>
+template <int DP>
 __device__ inline int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return DP == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-template <int D>
+template <int DP>
 __device__ inline int swz_v(int row) {
-  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+  return DP == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
 // v_permlane32_swap a, b exchanges the upper 32 lanes of a with the lower 32 lanes of b. With
@@ -206,8 +214,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Waves that share a SIMD for a tile shape: registers bound it (a d = 128 step with two key
-// blocks holds 189 VGPRs, with one 168; d = 64 about 135) and so does LDS (4 tiles of
-// 32*KB x D values per work-group).
+// blocks holds 189 VGPRs, with one 168; d = 64 about 150) and so does LDS (4 tiles of
+// 32*KB rows at the LDS pitch per work-group).
 constexpr int waves_per_simd(int d, int kb) { return d == 128 && kb == 1 ? 3 : 2; }
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
@@ -216,14 +224,19 @@ template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
+  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
   constexpr int BM = 32 * NW;
   constexpr int BN = 32 * KB;
-  constexpr int KCH = D / 8;             // 16-byte chunks per row
-  constexpr int ROWB = D * 2;            // bytes per row
-  constexpr int TILE_BYTES = BN * ROWB;  // one K or one V tile
-  constexpr int NKS = D / 16;            // MFMA k-steps of Q K^T
-  constexpr int NDB = D / 32;            // MFMA d-blocks of P V
+  constexpr int DP = lds_pitch(D);        // LDS row pitch (elements)
+  constexpr int KCH = D / 8;              // 16-byte chunks per row in HBM
+  constexpr int KCHP = DP / 8;            // 16-byte chunks per row in LDS
+  constexpr int ROWB = D * 2;             // bytes per row in HBM
+  constexpr int ROWBL = DP * 2;           // bytes per row in LDS
+  constexpr int TILE_BYTES = BN * ROWBL;  // one K or one V tile in LDS
+  constexpr int NKS = D / 16;             // MFMA k-steps of Q K^T
+  constexpr int NDB = D / 32;             // MFMA d-blocks of P V
   constexpr int NLD = TILE_BYTES / (NW * 1024);  // 1 KiB tile-load instructions per wave per matrix
+  constexpr int RPI = NW * 1024 / ROWBL;  // tile rows between a wave's consecutive load instructions
   static_assert(NLD >= 1 && TILE_BYTES % (NW * 1024) == 0, "each wave issues the same number of tile loads");
 
   // Two K and two V buffers as four separate arrays: the compiler can then prove that a
@@ -279,15 +292,17 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
 
   // ---- tile loads: instruction n of this wave fills LDS bytes [ii*1024, ii*1024 + 1024) of a
   // tile (ii = n*NW + wave); lane l writes physical chunk ii*64 + l, which holds logical chunk
-  // (pch ^ swizzle(row)) of tile row `row`. Moving to the next instruction moves 64 rows'
-  // worth of chunks, which leaves the swizzle unchanged, so the source offset of instruction n
-  // is the lane's offset for n = 0 plus n*NW*1024 bytes: one loop-invariant VGPR per matrix,
-  // and the 1 KiB steps go into the (scalar) buffer base.
+  // (pch ^ swizzle(row)) of tile row `row`. Moving to the next instruction moves RPI rows
+  // (16 or 32), which leaves the swizzle unchanged, so the source offset of instruction n is
+  // the lane's offset for n = 0 plus n*RPI rows of HBM: one loop-invariant VGPR per matrix,
+  // and the steps go into the (scalar) buffer base. A logical chunk past the head dimension
+  // is row padding: its lane reads from past the descriptor's end and writes zeros.
   int ld_koff, ld_voff;
   {
-    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
-    ld_koff = row * ROWB + ((pch ^ swz_k<D>(row)) << 4);
-    ld_voff = row * ROWB + ((pch ^ swz_v<D>(row)) << 4);
+    const int row = (wave * 64 + lane) / KCHP, pch = lane % KCHP;
+    const int ck = pch ^ swz_k<DP>(row), cv = pch ^ swz_v<DP>(row);
+    ld_koff = (KCH == KCHP || ck < KCH) ? row * ROWB + (ck << 4) : kPadOffset;
+    ld_voff = (KCH == KCHP || cv < KCH) ? row * ROWB + (cv << 4) : kPadOffset;
   }
   // One descriptor per tile and instruction: base at the instruction's first byte of the tile,
   // size up to the sequence end, so rows past N (ragged last tile, or a prefetch past the end)
@@ -297,7 +312,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       // 32-bit: the host keeps Nk*ROWB plus the few tiles a prefetch reaches past it below 2^31
-      const int first = j * TILE_BYTES + n * NW * 1024;  // this instruction's part
+      const int first = j * (BN * ROWB) + n * RPI * ROWB;  // this instruction's part
       const int rest = Nk * ROWB - first;
       const int bytes = rest > 0 ? rest : 0;
       void* bp = (void*)(base + first);
@@ -313,16 +328,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   // K (A operand of S^T = K Q^T): row 32kb + l32 (kb adds an immediate), logical chunk 2ks + h.
   int koff[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + h) ^ swz_k<D>(l32)) << 4);
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * ROWBL + (((2 * ks + h) ^ swz_k<DP>(l32)) << 4);
   // V^T via transposing reads: lane reads row 16t + 8u + 4h + i16/4 (t, u add immediates),
   // columns 32db + 16dh + 4(i16%4) .. +3.
   int voff[NDB];
   {
     const int vrow = 4 * h + (i16 >> 2);
-    const int sv = swz_v<D>(vrow);  // equals the swizzle of every row 16t + 8u + vrow
+    const int sv = swz_v<DP>(vrow);  // equals the swizzle of every row 16t + 8u + vrow
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      voff[db] = vrow * ROWB + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ sv) << 4) + ((i16 & 1) << 3);
+      voff[db] = vrow * ROWBL + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ sv) << 4) + ((i16 & 1) << 3);
   }
 
   // A ragged sequence end leaves tile rows that no load writes (if out-of-range lanes skip
@@ -343,14 +358,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
 
   // MFMA operands from LDS. K (A operand of S^T = K Q^T): block kb of 32 keys, k-step ks.
   auto k_operand = [&](const lds_char* kd, int kb, int ks) -> u32x4 {
-    return *(const lds_u32x4*)(kd + 32 * kb * ROWB + koff[ks]);
+    return *(const lds_u32x4*)(kd + 32 * kb * ROWBL + koff[ks]);
   };
   // V^T (A operand of O^T += V^T P^T) for 16-key step t2 and d-block db: two transposing reads.
   auto v_operand = [&](const lds_char* vd, int t2, int db) -> u32x4 {
     u32x4 a;
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
-      const lds_char* ap = vd + (16 * t2 + 8 * uu) * ROWB + voff[db];
+      const lds_char* ap = vd + (16 * t2 + 8 * uu) * ROWBL + voff[db];
       const u32x2 v2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ap));
       a[2 * uu] = v2[0];
       a[2 * uu + 1] = v2[1];
@@ -669,7 +684,9 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
                                                        void* o, float* lse, int64_t rows, int nsplit) {
   using E = Elt<BF16>;
   constexpr int TPR = D / 4;
-  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  constexpr int RPW = 256 / TPR;  // rows per work-group (threads past RPW * TPR idle)
+  if ((int)threadIdx.x >= RPW * TPR) return;
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
   const int c4 = (threadIdx.x % TPR) * 4;
   if (row >= rows) return;
   float m = -__builtin_inff();

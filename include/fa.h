@@ -65,7 +65,8 @@ typedef enum {
   FA_ERR_NULLPTR = 1,     /* a pointer argument is NULL */
   FA_ERR_SHAPE = 2,       /* B, Hq, Hkv, N or d < 1; Hq not a multiple of Hkv; non-finite
                              or non-positive scale; sizes beyond the 32-bit index range */
-  FA_ERR_UNSUPPORTED = 3, /* d not 64 or 128; in_dtype not F16/BF16; out_dtype not F32 or in_dtype */
+  FA_ERR_UNSUPPORTED = 3, /* d not 32, 64, 96 or 128 (backward: 64 or 128); in_dtype not
+                             F16/BF16; out_dtype not F32 or in_dtype */
   FA_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned */
   FA_ERR_HIP = 5          /* the HIP runtime reported an error; see fa_last_hip_error() */
 } fa_status;
@@ -76,7 +77,9 @@ typedef enum {
  *   q, k, v   device pointers, layouts above, element type in_dtype
  *   o         device pointer, [B][Hq][N][d] of out_dtype
  *   lse       device pointer, [B][Hq][N] float32
- *   B, Hq, Hkv, N, d   sizes; Hq % Hkv == 0; d in {64, 128}; N >= 1 (any N,
+ *   B, Hq, Hkv, N, d   sizes; Hq % Hkv == 0; d in {32, 64, 96, 128} (the
+ *             intelliparadigm page, section 1.3, asks for head dimensions that
+ *             are not powers of two); N >= 1 (any N,
  *             tails are masked); B*Hq*ceil(N/128) below 2^31; N*d at most
  *             2^30 - 2^16 (a K/V head plane under 2 GiB)
  *   scale     multiplies Q.K^T (commonly 1/sqrt(d)); finite and > 0
@@ -193,7 +196,7 @@ fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
  *             of scratch, owned by the caller. Its contents on entry do not
  *             matter; afterwards it holds per-row statistics. Calls that
  *             share a workspace must not run concurrently.
- *   sizes, scale, causal, in_dtype, stream: as for fa_fwd
+ *   sizes, scale, causal, in_dtype, stream: as for fa_fwd, except d in {64, 128}
  *
  * The outputs must not overlap any input, the workspace or each other. The
  * call enqueues three kernels on `stream` (row statistics, dK/dV, dQ) and

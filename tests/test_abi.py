@@ -71,7 +71,7 @@ def test_shape_errors(kw):
     assert call(**kw) == bnd.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(d=256), dict(in_dtype=bnd.FA_F32),
+@pytest.mark.parametrize("kw", [dict(d=48), dict(d=80), dict(d=16), dict(d=256), dict(in_dtype=bnd.FA_F32),
                                 dict(in_dtype=7), dict(out_dtype=bnd.FA_BF16),
                                 dict(in_dtype=bnd.FA_BF16, out_dtype=bnd.FA_F16)])
 def test_unsupported(kw):
@@ -81,6 +81,8 @@ def test_unsupported(kw):
 def test_alignment_is_checked_last():
     # every other argument valid: only the misaligned pointers stop the call
     assert call() == bnd.FA_ERR_ALIGN
+    for d in (32, 96):  # head dimensions that are multiples of 32 up to 128 pass validation
+        assert call(d=d) == bnd.FA_ERR_ALIGN
     assert call(in_dtype=bnd.FA_BF16, out_dtype=bnd.FA_BF16, d=128, causal=1, Hq=8, Hkv=2, N=1) == bnd.FA_ERR_ALIGN
 
 
@@ -241,7 +243,8 @@ def test_split_workspace_bytes():
     # requested splits are bounded by the 64-key tiles: 256 keys -> 4 tiles -> 2 chunks
     assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 8) == 2 * 1 * 10 * 65 * 4
     assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 17) == 0
-    assert bnd.split_workspace_bytes(1, 1, 10, 256, 96, 2) == 0
+    assert bnd.split_workspace_bytes(1, 1, 10, 256, 80, 2) == 0
+    assert bnd.split_workspace_bytes(1, 1, 10, 256, 96, 2) == 2 * 1 * 10 * 97 * 4
 
 
 def test_split_validation():
@@ -259,6 +262,7 @@ def test_split_validation():
     assert call(ws=0) == bnd.FA_ERR_NULLPTR          # a split needs its workspace
     assert call(ns=-1) == bnd.FA_ERR_SHAPE
     assert call(ns=17) == bnd.FA_ERR_SHAPE
-    assert call(d=96) == bnd.FA_ERR_UNSUPPORTED
+    assert call(d=80) == bnd.FA_ERR_UNSUPPORTED
     assert call() == bnd.FA_ERR_ALIGN
+    assert call(d=96) == bnd.FA_ERR_ALIGN
     assert call(ws=0, Nk=64) == bnd.FA_ERR_ALIGN     # no split possible: the workspace is not needed

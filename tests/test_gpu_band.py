@@ -61,7 +61,7 @@ BANDS = [  # (Nq, Nk, left, right)
 
 
 @pytest.mark.parametrize("Nq,Nk,left,right", BANDS)
-@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16)])
+@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16), (96, I.F16), (32, I.BF16)])
 def test_fwd_band(Nq, Nk, left, right, d, dt):
     seed = 900 + Nq + 3 * Nk + d
     qb, kb, vb, _ = draw(2, 4, 2, Nq, Nk, d, dt, seed)

@@ -89,6 +89,20 @@ def test_ragged_shapes(N, d, dt, causal):
     check_full(I.small_case(1, 2, 1, N, d, dt, causal, seed=100 + N))
 
 
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 257])
+@pytest.mark.parametrize("d,dt", [(32, I.F16), (32, I.BF16), (96, I.F16), (96, I.BF16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_32_and_96(N, d, dt, causal):
+    """Head dimensions that are not 64 or 128: rows sit at a padded LDS pitch."""
+    check_full(I.small_case(1, 2, 1, N, d, dt, causal, seed=700 + N + d))
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_head_dims_gqa_many_tiles(d):
+    check_full(I.small_case(2, 8, 2, 700, d, I.BF16, True, seed=750 + d, k_mult=2.0))
+    check_full(I.small_case(1, 4, 4, 1000, d, I.F16, False, seed=760 + d), out_dtype=torch.float16)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (8, 2), (8, 1), (16, 2)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_groups(Hq, Hkv, causal):
@@ -195,16 +209,18 @@ def structured_qkv(w, kind):
         # key j gains 3*j/N along the all-ones direction: its score grows by about 3*sqrt(d)*j/N
         k += (np.float32(3.0) * np.arange(w.N, dtype=np.float32) / np.float32(w.N))[:, None]
     else:
-        # a key near the end aligned with the queries' positive mean: score about 16*sqrt(d), which
-        # puts its exponential near 2^100 (d = 64) or past fp32's range (d = 128) against the
-        # reference the earlier keys set
-        k[:, :, w.N - 5, :] = np.float32(16.0)
+        # a key near the end aligned with the queries' positive mean: score about s*(sqrt(d) + z),
+        # z ~ N(0, 1) per row, which puts its exponential near 2^100 (d = 64) or past fp32's
+        # range (d >= 96) against the reference the earlier keys set. At d = 32 the spike is
+        # s = 64 so that every row's score stays above 60 out to z = -4.5.
+        k[:, :, w.N - 5, :] = np.float32(16.0 if w.d >= 64 else 64.0)
     return I.QKV(I.to_bits(q, w.dtype), I.to_bits(k, w.dtype), I.to_bits(v, w.dtype), w.dtype)
 
 
 @pytest.mark.parametrize("kind", ["rising", "late_spike"])
 @pytest.mark.parametrize("d,dt,Hq,Hkv", [(64, I.F16, 4, 2), (64, I.BF16, 4, 2), (128, I.F16, 4, 2),
-                                         (128, I.BF16, 4, 2), (128, I.BF16, 88, 8)])
+                                         (128, I.BF16, 4, 2), (128, I.BF16, 88, 8), (32, I.F16, 4, 2),
+                                         (96, I.BF16, 4, 2)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rescale_paths(kind, d, dt, Hq, Hkv, causal):
     w = I.small_case(2, Hq, Hkv, 333, d, dt, causal, seed=600 + d + Hq)
@@ -279,6 +295,6 @@ def test_outputs_written_in_place_and_errors_raise():
     torch.cuda.synchronize()
     assert o.data_ptr() == out.data_ptr() and torch.isfinite(out).all() and torch.isfinite(lse).all()
     with pytest.raises(bnd.FaError):
-        fa.fwd(q[..., :32].contiguous(), k[..., :32].contiguous(), v[..., :32].contiguous())
+        fa.fwd(q[..., :48].contiguous(), k[..., :48].contiguous(), v[..., :48].contiguous())  # d = 48
     with pytest.raises(bnd.FaError):
         fa.fwd(q[:, :1].expand(1, 3, 100, 64).contiguous(), k, v)  # 3 query heads over 2 K/V heads

@@ -77,6 +77,15 @@ def test_split_prefill_and_decode_shapes(Nq, Nk, band):
     run(1, 8, 2, Nq, Nk, 128, I.BF16, band, 0, 1200 + Nq + Nk)
 
 
+@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("band", [(None, None), (None, 0)])
+def test_split_head_dims_32_and_96(d, band):
+    # 96 / 4 = 24 merge lanes per row do not divide a 256-thread work-group: the tail idles
+    ws = run(1, 4, 2, 200, 1500, d, I.BF16, band, 3, 1400 + d)
+    assert ws > 0
+    run(1, 2, 1, 77, 1000, d, I.F16, band, 0, 1410 + d, out16=True)
+
+
 @pytest.mark.parametrize("dt", [I.F16, I.BF16])
 def test_split_output_in_input_dtype(dt):
     run(1, 4, 4, 300, 2048, 64, dt, (None, 0), 4, 1300, out16=True)
