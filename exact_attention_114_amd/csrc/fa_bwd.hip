@@ -32,7 +32,7 @@ fa_status launched() {
 template <bool BF16, int D, bool BAND>
 fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t grid_kv, int64_t grid_q,
                      hipStream_t s) {
-  constexpr int RPB = 256 / (D / 8);
+  constexpr int RPB = 256 / fa::prep_lanes(D);  // the prep kernel's rows per work-group
   const unsigned prep_grid = (unsigned)((prep_rows + RPB - 1) / RPB);
   if (o_f32)
     hipLaunchKernelGGL((fa::fa_bwd_prep_kernel<BF16, D, true>), dim3(prep_grid), dim3(256), 0, s, p);
@@ -64,7 +64,7 @@ fa_status check_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, 
                     int64_t* tq, int64_t* tk) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Nq * d > kMaxPlaneElems || Nk * d > kMaxPlaneElems) return FA_ERR_SHAPE;
   const int64_t lim = (int64_t)1 << 31;
   const int64_t t = (Nq + kTile - 1) / kTile, u = (Nk + kTile - 1) / kTile;
@@ -133,11 +133,18 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   const int64_t grid_q = B * Hq * tq;
   const bool bf16 = in_dtype == FA_BF16, o_f32 = o_dtype == FA_F32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (bf16)
-    return d == 64 ? dispatch_band<true, 64>(p, band, o_f32, prep_rows, grid_kv, grid_q, s)
-                   : dispatch_band<true, 128>(p, band, o_f32, prep_rows, grid_kv, grid_q, s);
-  return d == 64 ? dispatch_band<false, 64>(p, band, o_f32, prep_rows, grid_kv, grid_q, s)
-                 : dispatch_band<false, 128>(p, band, o_f32, prep_rows, grid_kv, grid_q, s);
+  switch (d) {
+#define FA_BWD_D(DD)                                                                            \
+  case DD:                                                                                      \
+    return bf16 ? dispatch_band<true, DD>(p, band, o_f32, prep_rows, grid_kv, grid_q, s)        \
+                : dispatch_band<false, DD>(p, band, o_f32, prep_rows, grid_kv, grid_q, s);
+    FA_BWD_D(32)
+    FA_BWD_D(64)
+    FA_BWD_D(96)
+    FA_BWD_D(128)
+#undef FA_BWD_D
+  }
+  return FA_ERR_UNSUPPORTED;
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -61,9 +61,10 @@ struct BwdParams {
 // aligned group of 4 rows at one 64-byte segment must hit 4 different 64-byte bank quarters).
 // The chunk index is XORed with a bijection of the row's low bits whose two high result bits come
 // from the row's two lowest bits.
-template <int D>
+// DP is the LDS row pitch in elements (lds_pitch: 64 or 128).
+template <int DP>
 __device__ inline int swz_u(int row) {
-  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  return DP == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
 __device__ inline float half_lo(unsigned w, bool bf16) {
@@ -73,11 +74,15 @@ __device__ inline float half_hi(unsigned w, bool bf16) {
   return bf16 ? __builtin_bit_cast(float, w & 0xffff0000u) : (float)__builtin_bit_cast(f16x2, w)[1];
 }
 
-// ---- 1. prep: D = rowsum(dO o O) and LSE*log2(e), one row per D/8 lanes ----------------------
+// Lanes per row of the prep kernel: D/8 rounded up to a power of two (the row sum is a
+// butterfly over them); lanes past D/8 hold zeros.
+constexpr int prep_lanes(int d) { return d <= 32 ? 4 : d <= 64 ? 8 : 16; }
+
+// ---- 1. prep: D = rowsum(dO o O) and LSE*log2(e), one row per prep_lanes(D) lanes -----------
 template <bool BF16, int D, bool O_F32>
 __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const BwdParams p) {
-  constexpr int TPR = D / 8;       // lanes per row, 8 elements each
-  constexpr int RPB = 256 / TPR;   // rows per work-group
+  constexpr int TPR = prep_lanes(D);  // lanes per row, 8 elements each
+  constexpr int RPB = 256 / TPR;      // rows per work-group
   const int64_t rows_per_head = (int64_t)p.ws_blk * 32;
   const int64_t rows = (int64_t)p.B * p.Hq * rows_per_head;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const BwdParams p) {
   const int64_t head = row / rows_per_head;
   const int i = (int)(row - head * rows_per_head);
   float acc = 0.f, lse2 = 0.f;
-  if (row < rows && i < p.Nq) {
+  if (row < rows && i < p.Nq && ch * 8 < D) {
     const int64_t e = (head * p.Nq + i) * D + ch * 8;
     const u32x4 g = *(const u32x4*)((const unsigned short*)p.dout + e);
     float o[8];
@@ -107,11 +112,11 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const BwdParams p) {
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc += half_lo(g[t], BF16) * o[2 * t] + half_hi(g[t], BF16) * o[2 * t + 1];
-    // a row that sees no key (LSE = -inf) gets +inf, so that every P of the row is 0
-    if (ch == 0) {
-      const float l = p.lse[head * p.Nq + i];
-      lse2 = l == -__builtin_inff() ? __builtin_inff() : l * 1.44269504088896340736f;
-    }
+  }
+  // a row that sees no key (LSE = -inf) gets +inf, so that every P of the row is 0
+  if (row < rows && i < p.Nq && ch == 0) {
+    const float l = p.lse[head * p.Nq + i];
+    lse2 = l == -__builtin_inff() ? __builtin_inff() : l * 1.44269504088896340736f;
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
@@ -130,17 +135,19 @@ __device__ inline int xcd_remap(int wg, int total) {
   return xcd * per + min(xcd, rem) + local;
 }
 
-// LDS-DMA of rows [r0, r0 + 32) of a [N][D] plane into a 32-row tile. Instruction n of wave w
-// fills tile bytes [(n*NW + w)*1024, +1024); lane offsets are loop invariant (the swizzle repeats
-// every 16 rows), the instruction's first byte goes into the descriptor base and rows past N
-// read as zero.
+// LDS-DMA of rows [r0, r0 + 32) of a [N][D] plane into a 32-row tile at LDS pitch DP.
+// Instruction n of wave w fills tile bytes [(n*NW + w)*1024, +1024), RPI rows further on per
+// instruction; lane offsets are loop invariant (the swizzle repeats every 16 rows), the
+// instruction's first byte goes into the descriptor base, rows past N read as zero and so do
+// the row-padding chunks (their lanes' offset lies past every descriptor's end).
 template <int D, int NW>
 __device__ inline void dma_rows(const char* plane, int N, int r0, lds_char* dst, int wave, int voff) {
-  constexpr int ROWB = D * 2, TB = 32 * ROWB, NLD = TB / (NW * 1024);
+  constexpr int ROWB = D * 2, ROWBL = lds_pitch(D) * 2, TB = 32 * ROWBL, NLD = TB / (NW * 1024);
+  constexpr int RPI = NW * 1024 / ROWBL;
   static_assert(NLD >= 1 && TB % (NW * 1024) == 0, "whole 1 KiB DMA instructions per wave");
 #pragma unroll
   for (int n = 0; n < NLD; ++n) {
-    const int first = r0 * ROWB + n * NW * 1024;
+    const int first = r0 * ROWB + n * RPI * ROWB;
     const int left = N * ROWB - first;
     const int bytes = left > 0 ? left : 0;
     void* bp = (void*)(plane + first);
@@ -150,18 +157,30 @@ __device__ inline void dma_rows(const char* plane, int N, int r0, lds_char* dst,
   }
 }
 
+// The DMA lane offset of a tile: lane l of wave w writes physical chunk (w*64 + l) of the
+// tile's first 1 KiB blocks, which holds logical chunk (pch ^ swizzle) of its row.
+template <int D>
+__device__ inline int dma_lane_off(int wave, int lane) {
+  constexpr int DP = lds_pitch(D), KCH = D / 8, KCHP = DP / 8;
+  const int row = (wave * 64 + lane) / KCHP, pch = lane % KCHP;
+  const int c = pch ^ swz_u<DP>(row);
+  return (KCH == KCHP || c < KCH) ? row * D * 2 + (c << 4) : kPadOffset;
+}
+
 // Lane offsets of a tile read as an MFMA operand. Rows: lane holds row l32, chunk 2ks + h.
 template <int D>
 __device__ inline int row_off(int l32, int h, int ks) {
-  return l32 * D * 2 + (((2 * ks + h) ^ swz_u<D>(l32)) << 4);
+  constexpr int DP = lds_pitch(D);
+  return l32 * DP * 2 + (((2 * ks + h) ^ swz_u<DP>(l32)) << 4);
 }
 // Transposed: lane reads rows 16t + 8u + 4h + i16/4 (t adds an immediate; u changes the swizzle,
 // see tr_half1), columns 32db + 16dh + 4(i16%4) .. +3.
 template <int D>
 __device__ inline int tr_off(int lane, int u, int db) {
+  constexpr int DP = lds_pitch(D);
   const int h = lane >> 5, i16 = lane & 15, dh = (lane >> 4) & 1;
   const int row = 8 * u + 4 * h + (i16 >> 2);
-  return row * D * 2 + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ swz_u<D>(row)) << 4) + ((i16 & 1) << 3);
+  return row * DP * 2 + (((4 * db + 2 * dh + ((i16 & 3) >> 1)) ^ swz_u<DP>(row)) << 4) + ((i16 & 1) << 3);
 }
 // The second half (rows + 8) has the swizzle's bit 1 flipped for every lane (rows 8u + 4h + r
 // give (row >> 2) & 3 = 2u + h), so its offset is (off0 ^ 32) + 8 rows: one VGPR per d-block,
@@ -202,7 +221,8 @@ template <bool BF16, int D, bool BAND, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
-  constexpr int ROWB = D * 2, KCH = D / 8, TB = 32 * ROWB;
+  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
+  constexpr int ROWBL = lds_pitch(D) * 2, TB = 32 * ROWBL;  // LDS row pitch and tile bytes
   constexpr int NKS = D / 16, NDB = D / 32;
   __shared__ __attribute__((aligned(1024))) char sQ0[TB];
   __shared__ __attribute__((aligned(1024))) char sQ1[TB];
@@ -227,11 +247,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   using T = unsigned short;
   const T* Kp = (const T*)p.k + (int64_t)bk * Nk * D;
   const T* Vp = (const T*)p.v + (int64_t)bk * Nk * D;
-  int ld_off;
-  {
-    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
-    ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
-  }
+  const int ld_off = dma_lane_off<D>(wave, lane);
   // this wave's 32 keys as the B operands of S = Q K^T and dP = dO V^T: lane holds key l32,
   // d = 16ks + 8h .. +7 (keys past Nk repeat row Nk-1, or read as zero from LDS; their gradients
   // are never stored). V's rows go to LDS when registers are short: 32 rows per wave, read with
@@ -348,8 +364,8 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dv[db] = E::mfma(pw[t2], tr_operand(tg, ROWB, t2, toff[db], x1[db]), dv[db]);
-        dk[db] = E::mfma(sw[t2], tr_operand(tq, ROWB, t2, toff[db], x1[db]), dk[db]);
+        dv[db] = E::mfma(pw[t2], tr_operand(tg, ROWBL, t2, toff[db], x1[db]), dv[db]);
+        dk[db] = E::mfma(sw[t2], tr_operand(tq, ROWBL, t2, toff[db], x1[db]), dk[db]);
       }
   }
 
@@ -377,7 +393,8 @@ template <bool BF16, int D, bool BAND, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p) {
   using E = Elt<BF16>;
-  constexpr int ROWB = D * 2, KCH = D / 8, TB = 32 * ROWB, BM = 32 * NW;
+  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
+  constexpr int ROWBL = lds_pitch(D) * 2, TB = 32 * ROWBL, BM = 32 * NW;  // LDS row pitch, tile bytes
   constexpr int NKS = D / 16, NDB = D / 32;
   __shared__ __attribute__((aligned(1024))) char sK0[TB];
   __shared__ __attribute__((aligned(1024))) char sK1[TB];
@@ -419,11 +436,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   const float* w = p.ws + (head * p.ws_blk + q0w / 32) * 64;
   const float lse2 = w[l32], dlt = w[32 + l32];
 
-  int ld_off;
-  {
-    const int row = (wave * 64 + lane) / KCH, pch = lane % KCH;
-    ld_off = row * ROWB + ((pch ^ swz_u<D>(row)) << 4);
-  }
+  const int ld_off = dma_lane_off<D>(wave, lane);
   int aoff[NKS], toff[NDB];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) aoff[ks] = row_off<D>(l32, h, ks);
@@ -489,7 +502,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = E::mfma(sw[t2], tr_operand(tk, ROWB, t2, toff[db], x1[db]), acc[db]);
+      for (int db = 0; db < NDB; ++db) acc[db] = E::mfma(sw[t2], tr_operand(tk, ROWBL, t2, toff[db], x1[db]), acc[db]);
   }
 
   // element i of block db: query q0w + 8(i/4) + 4h + i%4, column 32db + l32

@@ -275,7 +275,7 @@ const char* fa_status_str(fa_status s) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: a pointer argument is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes, head grouping, scale or causal flag";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 32, 64, 96 or 128 (64 or 128 for the backward), inputs fp16/bf16, output fp32 or the input type";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 32, 64, 96 or 128, inputs fp16/bf16, output fp32 or the input type";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error (see fa_last_hip_error)";
   }

@@ -65,8 +65,8 @@ typedef enum {
   FA_ERR_NULLPTR = 1,     /* a pointer argument is NULL */
   FA_ERR_SHAPE = 2,       /* B, Hq, Hkv, N or d < 1; Hq not a multiple of Hkv; non-finite
                              or non-positive scale; sizes beyond the 32-bit index range */
-  FA_ERR_UNSUPPORTED = 3, /* d not 32, 64, 96 or 128 (backward: 64 or 128); in_dtype not
-                             F16/BF16; out_dtype not F32 or in_dtype */
+  FA_ERR_UNSUPPORTED = 3, /* d not 32, 64, 96 or 128; in_dtype not F16/BF16; out_dtype
+                             not F32 or in_dtype */
   FA_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned */
   FA_ERR_HIP = 5          /* the HIP runtime reported an error; see fa_last_hip_error() */
 } fa_status;
@@ -196,7 +196,7 @@ fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
  *             of scratch, owned by the caller. Its contents on entry do not
  *             matter; afterwards it holds per-row statistics. Calls that
  *             share a workspace must not run concurrently.
- *   sizes, scale, causal, in_dtype, stream: as for fa_fwd, except d in {64, 128}
+ *   sizes, scale, causal, in_dtype, stream: as for fa_fwd
  *
  * The outputs must not overlap any input, the workspace or each other. The
  * call enqueues three kernels on `stream` (row statistics, dK/dV, dQ) and

@@ -142,7 +142,7 @@ def test_bwd_shape_errors(kw):
     assert call_bwd(**kw) == bnd.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(d=32), dict(d=256), dict(in_dtype=bnd.FA_F32), dict(in_dtype=9),
+@pytest.mark.parametrize("kw", [dict(d=48), dict(d=16), dict(d=256), dict(in_dtype=bnd.FA_F32), dict(in_dtype=9),
                                 dict(o_dtype=bnd.FA_BF16), dict(in_dtype=bnd.FA_BF16, o_dtype=bnd.FA_F16)])
 def test_bwd_unsupported(kw):
     assert call_bwd(**kw) == bnd.FA_ERR_UNSUPPORTED
@@ -158,7 +158,8 @@ def test_bwd_workspace_bytes():
     assert bnd.bwd_workspace_bytes(2, 3, 1, 64) == 2 * 3 * 128 * 2 * 4
     assert bnd.bwd_workspace_bytes(1, 1, 129, 128) == 256 * 2 * 4
     assert bnd.bwd_workspace_bytes(4, 32, 8192, 128) == 4 * 32 * 8192 * 2 * 4
-    assert bnd.bwd_workspace_bytes(1, 1, 64, 96) == 0
+    assert bnd.bwd_workspace_bytes(1, 1, 64, 80) == 0
+    assert bnd.bwd_workspace_bytes(1, 1, 64, 96) == 128 * 2 * 4
     assert bnd.bwd_workspace_bytes(0, 1, 64, 64) == 0
 
 
@@ -216,7 +217,8 @@ def test_bwd_ex_null_pointers(which):
 
 def test_bwd_ex_validation_order():
     assert call_bwd_ex(Nk=0) == bnd.FA_ERR_SHAPE
-    assert call_bwd_ex(d=96) == bnd.FA_ERR_UNSUPPORTED
+    assert call_bwd_ex(d=80) == bnd.FA_ERR_UNSUPPORTED
+    assert call_bwd_ex(d=96) == bnd.FA_ERR_ALIGN
     assert call_bwd_ex(o_dtype=bnd.FA_F16) == bnd.FA_ERR_UNSUPPORTED
     assert call_bwd_ex() == bnd.FA_ERR_ALIGN
 

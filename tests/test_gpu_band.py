@@ -99,7 +99,7 @@ def test_causal_flag_equals_band():
 
 @pytest.mark.parametrize("Nq,Nk,left,right", [(300, 300, 64, 0), (200, 333, None, 0), (333, 200, None, 0),
                                               (257, 257, 5, 5), (160, 96, 20, 70), (1, 300, None, 0)])
-@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16)])
+@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16), (96, I.BF16), (32, I.F16)])
 def test_bwd_band(Nq, Nk, left, right, d, dt):
     B, Hq, Hkv = 1, 4, 2
     seed = 970 + Nq + Nk + d
