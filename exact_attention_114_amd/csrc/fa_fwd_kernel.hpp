@@ -216,7 +216,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Waves that share a SIMD for a tile shape: registers bound it (a d = 128 step with two key
 // blocks holds 189 VGPRs, with one 168; d = 64 about 150) and so does LDS (4 tiles of
 // 32*KB rows at the LDS pitch per work-group).
-constexpr int waves_per_simd(int d, int kb) { return d == 128 && kb == 1 ? 3 : 2; }
+constexpr int waves_per_simd(int d, int kb) { return d >= 96 && kb == 1 ? 3 : 2; }
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
 // pipeline step takes KB blocks of 32 keys.

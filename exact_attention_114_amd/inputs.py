@@ -95,8 +95,9 @@ def _c4(n: int) -> Workload:
 
 
 # The five workloads: single-head, GPT-2 shaped, long head dim, the causal
-# sweep, and GQA causal long sequence with K scaled by 2; then two for the
-# widened path: a causal sliding window and a query block against long keys.
+# sweep, and GQA causal long sequence with K scaled by 2; then four for the
+# widened path: a causal sliding window, head dimensions 96 and 32, and a query
+# block against long keys.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
@@ -111,6 +112,12 @@ WORKLOADS: Dict[str, Workload] = {
         # (pre_tokens = 2048, next_tokens = 0; intelliparadigm page, section 2.2)
         Workload("window_b4_h48_n16384_d64_f16_w2048", 4, 48, 48, 16384, 64, F16, True, 0.125, 46,
                  window_left=2048),
+        # the walkthrough's causal benchmark shape at N = 8192 with head dimensions that are
+        # not 64 or 128 (the intelliparadigm page, section 1.3)
+        Workload("causal_b4_h48_n8192_d96_bf16", 4, 48, 48, 8192, 96, BF16, True,
+                 1.0 / math.sqrt(96.0), 48),
+        Workload("causal_b4_h48_n8192_d32_f16", 4, 48, 48, 8192, 32, F16, True,
+                 1.0 / math.sqrt(32.0), 49),
         # a short block of new queries against a long key sequence (the last 512 rows of a
         # causal 32768-token sequence), GQA heads as above: a grid too small to fill the chip
         # unless the keys are split

@@ -90,8 +90,11 @@ def test_tile_query():
     bm, bn, grid = bnd.tile(4, 32, 8, 8192, 128, True, bnd.FA_BF16)
     assert bm % 32 == 0 and grid == 4 * 32 * ((8192 + bm - 1) // bm)
     assert bnd.tile(4, 32, 8, 8192, 128, False, bnd.FA_BF16)[2] == grid
-    # d = 128 takes 32-key steps once the grid exceeds two work-groups per CU, else 64
+    # d = 128 and 96 take 32-key steps once the grid exceeds two work-groups per CU, else 64
     assert bn == 32 and grid > 512
+    assert bnd.tile(4, 32, 8, 8192, 96, True, bnd.FA_BF16)[1] == 32
+    assert bnd.tile(1, 16, 16, 2048, 96, False, bnd.FA_BF16)[1] == 64
+    assert bnd.tile(4, 48, 48, 8192, 32, True, bnd.FA_F16)[1] == 64
     assert bnd.tile(1, 16, 16, 2048, 128, False, bnd.FA_F16)[1] == 64
     assert bnd.tile(4, 48, 48, 8192, 64, True, bnd.FA_F16)[1] == 64
     bm, bn, grid = bnd.tile(1, 1, 1, 1, 64, False, bnd.FA_F16)

@@ -113,11 +113,12 @@ def test_gqa_groups(Hq, Hkv, causal):
 @pytest.mark.parametrize("N", [1, 33, 65, 300])
 @pytest.mark.parametrize("dt", [I.F16, I.BF16])
 @pytest.mark.parametrize("causal", [False, True])
-def test_d128_large_grid_shapes(N, dt, causal):
-    """d = 128 grids above two work-groups per CU run the kernel with 32-key steps."""
+@pytest.mark.parametrize("d", [128, 96])
+def test_d128_large_grid_shapes(N, dt, causal, d):
+    """d = 128 and 96 grids above two work-groups per CU run the kernel with 32-key steps."""
     T = (N + 127) // 128
     Hq = 4 * (-(-520 // (2 * T * 4)))  # B = 2: at least 520 work-groups, heads a multiple of 4
-    w = I.small_case(2, Hq, Hq // 4, N, 128, dt, causal, seed=600 + N, k_mult=2.0)
+    w = I.small_case(2, Hq, Hq // 4, N, d, dt, causal, seed=600 + N + d, k_mult=2.0)
     assert bnd.tile(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, bnd.FA_F16)[1] == 32
     check_full(w)
 
@@ -151,7 +152,8 @@ def sampled_rows(N, rng, n_random=24):
 
 @pytest.mark.parametrize("name", ["causal_b4_h48_n2048_d64_f16", "causal_b4_h48_n4096_d64_f16",
                                   "causal_b4_h48_n8192_d64_f16", "causal_b4_h48_n16384_d64_f16",
-                                  "gqa_causal_b4_hq32_hkv8_n8192_d128_bf16"])
+                                  "gqa_causal_b4_hq32_hkv8_n8192_d128_bf16", "causal_b4_h48_n8192_d96_bf16",
+                                  "causal_b4_h48_n8192_d32_f16"])
 def test_workload_sampled(name):
     w = I.WORKLOADS[name]
     qkv = I.workload_qkv(w)
