@@ -216,12 +216,16 @@ def band_visible(q_pos: np.ndarray, k_pos: np.ndarray, left: Optional[int], righ
 
 def head_attention_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                              left: Optional[int], right: Optional[int], off: int = 0,
-                             q_pos: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+                             q_pos: Optional[np.ndarray] = None,
+                             hidden: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of one (batch, head) under the band of ``band_visible``.
 
     Same definition as ``head_attention_fp64`` over each row's visible keys. A row that sees
     no key has an empty softmax; the reading taken is O = 0 and LSE = -inf (the log of an
-    empty sum).
+    empty sum). ``hidden`` [n, N] (rows as given in q), when present, hides key j from row i
+    wherever it is nonzero, on top of the band: the boolean attn_mask input of the Ascend
+    operator (intelliparadigm page, section 2.2), the Mask step of FlashAttention-1's
+    Algorithm 2 that the cnblogs page points to.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -235,6 +239,8 @@ def head_attention_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale:
     for r0 in range(0, n, ROW_BLOCK):
         r1 = min(n, r0 + ROW_BLOCK)
         vis = band_visible(q_pos[r0:r1], np.arange(N), left, right, off)
+        if hidden is not None:
+            vis &= ~np.asarray(hidden[r0:r1], dtype=bool)
         S = np.where(vis, _scores(q[r0:r1], k, scale), -np.inf)
         seen = vis.any(axis=1)
         if not seen.any():
@@ -249,10 +255,20 @@ def head_attention_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale:
     return O, LSE
 
 
+def mask_of_head(mask: Optional[np.ndarray], b: int, hq: int) -> Optional[np.ndarray]:
+    """The [Nq, Nk] slice of a [Bm, Hm, Nq, Nk] mask for (b, hq); a size-1 batch or head axis
+    is shared by every batch element or head."""
+    if mask is None:
+        return None
+    return mask[b if mask.shape[0] > 1 else 0, hq if mask.shape[1] > 1 else 0]
+
+
 def attention_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                        left: Optional[int], right: Optional[int]) -> Tuple[np.ndarray, np.ndarray]:
+                        left: Optional[int], right: Optional[int],
+                        mask: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Banded attention over [B,Hq,Nq,d] queries and [B,Hkv,Nk,d] keys/values (float64),
-    with the diagonal offset off = Nk - Nq. Returns (O [B,Hq,Nq,d], LSE [B,Hq,Nq])."""
+    with the diagonal offset off = Nk - Nq, and optionally a [Bm,Hm,Nq,Nk] mask (Bm in {1, B},
+    Hm in {1, Hq}) whose nonzero entries hide keys. Returns (O [B,Hq,Nq,d], LSE [B,Hq,Nq])."""
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     O = np.empty(q.shape, dtype=np.float64)
@@ -261,5 +277,5 @@ def attention_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: floa
         for hq in range(Hq):
             hk = kv_head_of(hq, Hq, Hkv)
             O[b, hq], LSE[b, hq] = head_attention_band_fp64(q[b, hq], k[b, hk], v[b, hk], scale, left, right,
-                                                            off=Nk - Nq)
+                                                            off=Nk - Nq, hidden=mask_of_head(mask, b, hq))
     return O, LSE

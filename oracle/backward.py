@@ -33,7 +33,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .attention import band_visible, head_attention_band_fp64, head_attention_fp64, kv_head_of
+from .attention import band_visible, head_attention_band_fp64, head_attention_fp64, kv_head_of, mask_of_head
 
 ROW_BLOCK = 1024  # query rows per block (bounds memory only)
 
@@ -97,7 +97,8 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
 
 def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                                   o_used: np.ndarray, scale: float, causal: bool, u: float,
-                                  e32: float = 2.0 ** -24, band: Optional[Tuple] = None
+                                  e32: float = 2.0 ** -24, band: Optional[Tuple] = None,
+                                  hidden: Optional[np.ndarray] = None
                                   ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """First-order elementwise error bounds (Bq [n,d], Bk [N,d], Bv [N,d]) for one head's
     gradients computed the way a tiled kernel does: S, dP and D accumulated in fp32 (unit
@@ -115,7 +116,8 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
       Bk = s sum_i [(u + rho_ij + n e32) |dS_ij| + P_ij eta_ij] |Q_ic|
     (a product sum_k a_k b_k whose factor a_k carries a relative error e moves by at most
     e sum_k |a_k b_k|; an fp32 sum of m terms by at most m e32 times the sum of magnitudes).
-    ``band`` = (left, right, off) replaces ``causal`` by the band of ``attention.band_visible``.
+    ``band`` = (left, right, off) replaces ``causal`` by the band of ``attention.band_visible``,
+    and ``hidden`` [n, N] (with a band) hides further keys where nonzero.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -127,7 +129,7 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
     if band is None:
         O, lse = head_attention_fp64(q, k, v, scale, causal)
     else:
-        O, lse = head_attention_band_fp64(q, k, v, scale, *band)
+        O, lse = head_attention_band_fp64(q, k, v, scale, *band, hidden=hidden)
     d_dev = np.abs(np.sum(do * (o_used - O), axis=1))
     d_mag = np.sum(np.abs(do * O), axis=1)
     bq = np.zeros(q.shape)
@@ -140,6 +142,8 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
         S = scale * (q[r0:r1] @ k[:kend].T)
         if band is not None:
             vis = band_visible(np.arange(r0, r1), np.arange(kend), band[0], band[1], band[2])
+            if hidden is not None:
+                vis &= ~np.asarray(hidden[r0:r1, :kend], dtype=bool)
             seen = np.isfinite(lse[r0:r1])
             P = np.where(vis & seen[:, None],
                          np.exp(np.where(vis, S, 0.0) - np.where(seen, lse[r0:r1], 0.0)[:, None]), 0.0)
@@ -161,22 +165,26 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
 
 
 def head_attention_bwd_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                                 left: Optional[int], right: Optional[int], off: int = 0
+                                 left: Optional[int], right: Optional[int], off: int = 0,
+                                 hidden: Optional[np.ndarray] = None
                                  ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Gradients of one head under the band of ``attention.band_visible`` (the same chain rule
-    as ``head_attention_bwd_fp64``; hidden entries and rows that see no key have P = 0)."""
+    """Gradients of one head under the band of ``attention.band_visible`` and the optional
+    ``hidden`` [n, N] mask (the same chain rule as ``head_attention_bwd_fp64``; hidden entries
+    and rows that see no key have P = 0)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     n, N = q.shape[0], k.shape[0]
-    _, lse = head_attention_band_fp64(q, k, v, scale, left, right, off)
+    _, lse = head_attention_band_fp64(q, k, v, scale, left, right, off, hidden=hidden)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for r0 in range(0, n, ROW_BLOCK):
         r1 = min(n, r0 + ROW_BLOCK)
         vis = band_visible(np.arange(r0, r1), np.arange(N), left, right, off)
+        if hidden is not None:
+            vis &= ~np.asarray(hidden[r0:r1], dtype=bool)
         seen = np.isfinite(lse[r0:r1])
         S = scale * (q[r0:r1] @ k.T)
         P = np.where(vis & seen[:, None], np.exp(np.where(vis, S, 0.0) - np.where(seen, lse[r0:r1], 0.0)[:, None]), 0.0)
@@ -190,9 +198,10 @@ def head_attention_bwd_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do
 
 
 def attention_bwd_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                            left: Optional[int], right: Optional[int]
+                            left: Optional[int], right: Optional[int], mask: Optional[np.ndarray] = None
                             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Banded gradients over [B,Hq,Nq,d] queries and [B,Hkv,Nk,d] keys/values, off = Nk - Nq."""
+    """Banded gradients over [B,Hq,Nq,d] queries and [B,Hkv,Nk,d] keys/values, off = Nk - Nq,
+    with the optional [Bm,Hm,Nq,Nk] mask of ``attention.attention_band_fp64``."""
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     dq = np.empty(q.shape, dtype=np.float64)
@@ -202,7 +211,7 @@ def attention_bwd_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.
         for hq in range(Hq):
             hk = kv_head_of(hq, Hq, Hkv)
             g_q, g_k, g_v = head_attention_bwd_band_fp64(q[b, hq], k[b, hk], v[b, hk], do[b, hq], scale, left, right,
-                                                         off=Nk - Nq)
+                                                         off=Nk - Nq, hidden=mask_of_head(mask, b, hq))
             dq[b, hq] = g_q
             dk[b, hk] += g_k
             dv[b, hk] += g_v
