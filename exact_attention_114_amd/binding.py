@@ -38,6 +38,9 @@ SIGNATURES = {
     "fa_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                      + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
+    "fa_fwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+                    + [ctypes.c_int64] * 6 + [ctypes.c_float] + [ctypes.c_int64] * 2
+                    + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -106,6 +109,32 @@ def fwd_split_raw(q: int, k: int, v: int, o: int, lse: int, ws: int, B: int, Hq:
                                        n_splits, in_dtype, out_dtype, stream)
 
 
+def fwd_mask_raw(q: int, k: int, v: int, o: int, lse: int, mask: int, m_sb: int, m_sh: int, m_ld: int, ws: int,
+                 B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, scale: float, left: int, right: int,
+                 n_splits: int, in_dtype: int, out_dtype: int, stream: int = 0) -> int:
+    """Call fa_fwd_mask with raw device addresses; returns the fa_status code."""
+    return load_library().fa_fwd_mask(q, k, v, o, lse, mask, m_sb, m_sh, m_ld, ws, B, Hq, Hkv, Nq, Nk, d,
+                                      float(scale), left, right, n_splits, in_dtype, out_dtype, stream)
+
+
+def mask_strides(mask, B: int, Hq: int, Nq: int, Nk: int) -> Tuple[int, int, int]:
+    """(batch, head, row) byte strides of a [B or 1, Hq or 1, Nq, Nk] bool or uint8 mask tensor,
+    a size-1 batch or head axis shared (stride 0). Rows must be contiguous and 4-byte aligned."""
+    import torch
+
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise FaError(FA_ERR_UNSUPPORTED, "mask must be bool or uint8 (nonzero hides the key)")
+    if mask.dim() != 4 or mask.shape[2] != Nq or mask.shape[3] != Nk or mask.shape[0] not in (1, B) \
+            or mask.shape[1] not in (1, Hq):
+        raise FaError(FA_ERR_SHAPE, f"mask shape {tuple(mask.shape)} is not [B or 1, Hq or 1, {Nq}, {Nk}]")
+    if mask.stride(3) != 1 or mask.stride(2) % 4 != 0:
+        raise FaError(FA_ERR_ALIGN, "mask rows must be contiguous with a row stride that is a multiple of 4 bytes "
+                                    "(pad the key axis)")
+    sb = mask.stride(0) if mask.shape[0] > 1 else 0
+    sh = mask.stride(1) if mask.shape[1] > 1 else 0
+    return sb, sh, mask.stride(2)
+
+
 def split_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: int) -> int:
     """Bytes of workspace fa_fwd_split needs (0: it would not split)."""
     return int(load_library().fa_fwd_split_workspace_bytes(B, Hq, Nq, Nk, d, n_splits))
@@ -130,7 +159,7 @@ def tile(B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool, in_dtype: int)
 
 
 def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=None, out_dtype=None,
-        out=None, lse=None, splits: Optional[int] = None, workspace=None, stream=None):
+        out=None, lse=None, splits: Optional[int] = None, workspace=None, mask=None, stream=None):
     """Exact attention forward on the GPU: returns (O, LSE).
 
     q: [B, Hq, Nq, d], k and v: [B, Hkv, Nk, d], contiguous fp16 or bf16 CUDA
@@ -140,7 +169,9 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
     keys as fa_fwd_ex does: query row i sees keys i + Nk - Nq - left ..
     i + Nk - Nq + right. splits (0 = automatic, or a chunk count up to 16) cuts each
     Q-tile's keys into chunks merged afterwards (fa_fwd_split); its workspace is
-    allocated when not given. Runs on ``stream`` (a torch stream) or torch's current stream.
+    allocated when not given. mask, a bool or uint8 [B or 1, Hq or 1, Nq, Nk] tensor whose
+    nonzero entries hide keys (fa_fwd_mask), applies on top of the band. Runs on ``stream``
+    (a torch stream) or torch's current stream.
     """
     import torch
 
@@ -182,6 +213,20 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
         raise FaError(FA_ERR_SHAPE, "all tensors must be on one device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if mask is not None:
+        if mask.device != q.device:
+            raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
+        sb, sh, ld = mask_strides(mask, B, Hq, N, Nk)
+        ns = 1 if splits is None else int(splits)
+        need = split_workspace_bytes(B, Hq, N, Nk, d, ns)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if need and (workspace.device != q.device or workspace.numel() * workspace.element_size() < need):
+            raise FaError(FA_ERR_SHAPE, f"workspace must hold {need} bytes on the inputs' device")
+        _check(fwd_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            mask.data_ptr(), sb, sh, ld, workspace.data_ptr() if need else 0, B, Hq, Hkv, N, Nk, d,
+                            scale, left, right, ns, in_code, out_code, stream.cuda_stream))
+        return out, lse
     if splits is not None:
         need = split_workspace_bytes(B, Hq, N, Nk, d, int(splits))
         if workspace is None:

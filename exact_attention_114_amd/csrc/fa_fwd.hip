@@ -63,10 +63,10 @@ void split_plan(int64_t grid, int64_t Nk, int requested, int* nsplit, int* kchun
   *nsplit = (int)((Nk + chunk - 1) / chunk);
 }
 
-template <bool BF16, int D, bool BAND, bool OUT_F32, int KB>
+template <bool BF16, int D, bool BAND, bool OUT_F32, int KB, bool AM>
 fa_status launch(const fa::Params& p, hipStream_t stream) {
-  // The K/V double buffer is static LDS inside the kernel (4 tiles of 32*KB x D values).
-  auto kern = fa::fa_fwd_kernel<BF16, D, BAND, OUT_F32, kWaves, KB>;
+  // The K/V double buffer is static LDS inside the kernel (4 tiles of 32*KB rows).
+  auto kern = fa::fa_fwd_kernel<BF16, D, BAND, OUT_F32, kWaves, KB, AM>;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -76,28 +76,31 @@ fa_status launch(const fa::Params& p, hipStream_t stream) {
   return FA_OK;
 }
 
-template <bool BF16, int D, bool BAND, bool OUT_F32>
+template <bool BF16, int D, bool BAND, bool OUT_F32, bool AM>
 fa_status dispatch_kb(const fa::Params& p, int kb, hipStream_t s) {
   if constexpr (D == 128 || D == 96) {
-    if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1>(p, s);
+    if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1, AM>(p, s);
   }
-  return launch<BF16, D, BAND, OUT_F32, 2>(p, s);
+  return launch<BF16, D, BAND, OUT_F32, 2, AM>(p, s);
 }
-template <bool BF16, int D, bool BAND>
+template <bool BF16, int D, bool BAND, bool AM>
 fa_status dispatch_out(const fa::Params& p, bool out_f32, int kb, hipStream_t s) {
-  return out_f32 ? dispatch_kb<BF16, D, BAND, true>(p, kb, s) : dispatch_kb<BF16, D, BAND, false>(p, kb, s);
+  return out_f32 ? dispatch_kb<BF16, D, BAND, true, AM>(p, kb, s) : dispatch_kb<BF16, D, BAND, false, AM>(p, kb, s);
 }
+// A mask runs on the banded kernel (with unlimited edges when there is no band).
 template <bool BF16, int D>
-fa_status dispatch_band(const fa::Params& p, bool band, bool out_f32, int kb, hipStream_t s) {
-  return band ? dispatch_out<BF16, D, true>(p, out_f32, kb, s) : dispatch_out<BF16, D, false>(p, out_f32, kb, s);
+fa_status dispatch_band(const fa::Params& p, bool band, bool am, bool out_f32, int kb, hipStream_t s) {
+  if (am) return dispatch_out<BF16, D, true, true>(p, out_f32, kb, s);
+  return band ? dispatch_out<BF16, D, true, false>(p, out_f32, kb, s)
+              : dispatch_out<BF16, D, false, false>(p, out_f32, kb, s);
 }
 template <bool BF16>
-fa_status dispatch_d(const fa::Params& p, int d, bool band, bool out_f32, int kb, hipStream_t s) {
+fa_status dispatch_d(const fa::Params& p, int d, bool band, bool am, bool out_f32, int kb, hipStream_t s) {
   switch (d) {
-    case 32: return dispatch_band<BF16, 32>(p, band, out_f32, kb, s);
-    case 64: return dispatch_band<BF16, 64>(p, band, out_f32, kb, s);
-    case 96: return dispatch_band<BF16, 96>(p, band, out_f32, kb, s);
-    default: return dispatch_band<BF16, 128>(p, band, out_f32, kb, s);
+    case 32: return dispatch_band<BF16, 32>(p, band, am, out_f32, kb, s);
+    case 64: return dispatch_band<BF16, 64>(p, band, am, out_f32, kb, s);
+    case 96: return dispatch_band<BF16, 96>(p, band, am, out_f32, kb, s);
+    default: return dispatch_band<BF16, 128>(p, band, am, out_f32, kb, s);
   }
 }
 
@@ -122,27 +125,52 @@ fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t 
   return FA_OK;
 }
 
-}  // namespace
+// The optional mask of fa_fwd_mask (data == nullptr: none).
+struct MaskArg {
+  const void* data = nullptr;
+  int64_t b_stride = 0, h_stride = 0, row_stride = 0;
+};
 
-extern "C" {
-
-fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
-                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
-                    int64_t window_right, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
+// Every forward entry point: validation, the split plan (n_splits = 1: never split; workspace
+// is then unused), the attention kernel and, with split keys, the merge.
+fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace, int64_t B,
+                  int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                  int64_t window_right, int n_splits, const MaskArg& mask, fa_dtype in_dtype, fa_dtype out_dtype,
+                  void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+  if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
   int64_t nq = 0, grid = 0;
-  const fa_status st = check_problem(B, Hq, Hkv, Nq, Nk, d, in_dtype, &nq, &grid);
+  fa_status st = check_problem(B, Hq, Hkv, Nq, Nk, d, in_dtype, &nq, &grid);
   if (st != FA_OK) return st;
+  int ns = 1, kc = (int)(((Nk + 63) / 64) * 64);
+  split_plan(grid, Nk, n_splits, &ns, &kc);
+  if (ns == 1) kc = (int)(((Nk + 63) / 64) * 64);
+  if (ns > 1 && !workspace) return FA_ERR_NULLPTR;
   if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
   if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const bool am = mask.data != nullptr;
+  if (am) {
+    // dword reads of the mask: rows, planes and the pointer 4-byte aligned; a head's plane
+    // addressed with 32-bit offsets
+    if (mask.row_stride < Nk || mask.b_stride < 0 || mask.h_stride < 0) return FA_ERR_SHAPE;
+    // (offsets reach a few tiles past a row's end: keep a 64 KiB margin below 2^31)
+    if (Nq * mask.row_stride > ((int64_t)1 << 31) - ((int64_t)1 << 16)) return FA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(mask.data) & 3u) || (mask.row_stride & 3) || (mask.b_stride & 3) ||
+        (mask.h_stride & 3))
+      return FA_ERR_ALIGN;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (ns > 1 && !aligned16(workspace)))
+    return FA_ERR_ALIGN;
+  const int64_t rows = B * Hq * Nq;
+  if (grid * ns >= ((int64_t)1 << 31) || rows * d * ns >= ((int64_t)1 << 40)) return FA_ERR_SHAPE;
 
   fa::Params p;
   p.q = q;
   p.k = k;
   p.v = v;
-  p.o = o;
-  p.lse = lse;
+  p.o = ns > 1 ? (void*)workspace : o;             // split: ns planes of fp32 O [rows][d]
+  p.lse = ns > 1 ? workspace + ns * rows * d : lse;  // then ns planes of fp32 LSE [rows]
   p.B = (int)B;
   p.Hq = (int)Hq;
   p.Hkv = (int)Hkv;
@@ -153,18 +181,58 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   p.right = window_right < 0 || window_right >= kUnlimited ? kUnlimited : (int)window_right;
   p.group = (int)(Hq / Hkv);
   p.n_qtiles = (int)nq;
-  p.nsplit = 1;
-  p.kchunk = (int)(((Nk + 63) / 64) * 64);
-  p.total_wg = (int)grid;
+  p.nsplit = ns;
+  p.kchunk = kc;
+  p.total_wg = (int)(grid * ns);
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  p.am = static_cast<const unsigned char*>(mask.data);
+  p.am_sb = mask.b_stride;
+  p.am_sh = mask.h_stride;
+  p.am_ld = (int)mask.row_stride;
 
   // With both edges unlimited every key is visible and no band is applied.
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const bool bf16 = in_dtype == FA_BF16;
-  const bool out_f32 = out_dtype == FA_F32;
-  const int kb = key_blocks(d, grid);
+  const bool out_f32 = ns > 1 || out_dtype == FA_F32;
+  const int kb = key_blocks(d, grid * ns);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return bf16 ? dispatch_d<true>(p, (int)d, band, out_f32, kb, s) : dispatch_d<false>(p, (int)d, band, out_f32, kb, s);
+  st = bf16 ? dispatch_d<true>(p, (int)d, band, am, out_f32, kb, s)
+            : dispatch_d<false>(p, (int)d, band, am, out_f32, kb, s);
+  if (st != FA_OK || ns == 1) return st;
+  const int rows_per_wg = 256 / (int)(d / 4);  // the merge kernel's rows per work-group
+  const dim3 mg((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+  const float* ow = workspace;
+  const float* lw = workspace + ns * rows * d;
+  const bool f32 = out_dtype == FA_F32;
+#define FA_MERGE(BF, DD, F32) hipLaunchKernelGGL((fa::fa_merge_kernel<BF, DD, F32>), mg, dim3(256), 0, s, ow, lw, o, lse, rows, ns)
+#define FA_MERGE_D(DD)                                                                  \
+  if (f32) { if (bf16) FA_MERGE(true, DD, true); else FA_MERGE(false, DD, true); }      \
+  else { if (bf16) FA_MERGE(true, DD, false); else FA_MERGE(false, DD, false); }
+  switch (d) {
+    case 32: FA_MERGE_D(32); break;
+    case 64: FA_MERGE_D(64); break;
+    case 96: FA_MERGE_D(96); break;
+    default: FA_MERGE_D(128); break;
+  }
+#undef FA_MERGE_D
+#undef FA_MERGE
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    fa::last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                    int64_t window_right, fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
+  return fwd_run(q, k, v, o, lse, nullptr, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, 1, MaskArg{},
+                 in_dtype, out_dtype, stream);
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
@@ -189,73 +257,23 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
                        int64_t window_left, int64_t window_right, int n_splits, fa_dtype in_dtype,
                        fa_dtype out_dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
-  if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
-  int64_t nq = 0, grid = 0;
-  fa_status st = check_problem(B, Hq, Hkv, Nq, Nk, d, in_dtype, &nq, &grid);
-  if (st != FA_OK) return st;
-  int ns = 1, kc = 0;
-  split_plan(grid, Nk, n_splits, &ns, &kc);
-  if (ns == 1)
-    return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, in_dtype, out_dtype,
-                     stream);
-  if (!workspace) return FA_ERR_NULLPTR;
-  if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
-  if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
-    return FA_ERR_ALIGN;
-  const int64_t rows = B * Hq * Nq;
-  if (grid * ns >= ((int64_t)1 << 31) || rows * d * ns >= ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  return fwd_run(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, n_splits,
+                 MaskArg{}, in_dtype, out_dtype, stream);
+}
 
-  fa::Params p;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = workspace;                      // ns planes of fp32 O [rows][d]
-  p.lse = workspace + ns * rows * d;    // then ns planes of fp32 LSE [rows]
-  p.B = (int)B;
-  p.Hq = (int)Hq;
-  p.Hkv = (int)Hkv;
-  p.Nq = (int)Nq;
-  p.Nk = (int)Nk;
-  p.off = (int)(Nk - Nq);
-  p.left = window_left < 0 || window_left >= kUnlimited ? kUnlimited : (int)window_left;
-  p.right = window_right < 0 || window_right >= kUnlimited ? kUnlimited : (int)window_right;
-  p.group = (int)(Hq / Hkv);
-  p.n_qtiles = (int)nq;
-  p.nsplit = ns;
-  p.kchunk = kc;
-  p.total_wg = (int)(grid * ns);
-  p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
-  const bool band = p.left != kUnlimited || p.right != kUnlimited;
-  const bool bf16 = in_dtype == FA_BF16;
-  const int kb = key_blocks(d, grid * ns);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = bf16 ? dispatch_d<true>(p, (int)d, band, true, kb, s) : dispatch_d<false>(p, (int)d, band, true, kb, s);
-  if (st != FA_OK) return st;
-  const int rows_per_wg = 256 / (int)(d / 4);  // the merge kernel's rows per work-group
-  const dim3 mg((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
-  const float* ow = workspace;
-  const float* lw = workspace + ns * rows * d;
-  const bool f32 = out_dtype == FA_F32;
-#define FA_MERGE(BF, DD, F32) hipLaunchKernelGGL((fa::fa_merge_kernel<BF, DD, F32>), mg, dim3(256), 0, s, ow, lw, o, lse, rows, ns)
-#define FA_MERGE_D(DD)                                                                  \
-  if (f32) { if (bf16) FA_MERGE(true, DD, true); else FA_MERGE(false, DD, true); }      \
-  else { if (bf16) FA_MERGE(true, DD, false); else FA_MERGE(false, DD, false); }
-  switch (d) {
-    case 32: FA_MERGE_D(32); break;
-    case 64: FA_MERGE_D(64); break;
-    case 96: FA_MERGE_D(96); break;
-    default: FA_MERGE_D(128); break;
-  }
-#undef FA_MERGE_D
-#undef FA_MERGE
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    fa::last_hip_error = (int)e;
-    return FA_ERR_HIP;
-  }
-  return FA_OK;
+fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, float* lse, const void* mask,
+                      int64_t mask_b_stride, int64_t mask_h_stride, int64_t mask_row_stride, float* workspace,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                      int64_t window_left, int64_t window_right, int n_splits, fa_dtype in_dtype,
+                      fa_dtype out_dtype, void* stream) {
+  if (!mask) return FA_ERR_NULLPTR;
+  MaskArg m;
+  m.data = mask;
+  m.b_stride = mask_b_stride;
+  m.h_stride = mask_h_stride;
+  m.row_stride = mask_row_stride;
+  return fwd_run(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, n_splits, m,
+                 in_dtype, out_dtype, stream);
 }
 
 fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, fa_dtype in_dtype,

@@ -46,7 +46,12 @@
 //      K/V tiles a Q-tile's band touches are loaded and computed, and only tiles crossing a
 //      band edge (or the ragged end of the keys) are masked. A row that sees no key gets
 //      O = 0 and LSE = -inf.
-//   6. Split keys. When batch x heads x Q-tiles leaves the GPU under-filled, the keys of each
+//   6. Mask input. The operator's optional boolean attn_mask (intelliparadigm page, section 2.2;
+//      the Mask step of FlashAttention-1's Algorithm 2 that the cnblogs page points to) hides a
+//      key from a query where its byte is nonzero, on top of the band. A lane reads the 16 bytes
+//      of its query row that match its 16 scores of a 32-key block as 4 dwords, one step ahead,
+//      and a wave skips the per-score selects on tiles its mask leaves whole.
+//   7. Split keys. When batch x heads x Q-tiles leaves the GPU under-filled, the keys of each
 //      Q-tile can be cut into chunks handled by separate work-groups (the FA2 walkthrough's
 //      point about adding parallelism along the sequence when batch and heads are small); each
 //      writes its chunk's normalised O and LSE, and a merge kernel combines them.
@@ -113,6 +118,11 @@ struct Params {
   int kchunk;    // keys per chunk, a multiple of 64 (every key-tile size)
   int total_wg;  // B * Hq * n_qtiles * nsplit
   float c;       // scale * log2(e)
+  // optional byte mask (kernels built with AM): byte [i][j] of the (b, hq) plane at
+  // am + b*am_sb + hq*am_sh, rows am_ld bytes apart; nonzero hides key j from query i
+  const unsigned char* am;
+  long long am_sb, am_sh;
+  int am_ld;
 };
 
 // ---- element-type traits ------------------------------------------------------------------
@@ -216,13 +226,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Waves that share a SIMD for a tile shape: registers bound it (a d = 128 step with two key
 // blocks holds 189 VGPRs, with one 168; d = 64 about 150) and so does LDS (4 tiles of
 // 32*KB rows at the LDS pitch per work-group).
-constexpr int waves_per_simd(int d, int kb) { return d >= 96 && kb == 1 ? 3 : 2; }
+constexpr int waves_per_simd(int d, int kb, bool am) { return d >= 96 && kb == 1 && !am ? 3 : 2; }
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
 // pipeline step takes KB blocks of 32 keys.
-template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB>
+template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB, bool AM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(const Params p) {
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, AM)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
   static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
   constexpr int BM = 32 * NW;
@@ -238,6 +248,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   constexpr int NLD = TILE_BYTES / (NW * 1024);  // 1 KiB tile-load instructions per wave per matrix
   constexpr int RPI = NW * 1024 / ROWBL;  // tile rows between a wave's consecutive load instructions
   static_assert(NLD >= 1 && TILE_BYTES % (NW * 1024) == 0, "each wave issues the same number of tile loads");
+  static_assert(!AM || BAND, "the masked kernel is built on the banded one");
 
   // Two K and two V buffers as four separate arrays: the compiler can then prove that a
   // prefetch into one buffer never aliases the reads of another, and does not stall on it.
@@ -416,6 +427,40 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   // lane l: query l%32, d = 16ks + 8h + 0..7
   load_k(j_lo, K0);
   load_k(j_lo + 1, K1);
+  // Mask words: am_w[kb][g] holds the bytes of keys kbase + 32kb + 8g + 4h + (0..3) of this
+  // lane's query row, i.e. scores 4g .. 4g+3 of block kb. One descriptor spans the head's
+  // plane (a read past it gives zeros); the lane's row and half go in a loop-invariant offset.
+  unsigned am_w[AM ? KB : 1][4];
+  __amdgpu_buffer_rsrc_t am_rs;
+  int am_v0 = 0;
+  // The whole offset goes into the vector operand (the scalar one stays 0): the range check
+  // covers the vector offset, so a prefetch past the plane reads zeros rather than memory.
+  auto load_am = [&](int jt, unsigned(&w)[AM ? KB : 1][4]) {
+    const int vo = am_v0 + jt * BN;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) w[kb][g] = __builtin_amdgcn_raw_buffer_load_b32(am_rs, vo + 32 * kb + 8 * g, 0, 0);
+  };
+  // hide the scores whose mask byte is nonzero; a wave whose words are all zero skips it
+  auto apply_am = [&](f32x16(&st)[KB], const unsigned(&w)[AM ? KB : 1][4]) {
+    unsigned any = 0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) any |= w[kb][0] | w[kb][1] | w[kb][2] | w[kb][3];
+    if (__builtin_amdgcn_ballot_w64(any != 0u) != 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          st[kb][i] = ((w[kb][i >> 2] >> (8 * (i & 3))) & 0xffu) != 0u ? -__builtin_inff() : st[kb][i];
+    }
+  };
+  if constexpr (AM) {
+    const unsigned char* plane = p.am + (long long)b * p.am_sb + (long long)hq * p.am_sh;
+    am_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.am_ld, kBufferWord3);
+    am_v0 = qr * p.am_ld + 4 * h;
+    load_am(j_lo, am_w);
+  }
   u32x4 qreg[NKS];
   {
     const u32x4* src = (const u32x4*)(Qp + (int64_t)qr * D + 8 * h);
@@ -483,6 +528,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
         }
     };
     if (need_mask) mask(scur);
+    if constexpr (AM) {
+      apply_am(scur, am_w);
+      load_am(j + 1, am_w);  // the next step's words; its closing wait covers them
+    }
 
     // ---- the MFMA stream: P V first (its operands are ready), then S_{j+1}
     u32x4 opnd[NM > 0 ? NM : 1];
@@ -600,6 +649,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
           for (int ks = 0; ks < NKS; ++ks) st[kb] = E::mfma(src[2 * ks], qreg[ks], st[kb]);
         }
         if (need_mask) mask(st);
+        if constexpr (AM) {
+          unsigned wj[AM ? KB : 1][4];
+          load_am(j, wj);
+          apply_am(st, wj);
+        }
 #pragma unroll
         for (int i = 0; i < 2 * KB; ++i) pm[i] = max8(st[i >> 1], 8 * (i & 1));
         const float m_new = fmaxf(m_run, row_max(pm));

@@ -148,6 +148,32 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        fa_dtype out_dtype, void* stream);
 
 /*
+ * fa_fwd_mask — fa_fwd_split with a mask input: the Ascend operator's optional
+ * boolean attn_mask (the intelliparadigm page, section 2.2), which is the Mask
+ * step of FlashAttention-1's Algorithm 2 that the cnblogs page points to. Key
+ * j is hidden from query i of head (b, h) when the byte
+ *   mask[b * mask_b_stride + h * mask_h_stride + i * mask_row_stride + j]
+ * is nonzero (the operator's convention: 1 means masked out), on top of the
+ * band. A row that sees no key gets O = 0 and lse = -inf.
+ *
+ *   mask            device pointer to bytes, 4-byte aligned, owned by the
+ *                   caller; read only
+ *   mask_b_stride, mask_h_stride   bytes between batch elements and between
+ *                   query heads; 0 shares one plane across them. Multiples of 4
+ *   mask_row_stride bytes between query rows: >= Nk, a multiple of 4, with
+ *                   Nq * mask_row_stride at most 2^31 - 2^16
+ *   workspace, n_splits   as fa_fwd_split (NULL and 1 for no split)
+ * Other arguments, errors and execution as fa_fwd_split; a NULL mask is
+ * FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN.
+ */
+fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const void* mask, int64_t mask_b_stride, int64_t mask_h_stride,
+                      int64_t mask_row_stride, float* workspace, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                      int64_t window_left, int64_t window_right, int n_splits,
+                      fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
+/*
  * fa_fwd_split_workspace_bytes — bytes of workspace fa_fwd_split needs
  * (chunks x rows x (d + 1) floats), 0 when it would not split (or the
  * arguments are invalid). Makes no HIP call.

@@ -271,3 +271,41 @@ def test_split_validation():
     assert call() == bnd.FA_ERR_ALIGN
     assert call(d=96) == bnd.FA_ERR_ALIGN
     assert call(ws=0, Nk=64) == bnd.FA_ERR_ALIGN     # no split possible: the workspace is not needed
+
+
+# ---------------------------------------------------------------- mask input
+
+def call_fwd_mask(**kw):
+    a = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, mask=BAD, sb=0, sh=0, ld=80, ws=0, B=1,
+             Hq=2, Hkv=1, Nq=64, Nk=80, d=64, scale=0.125, left=-1, right=-1, ns=1, i=bnd.FA_F16, o_=bnd.FA_F32)
+    a.update(kw)
+    return bnd.fwd_mask_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["sb"], a["sh"], a["ld"], a["ws"],
+                            a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["left"], a["right"],
+                            a["ns"], a["i"], a["o_"], 0)
+
+
+def test_fwd_mask_validation():
+    # the mask's sizes are checked before any alignment, so the misaligned fakes still reach them
+    assert call_fwd_mask(mask=0) == bnd.FA_ERR_NULLPTR
+    assert call_fwd_mask(ld=76) == bnd.FA_ERR_SHAPE            # rows shorter than Nk
+    assert call_fwd_mask(sb=-4) == bnd.FA_ERR_SHAPE
+    assert call_fwd_mask(ld=(1 << 31) // 64) == bnd.FA_ERR_SHAPE  # Nq * row stride past 2^31 - 2^16
+    assert call_fwd_mask(d=80) == bnd.FA_ERR_UNSUPPORTED
+    assert call_fwd_mask(ns=17) == bnd.FA_ERR_SHAPE
+    for kw in (dict(ld=82, Nk=81), dict(sh=6), dict()):     # row stride, plane stride, pointers
+        assert call_fwd_mask(**kw) == bnd.FA_ERR_ALIGN
+
+
+def test_mask_strides_of_tensors():
+    import torch
+
+    m = torch.zeros(2, 3, 8, 12, dtype=torch.bool)
+    assert bnd.mask_strides(m, 2, 3, 8, 12) == (3 * 8 * 12, 8 * 12, 12)
+    assert bnd.mask_strides(m[:1], 2, 3, 8, 12) == (0, 8 * 12, 12)
+    assert bnd.mask_strides(m[:1, :1], 2, 3, 8, 12) == (0, 0, 12)
+    with pytest.raises(bnd.FaError):
+        bnd.mask_strides(torch.zeros(1, 1, 8, 10, dtype=torch.bool), 1, 1, 8, 10)  # row stride 10
+    with pytest.raises(bnd.FaError):
+        bnd.mask_strides(torch.zeros(1, 1, 8, 12, dtype=torch.float32), 1, 1, 8, 12)
+    with pytest.raises(bnd.FaError):
+        bnd.mask_strides(m, 2, 4, 8, 12)

@@ -1,0 +1,172 @@
+"""GPU parity of the mask input (fa_fwd_mask): a byte mask whose nonzero entries hide keys, on
+top of the band, shared across batch elements or heads when its axis has size 1.
+
+Bars as for the forward: O within 2e-3 (fp16) or 1e-2 (bf16) of the fp64 oracle, LSE within
+1e-4 relative with a floor of 1, rows the mask hides completely exactly O = 0 and LSE = -inf.
+Masks: random (independent bytes), block-structured (whole tiles hidden or kept, which takes
+the kernel's skip path and can leave a row's first tiles empty), and key padding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_114_amd as fa
+from exact_attention_114_amd import binding as bnd
+from exact_attention_114_amd import inputs as I
+from oracle.attention import attention_band_fp64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_O = {I.F16: 2e-3, I.BF16: 1e-2}
+TOL_LSE = 1e-4
+
+
+def to_dev(bits, dt):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dt == I.F16 else torch.bfloat16).to(DEV)
+
+
+def draw(B, Hq, Hkv, Nq, Nk, d, dt, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return tuple(I.to_bits(g.standard_normal(s, dtype=np.float32), dt)
+                 for s in ((B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)))
+
+
+def make_mask(kind, shape, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    Bm, Hm, Nq, Nk = shape
+    if kind == "random":
+        m = (g.random(shape) < 0.3).astype(np.uint8)
+    elif kind == "blocks":
+        # 32 x 32 blocks hidden or kept as wholes, plus a few single bytes
+        blk = (g.random((Bm, Hm, (Nq + 31) // 32, (Nk + 31) // 32)) < 0.5).astype(np.uint8)
+        m = np.repeat(np.repeat(blk, 32, axis=2), 32, axis=3)[:, :, :Nq, :Nk].copy()
+        m[..., g.integers(0, Nq, 8), g.integers(0, Nk, 8)] ^= 1
+    else:  # key padding: element b keeps its first len_b keys
+        lens = g.integers(1, Nk + 1, Bm)
+        m = np.broadcast_to((np.arange(Nk)[None, None, None, :] >= lens[:, None, None, None]),
+                            shape).astype(np.uint8).copy()
+    return m
+
+
+def mask_to_dev(mask):
+    """The mask on the GPU with its rows padded to a multiple of 4 bytes, passed as a view."""
+    Nk = mask.shape[-1]
+    padded = np.ones(mask.shape[:-1] + ((Nk + 3) // 4 * 4,), np.uint8)
+    padded[..., :Nk] = mask
+    return torch.from_numpy(padded).to(DEV)[..., :Nk]
+
+
+def run(B, Hq, Hkv, Nq, Nk, d, dt, band, mask, seed, splits=None, out16=False, values=None):
+    qb, kb, vb = draw(B, Hq, Hkv, Nq, Nk, d, dt, seed) if values is None else values
+    scale = 1.0 / math.sqrt(d)
+    print(f"[gpu] fa_fwd_mask B={B} Hq={Hq} Nq={Nq} Nk={Nk} d={d} {dt} band={band} mask={mask.shape} "
+          f"splits={splits}", flush=True)
+    out_dtype = (torch.float16 if dt == I.F16 else torch.bfloat16) if out16 else torch.float32
+    tm = mask_to_dev(mask)
+    O, L = fa.fwd(to_dev(qb, dt), to_dev(kb, dt), to_dev(vb, dt), scale=scale, window=band, mask=tm,
+                  splits=splits, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    q, k, v = (I.bits_to_f64(x, dt) for x in (qb, kb, vb))
+    O_ref, L_ref = attention_band_fp64(q, k, v, I.scale_f32(scale), *band, mask=mask)
+    O = O.float().cpu().numpy().astype(np.float64)
+    L = L.cpu().numpy().astype(np.float64)
+    empty = np.isneginf(L_ref)
+    assert (np.isneginf(L) == empty).all() and (O[empty] == 0).all()
+    bar = TOL_O[dt]
+    if out16:
+        bits = I.to_bits(np.abs(O_ref).astype(np.float32), dt)
+        bar = bar + 0.5 * (I.bits_to_f64(bits + np.uint16(1), dt) - I.bits_to_f64(bits, dt))
+    assert (np.abs(O - O_ref) <= bar).all(), f"max|dO| {np.abs(O - O_ref).max():.3e}"
+    seen = ~empty
+    if seen.any():
+        err = (np.abs(L[seen] - L_ref[seen]) / np.maximum(1.0, np.abs(L_ref[seen]))).max()
+        assert err <= TOL_LSE, f"LSE rel err {err:.3e}"
+    return O, L
+
+
+@pytest.mark.parametrize("kind", ["random", "blocks", "padding"])
+@pytest.mark.parametrize("mshape", ["shared", "batch", "full"])
+@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16)])
+def test_mask_kinds_and_broadcast(kind, mshape, d, dt):
+    B, Hq, Hkv, Nq, Nk = 2, 4, 2, 200, 264
+    Bm, Hm = {"shared": (1, 1), "batch": (B, 1), "full": (B, Hq)}[mshape]
+    mask = make_mask(kind, (Bm, Hm, Nq, Nk), 1500 + d)
+    run(B, Hq, Hkv, Nq, Nk, d, dt, (None, None), mask, 1510 + d)
+
+
+@pytest.mark.parametrize("band", [(None, 0), (40, 0), (30, 20)])
+@pytest.mark.parametrize("d,dt", [(64, I.BF16), (128, I.F16), (96, I.BF16), (32, I.F16)])
+def test_mask_with_band(band, d, dt):
+    mask = make_mask("random", (1, 1, 150, 150), 1520 + d)
+    run(1, 4, 4, 150, 150, d, dt, band, mask, 1530 + d)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mask_large_grid_and_rows_hidden(d):
+    """Above 512 work-groups (32-key steps at d = 128); some rows hidden completely."""
+    B, Hq, Hkv, N = 2, 16, 4, 2100
+    mask = make_mask("blocks", (B, 1, N, N), 1540 + d)
+    mask[:, :, 5] = 1
+    mask[:, :, 1000:1003] = 1
+    O, L = run(B, Hq, Hkv, N, N, d, I.BF16, (None, 0), mask, 1550 + d)
+    assert np.isneginf(L[:, :, 5]).all()
+
+
+def test_causal_mask_equals_causal_flag_bitwise():
+    qb, kb, vb = draw(2, 4, 2, 333, 333, 128, I.BF16, 1560)
+    q, k, v = (to_dev(x, I.BF16) for x in (qb, kb, vb))
+    i = np.arange(333)
+    causal = (i[None, :] > i[:, None]).astype(np.uint8)[None, None]
+    a = fa.fwd(q, k, v, causal=True)
+    # 333 keys is not a multiple of 4: pad the mask's rows and pass a view
+    padded = np.ones((1, 1, 333, 336), np.uint8)
+    padded[..., :333] = causal
+    b = fa.fwd(q, k, v, mask=torch.from_numpy(padded).to(DEV)[..., :333])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_zero_mask_equals_no_mask_bitwise():
+    qb, kb, vb = draw(1, 8, 2, 300, 512, 64, I.F16, 1570)
+    q, k, v = (to_dev(x, I.F16) for x in (qb, kb, vb))
+    a = fa.fwd(q, k, v, window=(100, 0))
+    b = fa.fwd(q, k, v, window=(100, 0), mask=torch.zeros(1, 1, 300, 512, dtype=torch.bool, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_mask_with_split_keys(splits):
+    mask = make_mask("random", (1, 1, 100, 3000), 1580)
+    run(1, 4, 2, 100, 3000, 128, I.BF16, (None, 0), mask, 1581, splits=splits)
+    run(1, 2, 2, 70, 2000, 64, I.F16, (None, None), make_mask("padding", (1, 2, 70, 2000), 1582)[:1], 1583,
+        splits=splits, out16=True)
+
+
+def test_mask_rescale_path():
+    """Scores that rise along the keys force the reference to move; the mask hides some of the
+    tiles where it would move (the rare path reloads the tile's mask)."""
+    B, Hq, Hkv, N, d, dt = 1, 4, 2, 333, 64, I.F16
+    g = np.random.Generator(np.random.PCG64(1590))
+    q = g.standard_normal((B, Hq, N, d), dtype=np.float32) + np.float32(1.0)
+    k = g.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    k += (np.float32(3.0) * np.arange(N, dtype=np.float32) / np.float32(N))[:, None]
+    k[:, :, N - 5, :] = np.float32(16.0)
+    v = g.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    values = tuple(I.to_bits(x, dt) for x in (q, k, v))
+    mask = make_mask("random", (1, 1, N, N), 1591)
+    mask[..., N - 5] = 0  # the spike stays visible: it moves the reference on the last tiles
+    run(B, Hq, Hkv, N, N, d, dt, (None, None), mask, 0, values=values)
+
+
+def test_mask_errors_raise():
+    qb, kb, vb = draw(1, 2, 2, 64, 30, 64, I.F16, 1595)
+    q, k, v = (to_dev(x, I.F16) for x in (qb, kb, vb))
+    with pytest.raises(bnd.FaError):  # 30 keys: row stride 30 is not a multiple of 4
+        fa.fwd(q, k, v, mask=torch.zeros(1, 1, 64, 30, dtype=torch.bool, device=DEV))
+    with pytest.raises(bnd.FaError):
+        fa.fwd(q, k, v, mask=torch.zeros(1, 3, 64, 32, dtype=torch.bool, device=DEV)[..., :30])
