@@ -38,6 +38,8 @@ SIGNATURES = {
     "fa_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                      + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
+    "fa_bwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 9 + [ctypes.c_float]
+                    + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
                     + [ctypes.c_int64] * 6 + [ctypes.c_float] + [ctypes.c_int64] * 2
                     + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
@@ -115,6 +117,14 @@ def fwd_mask_raw(q: int, k: int, v: int, o: int, lse: int, mask: int, m_sb: int,
     """Call fa_fwd_mask with raw device addresses; returns the fa_status code."""
     return load_library().fa_fwd_mask(q, k, v, o, lse, mask, m_sb, m_sh, m_ld, ws, B, Hq, Hkv, Nq, Nk, d,
                                       float(scale), left, right, n_splits, in_dtype, out_dtype, stream)
+
+
+def bwd_mask_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, ws: int,
+                 mask: int, m_sb: int, m_sh: int, m_ld: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                 scale: float, left: int, right: int, in_dtype: int, o_dtype: int, stream: int = 0) -> int:
+    """Call fa_bwd_mask with raw device addresses; returns the fa_status code."""
+    return load_library().fa_bwd_mask(q, k, v, o, lse, dout, dq, dk, dv, ws, mask, m_sb, m_sh, m_ld, B, Hq, Hkv,
+                                      Nq, Nk, d, float(scale), left, right, in_dtype, o_dtype, stream)
 
 
 def mask_strides(mask, B: int, Hq: int, Nq: int, Nk: int) -> Tuple[int, int, int]:
@@ -264,7 +274,7 @@ def bwd_ex_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk:
 
 
 def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False, window=None,
-        workspace=None, grads=None, stream=None):
+        workspace=None, grads=None, mask=None, stream=None):
     """Gradients (dQ, dK, dV) of exact attention on the GPU, all float32.
 
     q, k, v as for ``fwd``; o and lse as ``fwd`` returned them (o float32 or
@@ -273,7 +283,8 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
     sequence length). The workspace (a uint8 CUDA tensor of at least
     ``bwd_workspace_bytes`` bytes) and the outputs (``grads``: contiguous
     float32 dq [B, Hq, N, d], dk and dv [B, Hkv, N, d]) are allocated when not
-    given. Runs on ``stream`` or torch's current stream.
+    given. mask, as for ``fwd`` (and the same one the forward used), goes to fa_bwd_mask.
+    Runs on ``stream`` or torch's current stream.
     """
     import torch
 
@@ -316,6 +327,14 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
             raise FaError(FA_ERR_SHAPE, "grads must be contiguous float32 dq [B,Hq,Nq,d], dk and dv [B,Hkv,Nk,d]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if mask is not None:
+        if mask.device != q.device:
+            raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
+        sb, sh, ld = mask_strides(mask, B, Hq, N, Nk)
+        _check(bwd_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), mask.data_ptr(), sb, sh,
+                            ld, B, Hq, Hkv, N, Nk, d, scale, left, right, in_code, o_code, stream.cuda_stream))
+        return dq, dk, dv
     _check(bwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, Nk, d,
                       scale, left, right, in_code, o_code, stream.cuda_stream))

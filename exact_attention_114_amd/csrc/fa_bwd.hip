@@ -29,7 +29,7 @@ fa_status launched() {
   return FA_OK;
 }
 
-template <bool BF16, int D, bool BAND>
+template <bool BF16, int D, bool BAND, bool AM>
 fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t grid_kv, int64_t grid_q,
                      hipStream_t s) {
   constexpr int RPB = 256 / fa::prep_lanes(D);  // the prep kernel's rows per work-group
@@ -42,20 +42,29 @@ fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t gri
   if (st != FA_OK) return st;
   p.n_tiles = (int)((p.Nk + kTile - 1) / kTile);
   p.total_wg = (int)grid_kv;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves>), dim3((unsigned)grid_kv), dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves, AM>), dim3((unsigned)grid_kv), dim3(kWaves * 64), 0, s, p);
   st = launched();
   if (st != FA_OK) return st;
   p.n_tiles = (int)((p.Nq + kTile - 1) / kTile);
   p.total_wg = (int)grid_q;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves>), dim3((unsigned)grid_q), dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves, AM>), dim3((unsigned)grid_q), dim3(kWaves * 64), 0, s, p);
   return launched();
 }
 
+// A mask runs on the banded kernels (with unlimited edges when there is no band).
 template <bool BF16, int D>
-fa_status dispatch_band(const fa::BwdParams& p, bool band, bool o_f32, int64_t pr, int64_t gkv, int64_t gq,
+fa_status dispatch_band(const fa::BwdParams& p, bool band, bool am, bool o_f32, int64_t pr, int64_t gkv, int64_t gq,
                         hipStream_t s) {
-  return band ? launch_all<BF16, D, true>(p, o_f32, pr, gkv, gq, s) : launch_all<BF16, D, false>(p, o_f32, pr, gkv, gq, s);
+  if (am) return launch_all<BF16, D, true, true>(p, o_f32, pr, gkv, gq, s);
+  return band ? launch_all<BF16, D, true, false>(p, o_f32, pr, gkv, gq, s)
+              : launch_all<BF16, D, false, false>(p, o_f32, pr, gkv, gq, s);
 }
+
+// The optional mask of fa_bwd_mask (data == nullptr: none).
+struct MaskArg {
+  const void* data = nullptr;
+  int64_t b_stride = 0, h_stride = 0, row_stride = 0;
+};
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -75,20 +84,11 @@ fa_status check_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, 
   return FA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d) {
-  int64_t wb = 0, t = 0, u = 0;
-  if (check_bwd(B, Hq, 1, N, 1, d, &wb, &t, &u) != FA_OK) return 0;
-  return (size_t)(B * Hq * wb * 64 * (int64_t)sizeof(float));
-}
-
-fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                    const void* dout, float* dq, float* dk, float* dv, float* workspace, int64_t B, int64_t Hq,
-                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
-                    int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
+// fa_bwd_ex and fa_bwd_mask: validation and the three launches.
+fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  float* dq, float* dk, float* dv, float* workspace, const MaskArg& mask, int64_t B, int64_t Hq,
+                  int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                  int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
   int64_t ws_blk = 0, tq = 0, tk = 0;
   const fa_status st = check_bwd(B, Hq, Hkv, Nq, Nk, d, &ws_blk, &tq, &tk);
@@ -96,6 +96,15 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
   if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (o_dtype != FA_F32 && o_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
+  const bool am = mask.data != nullptr;
+  if (am) {
+    // as the forward's mask: dword-aligned rows and planes, 32-bit offsets within a plane
+    if (mask.row_stride < Nk || mask.b_stride < 0 || mask.h_stride < 0) return FA_ERR_SHAPE;
+    if (Nq * mask.row_stride > ((int64_t)1 << 31) - ((int64_t)1 << 16)) return FA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(mask.data) & 3u) || (mask.row_stride & 3) || (mask.b_stride & 3) ||
+        (mask.h_stride & 3))
+      return FA_ERR_ALIGN;
+  }
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return FA_ERR_ALIGN;
@@ -126,6 +135,10 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   p.total_wg = 0;
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   p.scale = scale;
+  p.am = static_cast<const unsigned char*>(mask.data);
+  p.am_sb = mask.b_stride;
+  p.am_sh = mask.h_stride;
+  p.am_ld = (int)mask.row_stride;
 
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const int64_t prep_rows = B * Hq * ws_blk * 32;
@@ -136,8 +149,8 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   switch (d) {
 #define FA_BWD_D(DD)                                                                            \
   case DD:                                                                                      \
-    return bf16 ? dispatch_band<true, DD>(p, band, o_f32, prep_rows, grid_kv, grid_q, s)        \
-                : dispatch_band<false, DD>(p, band, o_f32, prep_rows, grid_kv, grid_q, s);
+    return bf16 ? dispatch_band<true, DD>(p, band, am, o_f32, prep_rows, grid_kv, grid_q, s)    \
+                : dispatch_band<false, DD>(p, band, am, o_f32, prep_rows, grid_kv, grid_q, s);
     FA_BWD_D(32)
     FA_BWD_D(64)
     FA_BWD_D(96)
@@ -145,6 +158,39 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
 #undef FA_BWD_D
   }
   return FA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d) {
+  int64_t wb = 0, t = 0, u = 0;
+  if (check_bwd(B, Hq, 1, N, 1, d, &wb, &t, &u) != FA_OK) return 0;
+  return (size_t)(B * Hq * wb * 64 * (int64_t)sizeof(float));
+}
+
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, float* dq, float* dk, float* dv, float* workspace, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                    int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, workspace, MaskArg{}, B, Hq, Hkv, Nq, Nk, d, scale, window_left,
+                 window_right, in_dtype, o_dtype, stream);
+}
+
+fa_status fa_bwd_mask(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, float* workspace, const void* mask,
+                      int64_t mask_b_stride, int64_t mask_h_stride, int64_t mask_row_stride, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                      int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
+  if (!mask) return FA_ERR_NULLPTR;
+  MaskArg m;
+  m.data = mask;
+  m.b_stride = mask_b_stride;
+  m.h_stride = mask_h_stride;
+  m.row_stride = mask_row_stride;
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, workspace, m, B, Hq, Hkv, Nq, Nk, d, scale, window_left,
+                 window_right, in_dtype, o_dtype, stream);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

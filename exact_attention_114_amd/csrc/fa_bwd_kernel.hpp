@@ -54,6 +54,11 @@ struct BwdParams {
   int total_wg;
   float c;       // scale * log2(e)
   float scale;
+  // optional byte mask (kernels built with AM), as in the forward's Params: nonzero hides key j
+  // from query i of head (b, hq) at am + b*am_sb + hq*am_sh + i*am_ld + j
+  const unsigned char* am;
+  long long am_sb, am_sh;
+  int am_ld;
 };
 
 // One LDS swizzle for tiles that are read both as rows (ds_read_b128: 16 consecutive rows at one
@@ -215,9 +220,15 @@ __device__ inline int lane_bytes4() {
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 2, %0" : "=v"(v));
   return v;
 }
+// The lane id, formed the same opaque way (held in no register across a loop).
+__device__ inline int lane_id_here() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
 
 // ---- 2. dK/dV ---------------------------------------------------------------------------------
-template <bool BF16, int D, bool BAND, int NW>
+template <bool BF16, int D, bool BAND, int NW, bool AM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -232,6 +243,11 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   __shared__ __attribute__((aligned(256))) float sW1[64];
   constexpr bool VL = bwd_v_in_lds(D);
   __shared__ __attribute__((aligned(1024))) char sV[VL ? NW * TB : 16];
+  // mask tiles: 32 query rows x the work-group's 32*NW keys, one byte each, double-buffered
+  static_assert(!AM || BAND, "the masked kernels are built on the banded ones");
+  constexpr int MROW = 32 * NW, MTB = 32 * MROW;
+  __shared__ __attribute__((aligned(1024))) char sM0[AM ? MTB : 16];
+  __shared__ __attribute__((aligned(1024))) char sM1[AM ? MTB : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -279,11 +295,35 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   const int nqb = q_hi >= q_lo ? q_hi / 32 - qb0 + 1 : 0;
   const int n_it = G * nqb;
 
-  auto issue_loads = [&](int it, lds_char* dq_, lds_char* dg_, float* dw_) {
+  // Mask tile DMA (4-byte loads): wave w fills rows [8w, 8w + 8) of the 32-row tile, two rows
+  // of MROW bytes per instruction; lane l writes row 8w + 2n + l/32, bytes 4(l%32) .. +3. Its
+  // offset within the instruction's rows is loop invariant; the instruction's first row goes into
+  // the descriptor base. Bytes past the head's plane read as zero; bytes of keys past Nk or rows
+  // past Nq only meet scores whose results are never stored (or multiply zero rows of dO).
+  constexpr int MRPW = 32 / NW;               // mask rows per wave
+  constexpr int MNI = MRPW * MROW / 256;      // 4-byte DMA instructions per wave per tile
+  static_assert(MROW == 128 && MNI * 256 == MRPW * MROW, "two 128-byte rows per instruction");
+  auto dma_mask = [&](int64_t head, int qb, lds_char* dm_) {
+    const int ln = lane_id_here();
+    const int am_off = (ln >> 5) * p.am_ld + 4 * (ln & 31);
+    const int64_t hb = head / p.Hq, hh = head - hb * p.Hq;
+    const unsigned char* plane = p.am + hb * p.am_sb + hh * p.am_sh;
+    const int64_t plane_bytes = (int64_t)Nq * p.am_ld;
+#pragma unroll
+    for (int n = 0; n < MNI; ++n) {
+      const int64_t first = (int64_t)(qb * 32 + MRPW * wave + 2 * n) * p.am_ld + k0;
+      const int64_t left = plane_bytes - first;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(plane + (left > 0 ? first : 0)), (short)0, left > 0 ? (int)left : 0, kBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dm_ + (MRPW * wave + 2 * n) * MROW), 4, am_off, 0, 0, 0);
+    }
+  };
+  auto issue_loads = [&](int it, lds_char* dq_, lds_char* dg_, float* dw_, lds_char* dm_) {
     const int g = it / nqb, qb = qb0 + (it - g * nqb);
     const int64_t head = (int64_t)b * p.Hq + hkv * G + g;
     dma_rows<D, NW>((const char*)((const T*)p.q + head * Nq * D), Nq, qb * 32, dq_, wave, ld_off);
     dma_rows<D, NW>((const char*)((const T*)p.dout + head * Nq * D), Nq, qb * 32, dg_, wave, ld_off);
+    if constexpr (AM) dma_mask(head, qb, dm_);
     if (wave == 0) {
       void* wp = (void*)(p.ws + (head * p.ws_blk + qb) * 64);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(wp, (short)0, 256, kBufferWord3);
@@ -299,7 +339,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   }
   const float c = p.c;
 
-  if (n_it > 0) issue_loads(0, (lds_char*)sQ0, (lds_char*)sG0, sW0);
+  if (n_it > 0) issue_loads(0, (lds_char*)sQ0, (lds_char*)sG0, sW0, (lds_char*)sM0);
   for (int it = 0; it < n_it; ++it) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -307,7 +347,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     const lds_char* tq = (const lds_char*)(odd ? sQ1 : sQ0);
     const lds_char* tg = (const lds_char*)(odd ? sG1 : sG0);
     const float* tw = odd ? sW1 : sW0;
-    if (it + 1 < n_it) issue_loads(it + 1, (lds_char*)(odd ? sQ0 : sQ1), (lds_char*)(odd ? sG0 : sG1), odd ? sW0 : sW1);
+    const lds_char* tm = (const lds_char*)(odd ? sM1 : sM0);
+    if (it + 1 < n_it)
+      issue_loads(it + 1, (lds_char*)(odd ? sQ0 : sQ1), (lds_char*)(odd ? sG0 : sG1), odd ? sW0 : sW1,
+                  (lds_char*)(odd ? sM0 : sM1));
     const int qb = qb0 + (it % nqb);
     const int q0 = qb * 32;
 
@@ -345,6 +388,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
           const int pa = 8 * g4 + 2 * r2, pb = pa + 1;
           s0 = (unsigned)(pa - vlo) > width ? -__builtin_inff() : s0;
           s1 = (unsigned)(pb - vlo) > width ? -__builtin_inff() : s1;
+        }
+        if constexpr (AM) {
+          // mask bytes of queries 8g4 + 4h + 2r2 (+1) and this lane's key
+          const int ln = lane_id_here();
+          const lds_char* mp = tm + (8 * g4 + 2 * r2) * MROW + 32 * wave + (ln >> 5) * (4 * MROW) + (ln & 31);
+          s0 = *(const lds_uchar*)mp != 0 ? -__builtin_inff() : s0;
+          s1 = *(const lds_uchar*)(mp + MROW) != 0 ? -__builtin_inff() : s1;
         }
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a[2 * r2]));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -a[2 * r2 + 1]));
@@ -389,7 +439,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
 }
 
 // ---- 3. dQ ------------------------------------------------------------------------------------
-template <bool BF16, int D, bool BAND, int NW>
+template <bool BF16, int D, bool BAND, int NW, bool AM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -455,6 +505,23 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
   const float c = p.c;
 
+  // mask words of the lane's query for a 32-key tile: dword g holds keys 32j + 8g + 4h + (0..3),
+  // i.e. scores 4g .. 4g+3 (as in the forward); loaded one tile ahead, the offset wholly in the
+  // vector operand so reads past the head's plane return zeros
+  unsigned am_w[4] = {0u, 0u, 0u, 0u};
+  __amdgpu_buffer_rsrc_t am_rs;
+  int am_v0 = 0;
+  auto load_am = [&](int jt) {
+    const int vo = am_v0 + 32 * jt;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) am_w[g4] = __builtin_amdgcn_raw_buffer_load_b32(am_rs, vo + 8 * g4, 0, 0);
+  };
+  if constexpr (AM) {
+    const unsigned char* plane = p.am + (long long)b * p.am_sb + (long long)hq * p.am_sh;
+    am_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.am_ld, kBufferWord3);
+    am_v0 = qr * p.am_ld + 4 * h;
+    if (nt > 0) load_am(j_lo);
+  }
   if (nt > 0) {
     dma_rows<D, NW>(Kp, Nk, j_lo * 32, (lds_char*)sK0, wave, ld_off);
     dma_rows<D, NW>(Vp, Nk, j_lo * 32, (lds_char*)sV0, wave, ld_off);
@@ -486,6 +553,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
         const int part = 8 * (i >> 2) + (i & 3);
         s[i] = (part > hi || (BAND && part < lo)) ? -__builtin_inff() : s[i];
       }
+    }
+    if constexpr (AM) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = ((am_w[i >> 2] >> (8 * (i & 3))) & 0xffu) != 0u ? -__builtin_inff() : s[i];
+      if (r + 1 < nt) load_am(j + 1);  // the next iteration's opening wait covers it
     }
     u32x4 sw[2];
 #pragma unroll

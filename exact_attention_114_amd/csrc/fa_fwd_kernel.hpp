@@ -84,6 +84,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_uchar;
 
 // A lane's sum of one tile's exponentials above this (2^8) triggers a rescale; below it every
 // exponential of the tile is at most 2^8.

@@ -249,6 +249,21 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
 
 /*
+ * fa_bwd_mask — fa_bwd_ex for a forward run with fa_fwd_mask: the same mask
+ * (arguments and layout as fa_fwd_mask) hides the same scores, so P and dS
+ * are zero there. The LSE must come from the masked forward.
+ * Other arguments, errors and execution as fa_bwd_ex; a NULL mask is
+ * FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN.
+ */
+fa_status fa_bwd_mask(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                      float* workspace, const void* mask, int64_t mask_b_stride,
+                      int64_t mask_h_stride, int64_t mask_row_stride, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                      int64_t window_left, int64_t window_right, fa_dtype in_dtype,
+                      fa_dtype o_dtype, void* stream);
+
+/*
  * fa_bwd_workspace_bytes — size in bytes of the workspace fa_bwd (or
  * fa_bwd_ex, with N = Nq) needs for these sizes (two floats per query row,
  * rows padded to a multiple of 128), or 0 when the sizes are invalid for

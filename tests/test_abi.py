@@ -309,3 +309,19 @@ def test_mask_strides_of_tensors():
         bnd.mask_strides(torch.zeros(1, 1, 8, 12, dtype=torch.float32), 1, 1, 8, 12)
     with pytest.raises(bnd.FaError):
         bnd.mask_strides(m, 2, 4, 8, 12)
+
+
+def test_bwd_mask_validation():
+    def call(**kw):
+        a = dict(mask=BAD, sb=0, sh=0, ld=80, B=1, Hq=2, Hkv=1, Nq=64, Nk=80, d=64, i=bnd.FA_F16)
+        a.update(kw)
+        return bnd.bwd_mask_raw(BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, a["mask"], a["sb"], a["sh"], a["ld"],
+                                a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], 0.125, -1, -1, a["i"],
+                                bnd.FA_F32, 0)
+    assert call(mask=0) == bnd.FA_ERR_NULLPTR
+    assert call(ld=76) == bnd.FA_ERR_SHAPE
+    assert call(sh=-4) == bnd.FA_ERR_SHAPE
+    assert call(ld=(1 << 31) // 64) == bnd.FA_ERR_SHAPE
+    assert call(d=80) == bnd.FA_ERR_UNSUPPORTED
+    for kw in (dict(ld=82, Nk=81), dict(sb=2), dict()):
+        assert call(**kw) == bnd.FA_ERR_ALIGN

@@ -170,3 +170,62 @@ def test_mask_errors_raise():
         fa.fwd(q, k, v, mask=torch.zeros(1, 1, 64, 30, dtype=torch.bool, device=DEV))
     with pytest.raises(bnd.FaError):
         fa.fwd(q, k, v, mask=torch.zeros(1, 3, 64, 32, dtype=torch.bool, device=DEV)[..., :30])
+
+
+# ---------------------------------------------------------------- gradients
+
+UNIT = {I.F16: 2.0 ** -11, I.BF16: 2.0 ** -8}
+
+
+def run_bwd(B, Hq, Hkv, Nq, Nk, d, dt, band, mask, seed):
+    """fa_bwd_mask against the fp64 gradients, within twice the first-order bound of the
+    oracle's error model (as the unmasked backward tests)."""
+    from oracle.attention import kv_head_of
+    from oracle.backward import attention_bwd_band_fp64, head_attention_bwd_bound_fp64
+
+    g = np.random.Generator(np.random.PCG64(seed))
+    qb, kb, vb, dob = (I.to_bits(g.standard_normal(s, dtype=np.float32), dt)
+                       for s in ((B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d), (B, Hq, Nq, d)))
+    scale = 1.0 / math.sqrt(d)
+    sc = I.scale_f32(scale)
+    q, k, v, do = (I.bits_to_f64(x, dt) for x in (qb, kb, vb, dob))
+    O, L = attention_band_fp64(q, k, v, sc, *band, mask=mask)
+    o32 = O.astype(np.float32)
+    print(f"[gpu] fa_bwd_mask B={B} Hq={Hq} Nq={Nq} Nk={Nk} d={d} {dt} band={band} mask={mask.shape}", flush=True)
+    grads = fa.bwd(to_dev(qb, dt), to_dev(kb, dt), to_dev(vb, dt), torch.from_numpy(o32).to(DEV),
+                   torch.from_numpy(L.astype(np.float32)).to(DEV), to_dev(dob, dt), scale=scale, window=band,
+                   mask=mask_to_dev(mask))
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy().astype(np.float64) for t in grads]
+    ref = attention_bwd_band_fp64(q, k, v, do, sc, *band, mask=mask)
+    bq = np.empty(q.shape)
+    bk = np.zeros(k.shape)
+    bv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head_of(h, Hq, Hkv)
+            hid = mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]
+            x, y, z = head_attention_bwd_bound_fp64(q[b, h], k[b, hk], v[b, hk], do[b, h], o32[b, h].astype(np.float64),
+                                                    sc, False, UNIT[dt], band=(band[0], band[1], Nk - Nq), hidden=hid)
+            bq[b, h] = x
+            bk[b, hk] += y
+            bv[b, hk] += z
+    for name, gg, r, bb in zip(("dQ", "dK", "dV"), got, ref, (bq, bk, bv)):
+        assert np.isfinite(gg).all(), f"non-finite {name}"
+        ratio = (np.abs(gg - r) / np.maximum(2.0 * bb, 1e-300)).max()
+        assert ratio <= 1.0, f"{name} error reaches {ratio:.3f} of the bar"
+
+
+@pytest.mark.parametrize("kind", ["random", "blocks", "padding"])
+@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16), (96, I.BF16), (32, I.F16)])
+def test_bwd_mask_kinds(kind, d, dt):
+    mask = make_mask(kind, (2, 1, 150, 260), 1600 + d)
+    run_bwd(2, 4, 2, 150, 260, d, dt, (None, None), mask, 1610 + d)
+
+
+@pytest.mark.parametrize("band", [(None, 0), (40, 10)])
+@pytest.mark.parametrize("d,dt", [(64, I.BF16), (128, I.F16)])
+def test_bwd_mask_with_band_and_hidden_rows(band, d, dt):
+    mask = make_mask("random", (1, 4, 200, 200), 1620 + d)
+    mask[:, 1, 7] = 1
+    run_bwd(1, 4, 2, 200, 200, d, dt, band, mask, 1630 + d)
