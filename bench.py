@@ -98,7 +98,9 @@ def planned_splits(w, splits: int) -> int:
     return ws // (w.B * w.Hq * w.N * (w.d + 1) * 4) if ws else 1
 
 
-def time_gpu(w, steps: int, warmup: int, splits: int = 0):
+def time_gpu(w, steps: int, warmup: int, splits: int = 0, mask=None):
+    """Seconds of wall time for `steps` forward calls, and the HIP-event average per call.
+    mask: an optional uint8 [B or 1, Hq or 1, N, Nk] array passed to fa_fwd_mask."""
     import torch
 
     import exact_attention_114_amd as fa
@@ -114,10 +116,11 @@ def time_gpu(w, steps: int, warmup: int, splits: int = 0):
     ws_bytes = binding.split_workspace_bytes(w.B, w.Hq, w.N, w.nk, w.d, splits)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    tm = None if mask is None else torch.from_numpy(mask).to(dev)
 
     def call():
         fa.fwd(q, k, v, scale=w.scale, window=w.band, out=out, lse=lse, splits=splits, workspace=ws,
-               stream=stream)
+               mask=tm, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -134,6 +137,29 @@ def time_gpu(w, steps: int, warmup: int, splits: int = 0):
     ev_ms = ev0.elapsed_time(ev1)
     assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
     return wall, ev_ms / steps
+
+
+def bench_mask(w, kind: str):
+    """A seeded byte mask for the workload and the FLOPs it leaves: 4 d per visible (query, key)
+    pair, the band and the mask both applied.
+
+    "document": each sequence packs documents of 1/8 to 1/2 of its length (drawn per batch
+    element from PCG64(seed + 2000)); a query sees only keys of its own document, one
+    [B, 1, N, N] mask shared by the heads.
+    """
+    import numpy as np
+
+    from exact_attention_114_amd import inputs as I
+
+    if kind != "document" or w.nk != w.N or w.window_left is not None:
+        raise SystemExit(f"--mask {kind}: only 'document' on square unwindowed workloads")
+    lens = I.document_lengths(w.B, w.N, w.seed + 2000, w.N // 8, w.N // 2)
+    mask = I.document_mask(lens, w.N)
+    pairs = 0
+    for row in lens:
+        for n in row:
+            pairs += n * (n + 1) // 2 if w.causal else n * n
+    return mask, 4.0 * w.Hq * w.d * pairs, lens
 
 
 BWD_METRIC = "attention bwd TFLOP/s (10·B·H·N²·d, causal halved) and % of MFMA peak, 1 GPU"
@@ -327,6 +353,7 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--bwd", action="store_true")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--mask", default="", help="'document': packed-document byte mask (fa_fwd_mask)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="")
     args = ap.parse_args()
@@ -375,8 +402,8 @@ def main():
                       flush=True)
 
     torch.cuda.synchronize()
-    wall, ms_launch = time_gpu(w, args.steps, args.warmup, args.splits)
-    flops = w.flops
+    mask, flops, doc_lens = (None, w.flops, None) if not args.mask else bench_mask(w, args.mask)
+    wall, ms_launch = time_gpu(w, args.steps, args.warmup, args.splits, mask)
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ms_launch * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -410,10 +437,16 @@ def main():
                      "algorithmic_hbm_bytes": algorithmic_bytes(w),
                      "kernel_ms": round(ms_launch, 5)},
     }
+    if mask is not None:
+        line["config"]["mask"] = {"kind": args.mask, "shape": list(mask.shape),
+                                  "documents_per_sequence": [len(r) for r in doc_lens],
+                                  "visible_fraction": round(flops / w.flops, 5)}
+        line["roofline"]["traffic"] = None
+        line["roofline"]["algorithmic_hbm_bytes"] = algorithmic_bytes(w) + float(mask.size)
     if ns > 1:
         line["roofline"]["note"] = ("split keys: kernel_ms and achieved cover the attention kernel and the "
                                     "merge kernel together (HIP events around the whole call)")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mask is None:  # the pooled oracle takes no mask
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
 

@@ -217,3 +217,31 @@ def small_case(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str, causal: bo
         scale = 1.0 / math.sqrt(d)
     return Workload(f"case_b{B}_hq{Hq}_hkv{Hkv}_n{N}_d{d}_{dtype}_{'c' if causal else 'nc'}_s{seed}",
                     B, Hq, Hkv, N, d, dtype, causal, scale, seed, k_mult)
+
+
+def document_lengths(B: int, N: int, seed: int, min_len: int, max_len: int) -> List[List[int]]:
+    """Lengths of the documents packed into each of B sequences of N tokens: each drawn
+    uniformly from [min_len, max_len] with PCG64(seed), the last one cut at N."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(B):
+        lens, total = [], 0
+        while total < N:
+            n = int(min(N - total, g.integers(min_len, max_len + 1)))
+            lens.append(n)
+            total += n
+        out.append(lens)
+    return out
+
+
+def document_mask(lengths: List[List[int]], N: int) -> np.ndarray:
+    """[B, 1, N, N] uint8 mask of packed documents: 1 (hidden) where query i and key j lie in
+    different documents of their sequence, 0 where they share one."""
+    B = len(lengths)
+    m = np.ones((B, 1, N, N), np.uint8)
+    for b, lens in enumerate(lengths):
+        s = 0
+        for n in lens:
+            m[b, 0, s:s + n, s:s + n] = 0
+            s += n
+    return m
