@@ -38,6 +38,7 @@ SIGNATURES = {
     "fa_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                      + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
+    "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
     "fa_bwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 9 + [ctypes.c_float]
                     + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
@@ -150,6 +151,11 @@ def split_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: i
     return int(load_library().fa_fwd_split_workspace_bytes(B, Hq, Nq, Nk, d, n_splits))
 
 
+def mask_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: int) -> int:
+    """Bytes of workspace fa_fwd_mask needs (0 for sizes it rejects)."""
+    return int(load_library().fa_fwd_mask_workspace_bytes(B, Hq, Nq, Nk, d, n_splits))
+
+
 def _edges(causal: bool, window) -> Tuple[int, int]:
     """(left, right) band edges for the C ABI, -1 meaning unlimited."""
     if window is None:
@@ -228,13 +234,13 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
             raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
         sb, sh, ld = mask_strides(mask, B, Hq, N, Nk)
         ns = 1 if splits is None else int(splits)
-        need = split_workspace_bytes(B, Hq, N, Nk, d, ns)
-        if need and workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        if need and (workspace.device != q.device or workspace.numel() * workspace.element_size() < need):
+        need = mask_workspace_bytes(B, Hq, N, Nk, d, ns)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        if workspace.device != q.device or workspace.numel() * workspace.element_size() < need:
             raise FaError(FA_ERR_SHAPE, f"workspace must hold {need} bytes on the inputs' device")
         _check(fwd_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                            mask.data_ptr(), sb, sh, ld, workspace.data_ptr() if need else 0, B, Hq, Hkv, N, Nk, d,
+                            mask.data_ptr(), sb, sh, ld, workspace.data_ptr(), B, Hq, Hkv, N, Nk, d,
                             scale, left, right, ns, in_code, out_code, stream.cuda_stream))
         return out, lse
     if splits is not None:

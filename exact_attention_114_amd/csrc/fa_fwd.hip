@@ -131,8 +131,15 @@ struct MaskArg {
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
 };
 
+// Workspace of a masked call: the split partials (if any), then the mask hull at the next
+// 256-byte boundary, sized for a mask with a plane per (batch, head).
+int64_t split_bytes(int ns, int64_t rows, int64_t d) { return ns > 1 ? ns * rows * (d + 1) * 4 : 0; }
+int64_t hull_offset(int ns, int64_t rows, int64_t d) { return (split_bytes(ns, rows, d) + 255) / 256 * 256; }
+int64_t hull_chunks(int64_t Nk) { return (Nk + fa::kHullKeys - 1) / fa::kHullKeys; }
+
 // Every forward entry point: validation, the split plan (n_splits = 1: never split; workspace
-// is then unused), the attention kernel and, with split keys, the merge.
+// is then unused unless there is a mask), the mask hull, the attention kernel and, with split
+// keys, the merge.
 fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
                   int64_t window_right, int n_splits, const MaskArg& mask, fa_dtype in_dtype, fa_dtype out_dtype,
@@ -145,10 +152,10 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   int ns = 1, kc = (int)(((Nk + 63) / 64) * 64);
   split_plan(grid, Nk, n_splits, &ns, &kc);
   if (ns == 1) kc = (int)(((Nk + 63) / 64) * 64);
-  if (ns > 1 && !workspace) return FA_ERR_NULLPTR;
+  const bool am = mask.data != nullptr;
+  if ((ns > 1 || am) && !workspace) return FA_ERR_NULLPTR;
   if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
   if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
-  const bool am = mask.data != nullptr;
   if (am) {
     // dword reads of the mask: rows, planes and the pointer 4-byte aligned; a head's plane
     // addressed with 32-bit offsets
@@ -160,10 +167,13 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
       return FA_ERR_ALIGN;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      (ns > 1 && !aligned16(workspace)))
+      ((ns > 1 || am) && !aligned16(workspace)))
     return FA_ERR_ALIGN;
   const int64_t rows = B * Hq * Nq;
   if (grid * ns >= ((int64_t)1 << 31) || rows * d * ns >= ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  const int64_t planes_b = am && mask.b_stride ? B : 1, planes_h = am && mask.h_stride ? Hq : 1;
+  const int64_t nch = hull_chunks(Nk);
+  if (am && planes_b * planes_h * nq * nch >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;  // hull grid
 
   fa::Params p;
   p.q = q;
@@ -189,6 +199,11 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   p.am_sb = mask.b_stride;
   p.am_sh = mask.h_stride;
   p.am_ld = (int)mask.row_stride;
+  int2* hull = am ? reinterpret_cast<int2*>(reinterpret_cast<char*>(workspace) + hull_offset(ns, rows, d)) : nullptr;
+  p.am_hull = hull;
+  p.hull_nch = (int)nch;
+  p.hull_sh = planes_h > 1 ? nq * nch : 0;
+  p.hull_sb = planes_b > 1 ? planes_h * nq * nch : 0;
 
   // With both edges unlimited every key is visible and no band is applied.
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
@@ -196,6 +211,29 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   const bool out_f32 = ns > 1 || out_dtype == FA_F32;
   const int kb = key_blocks(d, grid * ns);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (am) {
+    fa::HullParams hp;
+    hp.am = p.am;
+    hp.am_sb = p.am_sb;
+    hp.am_sh = p.am_sh;
+    hp.am_ld = p.am_ld;
+    hp.hull = hull;
+    hp.planes_b = (int)planes_b;
+    hp.planes_h = (int)planes_h;
+    hp.Nq = p.Nq;
+    hp.Nk = p.Nk;
+    hp.off = p.off;
+    hp.left = p.left;
+    hp.right = p.right;
+    hp.n_qtiles = p.n_qtiles;
+    hp.nch = (int)nch;
+    hipLaunchKernelGGL(fa::fa_mask_hull_kernel<kBlockM>, dim3((unsigned)(planes_b * planes_h * nq * nch)), dim3(256), 0, s, hp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      fa::last_hip_error = (int)e;
+      return FA_ERR_HIP;
+    }
+  }
   st = bf16 ? dispatch_d<true>(p, (int)d, band, am, out_f32, kb, s)
             : dispatch_d<false>(p, (int)d, band, am, out_f32, kb, s);
   if (st != FA_OK || ns == 1) return st;
@@ -251,6 +289,15 @@ size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t N
   split_plan(grid, Nk, n_splits, &ns, &kc);
   if (ns == 1) return 0;
   return (size_t)(ns * B * Hq * Nq * (d + 1) * (int64_t)sizeof(float));
+}
+
+size_t fa_fwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int n_splits) {
+  int64_t nq = 0, grid = 0;
+  if (n_splits < 0 || n_splits > kMaxSplits) return 0;
+  if (check_problem(B, Hq, 1, Nq, Nk, d, FA_F16, &nq, &grid) != FA_OK) return 0;
+  int ns = 1, kc = 0;
+  split_plan(grid, Nk, n_splits, &ns, &kc);
+  return (size_t)(hull_offset(ns, B * Hq * Nq, d) + B * Hq * nq * hull_chunks(Nk) * (int64_t)sizeof(int2));
 }
 
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,

@@ -50,7 +50,10 @@
 //      the Mask step of FlashAttention-1's Algorithm 2 that the cnblogs page points to) hides a
 //      key from a query where its byte is nonzero, on top of the band. A lane reads the 16 bytes
 //      of its query row that match its 16 scores of a 32-key block as 4 dwords, one step ahead,
-//      and a wave skips the per-score selects on tiles its mask leaves whole.
+//      and a wave skips the per-score selects on tiles its mask leaves whole. A pre-pass
+//      (fa_mask_hull_kernel) records, per Q-tile and chunk of keys, the first and last key any
+//      row of the tile may see; the attention kernel visits only the tiles between them, so
+//      keys a mask hides from a whole Q-tile (other documents, padding) cost nothing.
 //   7. Split keys. When batch x heads x Q-tiles leaves the GPU under-filled, the keys of each
 //      Q-tile can be cut into chunks handled by separate work-groups (the FA2 walkthrough's
 //      point about adding parallelism along the sequence when batch and heads are small); each
@@ -124,7 +127,16 @@ struct Params {
   const unsigned char* am;
   long long am_sb, am_sh;
   int am_ld;
+  // the mask's key hull (fa_mask_hull_kernel): int2 {first, last} visible key per (b, hq) mask
+  // plane, Q-tile and chunk of kHullKeys keys at am_hull + b*hull_sb + hq*hull_sh +
+  // t*hull_nch + chunk (the strides are 0 along an axis the mask shares)
+  const int2* am_hull;
+  long long hull_sb, hull_sh;
+  int hull_nch;
 };
+
+// Keys per chunk of the mask hull.
+constexpr int kHullKeys = 1024;
 
 // ---- element-type traits ------------------------------------------------------------------
 template <bool BF16>
@@ -399,8 +411,22 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, AM)))) void fa_fwd_kern
   // the K/V tiles the Q-tile's band touches: [j_lo, j_lo + nt)
   // keys this work-group may use: its chunk [split*kchunk, kend) (all keys when not split)
   const int kend = min(Nk, (split + 1) * p.kchunk);
-  const int lo_t = max(split * p.kchunk, BAND ? q0 + p.off - p.left : 0);
-  const int hi_t = min(kend - 1, BAND ? min(q0 + BM, Nq) - 1 + p.off + p.right : Nk - 1);
+  int lo_t = max(split * p.kchunk, BAND ? q0 + p.off - p.left : 0);
+  int hi_t = min(kend - 1, BAND ? min(q0 + BM, Nq) - 1 + p.off + p.right : Nk - 1);
+  if constexpr (AM) {
+    // narrow to the mask's hull for this Q-tile: keys outside it are hidden from every row
+    if (hi_t >= lo_t) {
+      const int2* hl = p.am_hull + b * p.hull_sb + hq * p.hull_sh + (int64_t)t * p.hull_nch;
+      int kmin = 0x7fffffff, kmax = -1;
+      for (int ch = lo_t / kHullKeys; ch <= hi_t / kHullKeys; ++ch) {
+        const int2 e = hl[ch];
+        kmin = min(kmin, e.x);
+        kmax = max(kmax, e.y);
+      }
+      lo_t = max(lo_t, kmin);
+      hi_t = min(hi_t, kmax);
+    }
+  }
   const int j_lo = lo_t / BN;
   const int nt = hi_t >= lo_t ? hi_t / BN - j_lo + 1 : 0;
   // the lane's visible keys: [klo, khi]. khi also stops at the chunk's end: the steps run past
@@ -726,6 +752,89 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, AM)))) void fa_fwd_kern
     if (h == 0)
       Ls[(int64_t)(b * p.Hq + hq) * Nq + qrow] =
           l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
+  }
+}
+
+// Mask hull: for one mask plane, one Q-tile of BM rows and one chunk of kHullKeys keys, the
+// first and last key that some row of the tile may see (mask byte zero, inside the tile's band,
+// below Nk), or {INT_MAX, -1} when there is none. 256 threads: thread x reads the dword of
+// keys k0 + 4x .. k0 + 4x + 3 of every row of the tile whose band reaches them (a wave reads 256
+// consecutive bytes of a row; every offset lies inside the plane); bytes past Nk never count.
+struct HullParams {
+  const unsigned char* am;
+  long long am_sb, am_sh;
+  int am_ld;
+  int2* hull;                // [planes_b][planes_h][n_qtiles][nch]
+  int planes_b, planes_h;    // B or 1, Hq or 1
+  int Nq, Nk, off, left, right;
+  int n_qtiles, nch;
+};
+
+template <int BM>
+__global__ __launch_bounds__(256) void fa_mask_hull_kernel(const HullParams p) {
+  int wg = blockIdx.x;
+  const int ch = wg % p.nch;
+  wg /= p.nch;
+  const int t = wg % p.n_qtiles;
+  const int plane = wg / p.n_qtiles;
+  const int pb = plane / p.planes_h, ph = plane - pb * p.planes_h;
+  const int q0 = t * BM, q1 = min(q0 + BM, p.Nq) - 1;
+  const int k0 = ch * kHullKeys, k1 = min(k0 + kHullKeys, p.Nk) - 1;
+  int kmin = 0x7fffffff, kmax = -1;
+  // the tile's band reaches keys q0 + off - left .. q1 + off + right (64-bit: edges may be 2^30)
+  if ((int64_t)k0 <= (int64_t)q1 + p.off + p.right && (int64_t)k1 >= (int64_t)q0 + p.off - p.left) {
+    const unsigned char* base = p.am + (long long)pb * p.am_sb + (long long)ph * p.am_sh;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, p.Nq * p.am_ld,
+                                                                        kBufferWord3);
+    const int key = k0 + 4 * (int)threadIdx.x;
+    if (key <= k1) {
+      // bit 7 of byte b of `zero` is set when some row's byte b is zero; rows past the tile or
+      // whose band misses this dword are not read. (Bytes of a read dword outside the row's
+      // band may count: the hull only has to contain the visible keys, and the attention
+      // kernel intersects it with the Q-tile's band.)
+      const int kl = min(key + 3, k1);  // the dword's last key below Nk
+      unsigned zero = 0u;
+      for (int r0 = q0; r0 <= q1; r0 += 16) {
+        unsigned w[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int r = r0 + u;  // band edges are at most 2^30: r + off +- edge fits in 32 bits
+          const bool need = r <= q1 && key <= r + p.off + p.right && kl >= r + p.off - p.left;
+          w[u] = need ? __builtin_amdgcn_raw_buffer_load_b32(rs, r * p.am_ld + key, 0, 0) : 0xffffffffu;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          // exact zero-byte test: the low seven bits of a byte plus 0x7f carry into bit 7 unless
+          // they are all zero, and bit 7 itself comes in through the OR with the byte
+          const unsigned x = w[u];
+          zero |= ~(((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x | 0x7f7f7f7fu);
+        }
+      }
+      const unsigned z = (((zero >> 7) & 1u) | ((zero >> 14) & 2u) | ((zero >> 21) & 4u) | ((zero >> 28) & 8u)) &
+                         (0xfu >> (3 - (kl - key)));
+      if (z != 0u) {
+        kmin = key + __builtin_ctz(z);
+        kmax = key + 31 - __builtin_clz(z);
+      }
+    }
+  }
+  // work-group reduction: within each wave, then across the four waves through LDS
+#pragma unroll
+  for (int sft = 32; sft >= 1; sft >>= 1) {
+    kmin = min(kmin, __shfl_xor(kmin, sft));
+    kmax = max(kmax, __shfl_xor(kmax, sft));
+  }
+  __shared__ int red[2][4];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int a = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+    const int z = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+    p.hull[((int64_t)plane * p.n_qtiles + t) * p.nch + ch] = make_int2(a, z);
   }
 }
 

@@ -162,9 +162,17 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
  *                   query heads; 0 shares one plane across them. Multiples of 4
  *   mask_row_stride bytes between query rows: >= Nk, a multiple of 4, with
  *                   Nq * mask_row_stride at most 2^31 - 2^16
- *   workspace, n_splits   as fa_fwd_split (NULL and 1 for no split)
- * Other arguments, errors and execution as fa_fwd_split; a NULL mask is
- * FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN.
+ *   workspace       device pointer to fa_fwd_mask_workspace_bytes(...) bytes,
+ *                   16-byte aligned, owned by the caller; never NULL (the
+ *                   split partials, if any, then the mask's key hull)
+ *   n_splits        as fa_fwd_split (1: no split)
+ * Before the attention kernel a pre-pass reads the mask once and records, for
+ * each Q-tile of 128 rows and chunk of 1024 keys, the first and last key some
+ * row of the tile may see; the attention kernel then visits only the key tiles
+ * between them, so the keys a mask hides from a whole Q-tile cost no work.
+ * Other arguments, errors and execution as fa_fwd_split; a NULL mask or
+ * workspace is FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN. Calls that share
+ * a workspace must not run concurrently.
  */
 fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, float* lse,
                       const void* mask, int64_t mask_b_stride, int64_t mask_h_stride,
@@ -172,6 +180,15 @@ fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, floa
                       int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
                       int64_t window_left, int64_t window_right, int n_splits,
                       fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_fwd_mask_workspace_bytes — bytes of workspace fa_fwd_mask needs: the
+ * split partials of fa_fwd_split_workspace_bytes rounded up to 256 bytes, then
+ * B x Hq x ceil(Nq / 128) x ceil(Nk / 1024) pairs of int32 for the mask's key
+ * hull. 0 when the arguments are invalid. Makes no HIP call.
+ */
+size_t fa_fwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d,
+                                   int n_splits);
 
 /*
  * fa_fwd_split_workspace_bytes — bytes of workspace fa_fwd_split needs

@@ -276,7 +276,7 @@ def test_split_validation():
 # ---------------------------------------------------------------- mask input
 
 def call_fwd_mask(**kw):
-    a = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, mask=BAD, sb=0, sh=0, ld=80, ws=0, B=1,
+    a = dict(q=BAD, k=BAD, v=BAD, o=BAD, lse=BAD, mask=BAD, sb=0, sh=0, ld=80, ws=BAD, B=1,
              Hq=2, Hkv=1, Nq=64, Nk=80, d=64, scale=0.125, left=-1, right=-1, ns=1, i=bnd.FA_F16, o_=bnd.FA_F32)
     a.update(kw)
     return bnd.fwd_mask_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["sb"], a["sh"], a["ld"], a["ws"],
@@ -287,6 +287,7 @@ def call_fwd_mask(**kw):
 def test_fwd_mask_validation():
     # the mask's sizes are checked before any alignment, so the misaligned fakes still reach them
     assert call_fwd_mask(mask=0) == bnd.FA_ERR_NULLPTR
+    assert call_fwd_mask(ws=0) == bnd.FA_ERR_NULLPTR             # the mask hull needs the workspace
     assert call_fwd_mask(ld=76) == bnd.FA_ERR_SHAPE            # rows shorter than Nk
     assert call_fwd_mask(sb=-4) == bnd.FA_ERR_SHAPE
     assert call_fwd_mask(ld=(1 << 31) // 64) == bnd.FA_ERR_SHAPE  # Nq * row stride past 2^31 - 2^16
@@ -294,6 +295,19 @@ def test_fwd_mask_validation():
     assert call_fwd_mask(ns=17) == bnd.FA_ERR_SHAPE
     for kw in (dict(ld=82, Nk=81), dict(sh=6), dict()):     # row stride, plane stride, pointers
         assert call_fwd_mask(**kw) == bnd.FA_ERR_ALIGN
+
+
+def test_mask_workspace_bytes():
+    # split partials (if any) rounded up to 256 bytes, then one int32 pair per (b, h, Q-tile, 1024 keys)
+    assert bnd.mask_workspace_bytes(1, 2, 64, 80, 64, 1) == 2 * 1 * 1 * 8
+    assert bnd.mask_workspace_bytes(4, 32, 8192, 8192, 128, 0) == 4 * 32 * 64 * 8 * 8
+    assert bnd.mask_workspace_bytes(2, 3, 129, 1025, 64, 1) == 2 * 3 * 2 * 2 * 8
+    split = 3 * 16 * 100 * 129 * 4
+    assert bnd.mask_workspace_bytes(1, 16, 100, 2048, 128, 3) == (split + 255) // 256 * 256 + 16 * 1 * 2 * 8
+    split = 2 * 1 * 10 * 65 * 4
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 8) == (split + 255) // 256 * 256 + 8
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 80, 2) == 0
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 17) == 0
 
 
 def test_mask_strides_of_tensors():

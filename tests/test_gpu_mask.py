@@ -163,6 +163,78 @@ def test_mask_rescale_path():
     run(B, Hq, Hkv, N, N, d, dt, (None, None), mask, 0, values=values)
 
 
+# ---------------------------------------------------------------- the mask's key hull
+# The pre-pass records, per Q-tile and 1024 keys, the first and last key some row may see, and
+# the attention kernel skips the tiles outside. Document masks (packed sequences: a query sees
+# only its own document) hide most tiles from every row of a Q-tile; key padding hides a tail.
+
+
+@pytest.mark.parametrize("band", [(None, 0), (None, None), (700, 0)])
+@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16)])
+def test_document_mask_skips_tiles(band, d, dt):
+    """Documents of 37..1200 tokens in sequences of 2500 (three hull chunks, a ragged end)."""
+    B, Hq, Hkv, N = 2, 4, 2, 2500
+    lens = I.document_lengths(B, N, 1600 + d, 37, 1200)
+    mask = I.document_mask(lens, N)
+    run(B, Hq, Hkv, N, N, d, dt, band, mask, 1610 + d)
+
+
+def test_document_mask_per_head_and_split():
+    """A plane per (batch, head): each head packs its own documents; with and without split keys,
+    and Nq < Nk (the queries are the last rows of the sequence)."""
+    B, Hq, Hkv, Nq, Nk = 2, 3, 3, 300, 2600
+    planes = [I.document_mask(I.document_lengths(1, Nk, 1620 + i, 50, 900), Nk)[0, 0, Nk - Nq:]
+              for i in range(B * Hq)]
+    mask = np.stack(planes).reshape(B, Hq, Nq, Nk)
+    for splits in (None, 0, 3):
+        run(B, Hq, Hkv, Nq, Nk, 64, I.F16, (None, 0), mask, 1630, splits=splits)
+
+
+def test_mask_hides_whole_q_tiles():
+    """Q-tiles whose rows see nothing (mask rows all ones) write O = 0, LSE = -inf; a padding
+    mask hides every key past each sequence's length."""
+    B, Hq, Hkv, N = 2, 2, 1, 700
+    mask = make_mask("padding", (B, 1, N, N), 1640)
+    mask[0, 0, 128:256] = 1  # the second Q-tile of batch 0 sees no key
+    O, L = run(B, Hq, Hkv, N, N, 128, I.BF16, (None, None), mask, 1641)
+    assert np.isneginf(L[0, :, 128:256]).all() and (O[0, :, 128:256] == 0).all()
+
+
+def test_document_mask_gqa_workload_sampled_rows():
+    """The GQA workload at full size with the document mask the benchmark uses (bench.py
+    --mask document), on rows the oracle computes one by one."""
+    from oracle.attention import head_attention_band_fp64
+
+    w = I.WORKLOADS["gqa_causal_b4_hq32_hkv8_n8192_d128_bf16"]
+    lens = I.document_lengths(w.B, w.N, w.seed + 2000, w.N // 8, w.N // 2)
+    mask = I.document_mask(lens, w.N)
+    qkv = I.workload_qkv(w)
+    print(f"[gpu] fa_fwd_mask {w.name} document mask {[len(r) for r in lens]}", flush=True)
+    O, L = fa.fwd(*(to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v)), scale=w.scale, window=w.band,
+                  mask=torch.from_numpy(mask).to(DEV))
+    torch.cuda.synchronize()
+    O = O.cpu().numpy().astype(np.float64)
+    L = L.cpu().numpy().astype(np.float64)
+    rng = np.random.Generator(np.random.PCG64(1650))
+    starts = np.cumsum([0] + lens[0][:-1])
+    rows = np.unique(np.concatenate([starts, starts + 1, starts - 1, [w.N - 1], rng.integers(0, w.N, 24)]))
+    rows = rows[(rows >= 0) & (rows < w.N)]
+    for b, h in [(0, 0), (0, 5), (3, 31)]:
+        if b != 0:
+            starts = np.cumsum([0] + lens[b][:-1])
+            rows = np.unique(np.concatenate([starts, starts + 1, rng.integers(0, w.N, 24)]))
+            rows = rows[(rows >= 0) & (rows < w.N)]
+        q = I.bits_to_f64(qkv.q[b, h][rows], w.dtype)
+        k = I.bits_to_f64(qkv.k[b, h // (w.Hq // w.Hkv)], w.dtype)
+        v = I.bits_to_f64(qkv.v[b, h // (w.Hq // w.Hkv)], w.dtype)
+        O_ref, L_ref = head_attention_band_fp64(q, k, v, I.scale_f32(w.scale), None, 0, q_pos=rows,
+                                                hidden=mask[b, 0][rows])
+        err_o = np.abs(O[b, h][rows] - O_ref).max()
+        assert err_o <= TOL_O[w.dtype], f"head ({b},{h}) max|dO| {err_o:.3e}"
+        err_l = (np.abs(L[b, h][rows] - L_ref) / np.maximum(1.0, np.abs(L_ref))).max()
+        assert err_l <= TOL_LSE, f"head ({b},{h}) LSE rel err {err_l:.3e}"
+
+
 def test_mask_errors_raise():
     qb, kb, vb = draw(1, 2, 2, 64, 30, 64, I.F16, 1595)
     q, k, v = (to_dev(x, I.F16) for x in (qb, kb, vb))
