@@ -113,8 +113,11 @@ def time_gpu(w, steps: int, warmup: int, splits: int = 0, mask=None):
     del qkv
     out = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
-    ws_bytes = (binding.split_workspace_bytes if mask is None else binding.mask_workspace_bytes)(
-        w.B, w.Hq, w.N, w.nk, w.d, splits)
+    if mask is None:
+        ws_bytes = binding.split_workspace_bytes(w.B, w.Hq, w.N, w.nk, w.d, splits)
+    else:  # a [B or 1, Hq or 1, N, Nk] byte mask, contiguous
+        ws_bytes = binding.mask_workspace_bytes(w.B, w.Hq, w.N, w.nk, w.d, splits,
+                                                int(mask.shape[0] > 1), int(mask.shape[1] > 1))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     tm = None if mask is None else torch.from_numpy(mask).to(dev)

@@ -38,7 +38,7 @@ SIGNATURES = {
     "fa_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                      + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
-    "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
+    "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 2),
     "fa_bwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 9 + [ctypes.c_float]
                     + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
@@ -151,9 +151,12 @@ def split_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: i
     return int(load_library().fa_fwd_split_workspace_bytes(B, Hq, Nq, Nk, d, n_splits))
 
 
-def mask_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: int) -> int:
-    """Bytes of workspace fa_fwd_mask needs (0 for sizes it rejects)."""
-    return int(load_library().fa_fwd_mask_workspace_bytes(B, Hq, Nq, Nk, d, n_splits))
+def mask_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: int, mask_b_stride: int,
+                         mask_h_stride: int) -> int:
+    """Bytes of workspace fa_fwd_mask needs for a mask with these batch and head strides
+    (0: shared along that axis); 0 for sizes it rejects."""
+    return int(load_library().fa_fwd_mask_workspace_bytes(B, Hq, Nq, Nk, d, n_splits, mask_b_stride,
+                                                           mask_h_stride))
 
 
 def _edges(causal: bool, window) -> Tuple[int, int]:
@@ -234,7 +237,7 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
             raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
         sb, sh, ld = mask_strides(mask, B, Hq, N, Nk)
         ns = 1 if splits is None else int(splits)
-        need = mask_workspace_bytes(B, Hq, N, Nk, d, ns)
+        need = mask_workspace_bytes(B, Hq, N, Nk, d, ns, sb, sh)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         if workspace.device != q.device or workspace.numel() * workspace.element_size() < need:

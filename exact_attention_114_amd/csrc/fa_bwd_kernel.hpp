@@ -220,12 +220,7 @@ __device__ inline int lane_bytes4() {
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 2, %0" : "=v"(v));
   return v;
 }
-// The lane id, formed the same opaque way (held in no register across a loop).
-__device__ inline int lane_id_here() {
-  int v;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
-  return v;
-}
+// (lane_id_here, the lane id formed the same opaque way, is in fa_fwd_kernel.hpp.)
 
 // ---- 2. dK/dV ---------------------------------------------------------------------------------
 template <bool BF16, int D, bool BAND, int NW, bool AM>

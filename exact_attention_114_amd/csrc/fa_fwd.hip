@@ -131,11 +131,28 @@ struct MaskArg {
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
 };
 
-// Workspace of a masked call: the split partials (if any), then the mask hull at the next
-// 256-byte boundary, sized for a mask with a plane per (batch, head).
-int64_t split_bytes(int ns, int64_t rows, int64_t d) { return ns > 1 ? ns * rows * (d + 1) * 4 : 0; }
-int64_t hull_offset(int ns, int64_t rows, int64_t d) { return (split_bytes(ns, rows, d) + 255) / 256 * 256; }
+// Workspace of a masked call, each part at a 256-byte boundary: the split partials (if any),
+// the mask hull (an int2 per plane, Q-tile and chunk of kHullKeys keys), then the mask as bits
+// (ceil(Nk / 32) words per row of each plane). A plane per batch element and/or head when the
+// mask's stride along that axis is nonzero.
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 int64_t hull_chunks(int64_t Nk) { return (Nk + fa::kHullKeys - 1) / fa::kHullKeys; }
+struct MaskLayout {
+  int64_t planes_b, planes_h, nch, nw, hull_off, bits_off, bytes;
+};
+MaskLayout mask_layout(int ns, int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int64_t nq,
+                       int64_t b_stride, int64_t h_stride) {
+  MaskLayout m;
+  m.planes_b = b_stride ? B : 1;
+  m.planes_h = h_stride ? Hq : 1;
+  m.nch = hull_chunks(Nk);
+  m.nw = (Nk + 31) / 32;
+  const int64_t planes = m.planes_b * m.planes_h;
+  m.hull_off = align256(ns > 1 ? ns * B * Hq * Nq * (d + 1) * 4 : 0);
+  m.bits_off = align256(m.hull_off + planes * nq * m.nch * 8);
+  m.bytes = m.bits_off + planes * Nq * m.nw * 4;
+  return m;
+}
 
 // Every forward entry point: validation, the split plan (n_splits = 1: never split; workspace
 // is then unused unless there is a mask), the mask hull, the attention kernel and, with split
@@ -171,9 +188,8 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
     return FA_ERR_ALIGN;
   const int64_t rows = B * Hq * Nq;
   if (grid * ns >= ((int64_t)1 << 31) || rows * d * ns >= ((int64_t)1 << 40)) return FA_ERR_SHAPE;
-  const int64_t planes_b = am && mask.b_stride ? B : 1, planes_h = am && mask.h_stride ? Hq : 1;
-  const int64_t nch = hull_chunks(Nk);
-  if (am && planes_b * planes_h * nq * nch >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;  // hull grid
+  const MaskLayout ml = mask_layout(ns, B, Hq, Nq, Nk, d, nq, am ? mask.b_stride : 0, am ? mask.h_stride : 0);
+  if (am && ml.planes_b * ml.planes_h * nq * ml.nch >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;  // prep grid
 
   fa::Params p;
   p.q = q;
@@ -195,15 +211,17 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   p.kchunk = kc;
   p.total_wg = (int)(grid * ns);
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
-  p.am = static_cast<const unsigned char*>(mask.data);
-  p.am_sb = mask.b_stride;
-  p.am_sh = mask.h_stride;
-  p.am_ld = (int)mask.row_stride;
-  int2* hull = am ? reinterpret_cast<int2*>(reinterpret_cast<char*>(workspace) + hull_offset(ns, rows, d)) : nullptr;
+  char* const wsb = reinterpret_cast<char*>(workspace);
+  int2* const hull = am ? reinterpret_cast<int2*>(wsb + ml.hull_off) : nullptr;
+  unsigned* const bits = am ? reinterpret_cast<unsigned*>(wsb + ml.bits_off) : nullptr;
+  p.am_bits = bits;
+  p.am_nw = (int)ml.nw;
+  p.bits_sh = ml.planes_h > 1 ? Nq * ml.nw : 0;
+  p.bits_sb = ml.planes_b > 1 ? ml.planes_h * Nq * ml.nw : 0;
   p.am_hull = hull;
-  p.hull_nch = (int)nch;
-  p.hull_sh = planes_h > 1 ? nq * nch : 0;
-  p.hull_sb = planes_b > 1 ? planes_h * nq * nch : 0;
+  p.hull_nch = (int)ml.nch;
+  p.hull_sh = ml.planes_h > 1 ? nq * ml.nch : 0;
+  p.hull_sb = ml.planes_b > 1 ? ml.planes_h * nq * ml.nch : 0;
 
   // With both edges unlimited every key is visible and no band is applied.
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
@@ -212,22 +230,24 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   const int kb = key_blocks(d, grid * ns);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (am) {
-    fa::HullParams hp;
-    hp.am = p.am;
-    hp.am_sb = p.am_sb;
-    hp.am_sh = p.am_sh;
-    hp.am_ld = p.am_ld;
-    hp.hull = hull;
-    hp.planes_b = (int)planes_b;
-    hp.planes_h = (int)planes_h;
-    hp.Nq = p.Nq;
-    hp.Nk = p.Nk;
-    hp.off = p.off;
-    hp.left = p.left;
-    hp.right = p.right;
-    hp.n_qtiles = p.n_qtiles;
-    hp.nch = (int)nch;
-    hipLaunchKernelGGL(fa::fa_mask_hull_kernel<kBlockM>, dim3((unsigned)(planes_b * planes_h * nq * nch)), dim3(256), 0, s, hp);
+    fa::PrepParams pp;
+    pp.am = static_cast<const unsigned char*>(mask.data);
+    pp.am_sb = mask.b_stride;
+    pp.am_sh = mask.h_stride;
+    pp.am_ld = (int)mask.row_stride;
+    pp.hull = hull;
+    pp.bits = bits;
+    pp.planes_h = (int)ml.planes_h;
+    pp.Nq = p.Nq;
+    pp.Nk = p.Nk;
+    pp.off = p.off;
+    pp.left = p.left;
+    pp.right = p.right;
+    pp.n_qtiles = p.n_qtiles;
+    pp.nch = (int)ml.nch;
+    pp.nw = (int)ml.nw;
+    hipLaunchKernelGGL(fa::fa_mask_prep_kernel<kBlockM>, dim3((unsigned)(ml.planes_b * ml.planes_h * nq * ml.nch)),
+                       dim3(256), 0, s, pp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       fa::last_hip_error = (int)e;
@@ -291,13 +311,14 @@ size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t N
   return (size_t)(ns * B * Hq * Nq * (d + 1) * (int64_t)sizeof(float));
 }
 
-size_t fa_fwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int n_splits) {
+size_t fa_fwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int n_splits,
+                                   int64_t mask_b_stride, int64_t mask_h_stride) {
   int64_t nq = 0, grid = 0;
-  if (n_splits < 0 || n_splits > kMaxSplits) return 0;
+  if (n_splits < 0 || n_splits > kMaxSplits || mask_b_stride < 0 || mask_h_stride < 0) return 0;
   if (check_problem(B, Hq, 1, Nq, Nk, d, FA_F16, &nq, &grid) != FA_OK) return 0;
   int ns = 1, kc = 0;
   split_plan(grid, Nk, n_splits, &ns, &kc);
-  return (size_t)(hull_offset(ns, B * Hq * Nq, d) + B * Hq * nq * hull_chunks(Nk) * (int64_t)sizeof(int2));
+  return (size_t)mask_layout(ns, B, Hq, Nq, Nk, d, nq, mask_b_stride, mask_h_stride).bytes;
 }
 
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,

@@ -48,10 +48,11 @@
 //      O = 0 and LSE = -inf.
 //   6. Mask input. The operator's optional boolean attn_mask (intelliparadigm page, section 2.2;
 //      the Mask step of FlashAttention-1's Algorithm 2 that the cnblogs page points to) hides a
-//      key from a query where its byte is nonzero, on top of the band. A lane reads the 16 bytes
-//      of its query row that match its 16 scores of a 32-key block as 4 dwords, one step ahead,
-//      and a wave skips the per-score selects on tiles its mask leaves whole. A pre-pass
-//      (fa_mask_hull_kernel) records, per Q-tile and chunk of keys, the first and last key any
+//      key from a query where its byte is nonzero, on top of the band. A lane reads the mask
+//      word of its query row for each 32-key block one step ahead, and a wave skips the
+//      per-score selects on tiles its mask leaves whole. A pre-pass
+//      (fa_mask_prep_kernel) packs the byte mask into one bit per key, so a lane reads one word
+//      per 32-key block, and records, per Q-tile and chunk of keys, the first and last key any
 //      row of the tile may see; the attention kernel visits only the tiles between them, so
 //      keys a mask hides from a whole Q-tile (other documents, padding) cost nothing.
 //   7. Split keys. When batch x heads x Q-tiles leaves the GPU under-filled, the keys of each
@@ -122,14 +123,14 @@ struct Params {
   int kchunk;    // keys per chunk, a multiple of 64 (every key-tile size)
   int total_wg;  // B * Hq * n_qtiles * nsplit
   float c;       // scale * log2(e)
-  // optional byte mask (kernels built with AM): byte [i][j] of the (b, hq) plane at
-  // am + b*am_sb + hq*am_sh, rows am_ld bytes apart; nonzero hides key j from query i
-  const unsigned char* am;
-  long long am_sb, am_sh;
-  int am_ld;
-  // the mask's key hull (fa_mask_hull_kernel): int2 {first, last} visible key per (b, hq) mask
-  // plane, Q-tile and chunk of kHullKeys keys at am_hull + b*hull_sb + hq*hull_sh +
-  // t*hull_nch + chunk (the strides are 0 along an axis the mask shares)
+  // optional mask (kernels built with AM), as fa_mask_prep_kernel leaves it: one bit per
+  // (query, key), set where the key is hidden, in rows of am_nw 32-bit words; the (b, hq)
+  // plane starts at am_bits + b*bits_sb + hq*bits_sh (strides 0 along an axis the mask shares)
+  const unsigned* am_bits;
+  long long bits_sb, bits_sh;
+  int am_nw;
+  // the mask's key hull: int2 {first, last} visible key per plane, Q-tile and chunk of
+  // kHullKeys keys at am_hull + b*hull_sb + hq*hull_sh + t*hull_nch + chunk
   const int2* am_hull;
   long long hull_sb, hull_sh;
   int hull_nch;
@@ -137,6 +138,14 @@ struct Params {
 
 // Keys per chunk of the mask hull.
 constexpr int kHullKeys = 1024;
+
+// The lane id, formed where it is used by an opaque instruction sequence: it cannot be hoisted
+// out of a loop, so it holds no register across the loop.
+__device__ inline int lane_id_here() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
 
 // ---- element-type traits ------------------------------------------------------------------
 template <bool BF16>
@@ -239,13 +248,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Waves that share a SIMD for a tile shape: registers bound it (a d = 128 step with two key
 // blocks holds 189 VGPRs, with one 168; d = 64 about 150) and so does LDS (4 tiles of
 // 32*KB rows at the LDS pitch per work-group).
-constexpr int waves_per_simd(int d, int kb, bool am) { return d >= 96 && kb == 1 && !am ? 3 : 2; }
+constexpr int waves_per_simd(int d, int kb) { return d >= 96 && kb == 1 ? 3 : 2; }
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
 // pipeline step takes KB blocks of 32 keys.
 template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB, bool AM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, AM)))) void fa_fwd_kernel(const Params p) {
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
   static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
   constexpr int BM = 32 * NW;
@@ -454,38 +463,38 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, AM)))) void fa_fwd_kern
   // lane l: query l%32, d = 16ks + 8h + 0..7
   load_k(j_lo, K0);
   load_k(j_lo + 1, K1);
-  // Mask words: am_w[kb][g] holds the bytes of keys kbase + 32kb + 8g + 4h + (0..3) of this
-  // lane's query row, i.e. scores 4g .. 4g+3 of block kb. One descriptor spans the head's
-  // plane (a read past it gives zeros); the lane's row and half go in a loop-invariant offset.
-  unsigned am_w[AM ? KB : 1][4];
+  // Mask bits: am_w[kb] is the word of keys kbase + 32kb .. + 31 of this lane's query row; bit
+  // 8g + 4h + i (i < 4) covers the lane's score 4g + i of block kb. One descriptor spans the
+  // plane (a read past it gives zeros); the whole offset goes into the vector operand (the
+  // scalar one stays 0), so the range check covers it and a prefetch past the plane reads zeros.
+  // The lane's row offset is formed at each load from an opaque lane id (the masked d = 128
+  // kernel has no register to keep it in); rows past Nq read the last row.
+  unsigned am_w[AM ? KB : 1];
   __amdgpu_buffer_rsrc_t am_rs;
-  int am_v0 = 0;
-  // The whole offset goes into the vector operand (the scalar one stays 0): the range check
-  // covers the vector offset, so a prefetch past the plane reads zeros rather than memory.
-  auto load_am = [&](int jt, unsigned(&w)[AM ? KB : 1][4]) {
-    const int vo = am_v0 + jt * BN;
+  auto load_am = [&](int jt, unsigned(&w)[AM ? KB : 1]) {
+    const int row = min(q0w + (lane_id_here() & 31), Nq - 1);
+    const int vo = (row * p.am_nw + jt * KB) * 4;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) w[kb][g] = __builtin_amdgcn_raw_buffer_load_b32(am_rs, vo + 32 * kb + 8 * g, 0, 0);
+    for (int kb = 0; kb < KB; ++kb) w[kb] = __builtin_amdgcn_raw_buffer_load_b32(am_rs, vo + 4 * kb, 0, 0);
   };
-  // hide the scores whose mask byte is nonzero; a wave whose words are all zero skips it
-  auto apply_am = [&](f32x16(&st)[KB], const unsigned(&w)[AM ? KB : 1][4]) {
+  // hide the scores whose bit is set; a wave whose words are all zero skips it
+  auto apply_am = [&](f32x16(&st)[KB], const unsigned(&w)[AM ? KB : 1]) {
     unsigned any = 0;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) any |= w[kb][0] | w[kb][1] | w[kb][2] | w[kb][3];
+    for (int kb = 0; kb < KB; ++kb) any |= w[kb];
     if (__builtin_amdgcn_ballot_w64(any != 0u) != 0) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) {
+        const unsigned x = w[kb] >> (4 * h);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          st[kb][i] = ((w[kb][i >> 2] >> (8 * (i & 3))) & 0xffu) != 0u ? -__builtin_inff() : st[kb][i];
+          st[kb][i] = ((x >> (8 * (i >> 2) + (i & 3))) & 1u) != 0u ? -__builtin_inff() : st[kb][i];
+      }
     }
   };
   if constexpr (AM) {
-    const unsigned char* plane = p.am + (long long)b * p.am_sb + (long long)hq * p.am_sh;
-    am_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.am_ld, kBufferWord3);
-    am_v0 = qr * p.am_ld + 4 * h;
+    const unsigned* plane = p.am_bits + b * p.bits_sb + hq * p.bits_sh;
+    am_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.am_nw * 4, kBufferWord3);
     load_am(j_lo, am_w);
   }
   u32x4 qreg[NKS];
@@ -677,7 +686,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, AM)))) void fa_fwd_kern
         }
         if (need_mask) mask(st);
         if constexpr (AM) {
-          unsigned wj[AM ? KB : 1][4];
+          unsigned wj[AM ? KB : 1];
           load_am(j, wj);
           apply_am(st, wj);
         }
@@ -755,23 +764,31 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, AM)))) void fa_fwd_kern
   }
 }
 
-// Mask hull: for one mask plane, one Q-tile of BM rows and one chunk of kHullKeys keys, the
-// first and last key that some row of the tile may see (mask byte zero, inside the tile's band,
-// below Nk), or {INT_MAX, -1} when there is none. 256 threads: thread x reads the dword of
-// keys k0 + 4x .. k0 + 4x + 3 of every row of the tile whose band reaches them (a wave reads 256
-// consecutive bytes of a row; every offset lies inside the plane); bytes past Nk never count.
-struct HullParams {
-  const unsigned char* am;
+// Mask preparation, run once per call before the attention kernel. For one mask plane, one
+// Q-tile of BM rows and one chunk of kHullKeys keys it
+//   - packs the byte mask into bits: word k/32 of a row, bit k%32, set where key k is hidden
+//     (a nonzero byte, a key past Nk, or a 32-key word outside the row's band, which the band
+//     hides anyway), for every row of the tile;
+//   - records the chunk's hull: the first and last key some row of the tile may see, or
+//     {INT_MAX, -1} when there is none (a word is counted whole when the band reaches it: the
+//     hull only has to contain the visible keys, and the attention kernel intersects it with
+//     the Q-tile's band).
+// 256 threads: thread x packs word x%32 of the chunk for rows x/32, x/32 + 8, ... reading its
+// 32 bytes as 8 dwords (32 threads cover 1 KiB of a row). Every read lies inside the plane.
+struct PrepParams {
+  const unsigned char* am;   // byte [i][j] of plane (pb, ph) at am + pb*am_sb + ph*am_sh + i*am_ld + j
   long long am_sb, am_sh;
   int am_ld;
-  int2* hull;                // [planes_b][planes_h][n_qtiles][nch]
-  int planes_b, planes_h;    // B or 1, Hq or 1
+  int2* hull;                // [planes][n_qtiles][nch]
+  unsigned* bits;            // [planes][Nq][nw]
+  int planes_h;              // Hq or 1 (planes are numbered pb * planes_h + ph)
   int Nq, Nk, off, left, right;
-  int n_qtiles, nch;
+  int n_qtiles, nch, nw;
 };
 
 template <int BM>
-__global__ __launch_bounds__(256) void fa_mask_hull_kernel(const HullParams p) {
+__global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
+  static_assert(BM % 8 == 0, "eight rows per pass");
   int wg = blockIdx.x;
   const int ch = wg % p.nch;
   wg /= p.nch;
@@ -779,44 +796,43 @@ __global__ __launch_bounds__(256) void fa_mask_hull_kernel(const HullParams p) {
   const int plane = wg / p.n_qtiles;
   const int pb = plane / p.planes_h, ph = plane - pb * p.planes_h;
   const int q0 = t * BM, q1 = min(q0 + BM, p.Nq) - 1;
-  const int k0 = ch * kHullKeys, k1 = min(k0 + kHullKeys, p.Nk) - 1;
-  int kmin = 0x7fffffff, kmax = -1;
-  // the tile's band reaches keys q0 + off - left .. q1 + off + right (64-bit: edges may be 2^30)
-  if ((int64_t)k0 <= (int64_t)q1 + p.off + p.right && (int64_t)k1 >= (int64_t)q0 + p.off - p.left) {
-    const unsigned char* base = p.am + (long long)pb * p.am_sb + (long long)ph * p.am_sh;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, p.Nq * p.am_ld,
-                                                                        kBufferWord3);
-    const int key = k0 + 4 * (int)threadIdx.x;
-    if (key <= k1) {
-      // bit 7 of byte b of `zero` is set when some row's byte b is zero; rows past the tile or
-      // whose band misses this dword are not read. (Bytes of a read dword outside the row's
-      // band may count: the hull only has to contain the visible keys, and the attention
-      // kernel intersects it with the Q-tile's band.)
-      const int kl = min(key + 3, k1);  // the dword's last key below Nk
-      unsigned zero = 0u;
-      for (int r0 = q0; r0 <= q1; r0 += 16) {
-        unsigned w[16];
+  const int wi = threadIdx.x & 31;                 // word within the chunk
+  const int kw = ch * kHullKeys + 32 * wi;         // its first key
+  const bool wvalid = kw < p.Nk;                   // the word exists in a row
+  const int nk = wvalid ? min(32, p.Nk - kw) : 0;  // its keys below Nk
+  const unsigned tail = nk >= 32 ? 0u : ~0u << nk;  // bits of keys past Nk: hidden
+  const unsigned char* base = p.am + (long long)pb * p.am_sb + (long long)ph * p.am_sh;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, p.Nq * p.am_ld,
+                                                                      kBufferWord3);
+  unsigned* const brow = p.bits + (int64_t)plane * p.Nq * p.nw + ch * (kHullKeys / 32) + wi;
+  unsigned vis = 0u;  // keys of this word some row may see
+  for (int r = q0 + (int)(threadIdx.x >> 5); r <= q1; r += 8) {
+    // band edges are at most 2^30: r + off +- edge fits in 32 bits
+    const bool need = wvalid && kw <= r + p.off + p.right && kw + nk - 1 >= r + p.off - p.left;
+    unsigned hid = ~0u;
+    if (need) {
+      unsigned w[8];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int r = r0 + u;  // band edges are at most 2^30: r + off +- edge fits in 32 bits
-          const bool need = r <= q1 && key <= r + p.off + p.right && kl >= r + p.off - p.left;
-          w[u] = need ? __builtin_amdgcn_raw_buffer_load_b32(rs, r * p.am_ld + key, 0, 0) : 0xffffffffu;
-        }
+      for (int u = 0; u < 8; ++u)
+        w[u] = 4 * u < nk ? __builtin_amdgcn_raw_buffer_load_b32(rs, r * p.am_ld + kw + 4 * u, 0, 0) : ~0u;
+      hid = 0u;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          // exact zero-byte test: the low seven bits of a byte plus 0x7f carry into bit 7 unless
-          // they are all zero, and bit 7 itself comes in through the OR with the byte
-          const unsigned x = w[u];
-          zero |= ~(((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x | 0x7f7f7f7fu);
-        }
+      for (int u = 0; u < 8; ++u) {
+        // exact zero-byte test: the low seven bits of a byte plus 0x7f carry into bit 7 unless
+        // they are all zero, and bit 7 itself comes in through the OR with the byte
+        const unsigned z = ~(((w[u] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[u] | 0x7f7f7f7fu);
+        const unsigned nib = ((z >> 7) & 1u) | ((z >> 14) & 2u) | ((z >> 21) & 4u) | ((z >> 28) & 8u);
+        hid |= (~nib & 0xfu) << (4 * u);
       }
-      const unsigned z = (((zero >> 7) & 1u) | ((zero >> 14) & 2u) | ((zero >> 21) & 4u) | ((zero >> 28) & 8u)) &
-                         (0xfu >> (3 - (kl - key)));
-      if (z != 0u) {
-        kmin = key + __builtin_ctz(z);
-        kmax = key + 31 - __builtin_clz(z);
-      }
+      hid |= tail;
     }
+    vis |= ~hid;
+    if (wvalid) brow[(int64_t)r * p.nw] = hid;
+  }
+  int kmin = 0x7fffffff, kmax = -1;
+  if (vis != 0u) {
+    kmin = kw + __builtin_ctz(vis);
+    kmax = kw + 31 - __builtin_clz(vis);
   }
   // work-group reduction: within each wave, then across the four waves through LDS
 #pragma unroll

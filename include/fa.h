@@ -162,14 +162,17 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
  *                   query heads; 0 shares one plane across them. Multiples of 4
  *   mask_row_stride bytes between query rows: >= Nk, a multiple of 4, with
  *                   Nq * mask_row_stride at most 2^31 - 2^16
- *   workspace       device pointer to fa_fwd_mask_workspace_bytes(...) bytes,
+ *   workspace       device pointer to fa_fwd_mask_workspace_bytes(..., mask_b_stride,
+ *                   mask_h_stride) bytes,
  *                   16-byte aligned, owned by the caller; never NULL (the
  *                   split partials, if any, then the mask's key hull)
  *   n_splits        as fa_fwd_split (1: no split)
- * Before the attention kernel a pre-pass reads the mask once and records, for
- * each Q-tile of 128 rows and chunk of 1024 keys, the first and last key some
- * row of the tile may see; the attention kernel then visits only the key tiles
- * between them, so the keys a mask hides from a whole Q-tile cost no work.
+ * Before the attention kernel a pre-pass reads the mask once, packs it into one
+ * bit per key in the workspace (the attention kernel reads those bits), and
+ * records, for each Q-tile of 128 rows and chunk of 1024 keys, the first and
+ * last key some row of the tile may see; the attention kernel then visits only
+ * the key tiles between them, so the keys a mask hides from a whole Q-tile
+ * cost no work.
  * Other arguments, errors and execution as fa_fwd_split; a NULL mask or
  * workspace is FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN. Calls that share
  * a workspace must not run concurrently.
@@ -182,13 +185,17 @@ fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, floa
                       fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
 
 /*
- * fa_fwd_mask_workspace_bytes — bytes of workspace fa_fwd_mask needs: the
- * split partials of fa_fwd_split_workspace_bytes rounded up to 256 bytes, then
- * B x Hq x ceil(Nq / 128) x ceil(Nk / 1024) pairs of int32 for the mask's key
- * hull. 0 when the arguments are invalid. Makes no HIP call.
+ * fa_fwd_mask_workspace_bytes — bytes of workspace fa_fwd_mask needs for a mask
+ * with these batch and head strides (0: shared along that axis), each part
+ * starting at a 256-byte boundary: the split partials of
+ * fa_fwd_split_workspace_bytes, then P x ceil(Nq / 128) x ceil(Nk / 1024)
+ * pairs of int32 (the mask's key hull), then P x Nq x ceil(Nk / 32) words of
+ * 32 bits (the mask packed to one bit per key), where P, the number of mask
+ * planes, is (B if mask_b_stride else 1) x (Hq if mask_h_stride else 1).
+ * 0 when the arguments are invalid. Makes no HIP call.
  */
 size_t fa_fwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d,
-                                   int n_splits);
+                                   int n_splits, int64_t mask_b_stride, int64_t mask_h_stride);
 
 /*
  * fa_fwd_split_workspace_bytes — bytes of workspace fa_fwd_split needs

@@ -298,16 +298,20 @@ def test_fwd_mask_validation():
 
 
 def test_mask_workspace_bytes():
-    # split partials (if any) rounded up to 256 bytes, then one int32 pair per (b, h, Q-tile, 1024 keys)
-    assert bnd.mask_workspace_bytes(1, 2, 64, 80, 64, 1) == 2 * 1 * 1 * 8
-    assert bnd.mask_workspace_bytes(4, 32, 8192, 8192, 128, 0) == 4 * 32 * 64 * 8 * 8
-    assert bnd.mask_workspace_bytes(2, 3, 129, 1025, 64, 1) == 2 * 3 * 2 * 2 * 8
+    # parts at 256-byte boundaries: split partials (if any), an int32 pair per (plane, Q-tile,
+    # 1024 keys), then ceil(Nk / 32) words per row of each plane; a plane per batch element or
+    # head only where the mask's stride along that axis is nonzero
+    assert bnd.mask_workspace_bytes(1, 2, 64, 80, 64, 1, 0, 0) == 256 + 64 * 3 * 4
+    assert bnd.mask_workspace_bytes(4, 32, 8192, 8192, 128, 0, 1, 0) == 4 * 64 * 8 * 8 + 4 * 8192 * 256 * 4
+    assert bnd.mask_workspace_bytes(2, 3, 129, 1025, 64, 1, 1, 1) == 256 + 6 * 129 * 33 * 4
     split = 3 * 16 * 100 * 129 * 4
-    assert bnd.mask_workspace_bytes(1, 16, 100, 2048, 128, 3) == (split + 255) // 256 * 256 + 16 * 1 * 2 * 8
+    assert split % 256 == 0
+    assert bnd.mask_workspace_bytes(1, 16, 100, 2048, 128, 3, 0, 400) == split + 256 + 16 * 100 * 64 * 4
     split = 2 * 1 * 10 * 65 * 4
-    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 8) == (split + 255) // 256 * 256 + 8
-    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 80, 2) == 0
-    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 17) == 0
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 8, 0, 0) == (split + 255) // 256 * 256 + 256 + 10 * 8 * 4
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 80, 2, 0, 0) == 0
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 17, 0, 0) == 0
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 1, -4, 0) == 0
 
 
 def test_mask_strides_of_tensors():
