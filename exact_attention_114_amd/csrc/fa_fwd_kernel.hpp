@@ -463,8 +463,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   // lane l: query l%32, d = 16ks + 8h + 0..7
   load_k(j_lo, K0);
   load_k(j_lo + 1, K1);
-  // Mask bits: am_w[kb] is the word of keys kbase + 32kb .. + 31 of this lane's query row; bit
-  // 8g + 4h + i (i < 4) covers the lane's score 4g + i of block kb. One descriptor spans the
+  // Mask bits: am_w[kb] is the word of keys kbase + 32kb .. + 31 of this lane's query row; the
+  // lane's score 4g + i of block kb (key 32kb + 8g + 4h + i) is bit 8i + 2g + h. One descriptor spans the
   // plane (a read past it gives zeros); the whole offset goes into the vector operand (the
   // scalar one stays 0), so the range check covers it and a prefetch past the plane reads zeros.
   // The lane's row offset is formed at each load from an opaque lane id (the masked d = 128
@@ -485,10 +485,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     if (__builtin_amdgcn_ballot_w64(any != 0u) != 0) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const unsigned x = w[kb] >> (4 * h);
+        const unsigned x = w[kb] >> h;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          st[kb][i] = ((x >> (8 * (i >> 2) + (i & 3))) & 1u) != 0u ? -__builtin_inff() : st[kb][i];
+          st[kb][i] = ((x >> (8 * (i & 3) + 2 * (i >> 2))) & 1u) != 0u ? -__builtin_inff() : st[kb][i];
       }
     }
   };
@@ -766,15 +766,17 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
 
 // Mask preparation, run once per call before the attention kernel. For one mask plane, one
 // Q-tile of BM rows and one chunk of kHullKeys keys it
-//   - packs the byte mask into bits: word k/32 of a row, bit k%32, set where key k is hidden
-//     (a nonzero byte, a key past Nk, or a 32-key word outside the row's band, which the band
-//     hides anyway), for every row of the tile;
+//   - packs the byte mask into bits, 32 keys to a word: key 32w + 4s + b of a row (s < 8,
+//     b < 4) is bit 8b + s of the row's word w, set where the key is hidden (a nonzero byte, a
+//     key past Nk, or a group of four keys outside the row's band, which the band hides
+//     anyway), for every row of the tile;
 //   - records the chunk's hull: the first and last key some row of the tile may see, or
-//     {INT_MAX, -1} when there is none (a word is counted whole when the band reaches it: the
-//     hull only has to contain the visible keys, and the attention kernel intersects it with
-//     the Q-tile's band).
-// 256 threads: thread x packs word x%32 of the chunk for rows x/32, x/32 + 8, ... reading its
-// 32 bytes as 8 dwords (32 threads cover 1 KiB of a row). Every read lies inside the plane.
+//     {INT_MAX, -1} when there is none (a group of four keys counts whole when the band reaches
+//     it: the hull only has to contain the visible keys, and the attention kernel intersects
+//     it with the Q-tile's band).
+// 256 threads: thread x reads dword x of the chunk (keys k0 + 4x .. + 3) of every row of the
+// tile whose band reaches it (a wave reads 256 consecutive bytes of a row; every read lies
+// inside the plane), and the eight threads of one word gather its bits by DPP moves.
 struct PrepParams {
   const unsigned char* am;   // byte [i][j] of plane (pb, ph) at am + pb*am_sb + ph*am_sh + i*am_ld + j
   long long am_sb, am_sh;
@@ -788,7 +790,6 @@ struct PrepParams {
 
 template <int BM>
 __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
-  static_assert(BM % 8 == 0, "eight rows per pass");
   int wg = blockIdx.x;
   const int ch = wg % p.nch;
   wg /= p.nch;
@@ -796,43 +797,56 @@ __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
   const int plane = wg / p.n_qtiles;
   const int pb = plane / p.planes_h, ph = plane - pb * p.planes_h;
   const int q0 = t * BM, q1 = min(q0 + BM, p.Nq) - 1;
-  const int wi = threadIdx.x & 31;                 // word within the chunk
-  const int kw = ch * kHullKeys + 32 * wi;         // its first key
-  const bool wvalid = kw < p.Nk;                   // the word exists in a row
-  const int nk = wvalid ? min(32, p.Nk - kw) : 0;  // its keys below Nk
-  const unsigned tail = nk >= 32 ? 0u : ~0u << nk;  // bits of keys past Nk: hidden
+  const int x = (int)threadIdx.x;
+  const int sl = x & 7;                                    // this thread's slot in its word
+  const int key = ch * kHullKeys + 4 * x;                  // its first key
+  const int nk = max(0, min(4, p.Nk - key));               // its keys below Nk
+  const unsigned mine = 0x01010101u << sl;                 // its bits in the word: 8b + sl
+  const unsigned tail = nk >= 4 ? 0u : (0xffffffffu << (8 * nk)) & mine;  // keys past Nk: hidden
+  const int wi = ch * (kHullKeys / 32) + (x >> 3);         // the word it contributes to
+  const bool store = sl == 0 && wi < p.nw;                 // one thread per existing word stores
   const unsigned char* base = p.am + (long long)pb * p.am_sb + (long long)ph * p.am_sh;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, p.Nq * p.am_ld,
                                                                       kBufferWord3);
-  unsigned* const brow = p.bits + (int64_t)plane * p.Nq * p.nw + ch * (kHullKeys / 32) + wi;
-  unsigned vis = 0u;  // keys of this word some row may see
-  for (int r = q0 + (int)(threadIdx.x >> 5); r <= q1; r += 8) {
-    // band edges are at most 2^30: r + off +- edge fits in 32 bits
-    const bool need = wvalid && kw <= r + p.off + p.right && kw + nk - 1 >= r + p.off - p.left;
-    unsigned hid = ~0u;
-    if (need) {
-      unsigned w[8];
+  unsigned* const bcol = p.bits + (int64_t)plane * p.Nq * p.nw + wi;
+  unsigned vis = 0u;  // bits (8b + sl) of this thread's keys that some row may see
+  for (int r0 = q0; r0 <= q1; r0 += 16) {
+    unsigned w[16];
+    bool any = false;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        w[u] = 4 * u < nk ? __builtin_amdgcn_raw_buffer_load_b32(rs, r * p.am_ld + kw + 4 * u, 0, 0) : ~0u;
-      hid = 0u;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        // exact zero-byte test: the low seven bits of a byte plus 0x7f carry into bit 7 unless
-        // they are all zero, and bit 7 itself comes in through the OR with the byte
-        const unsigned z = ~(((w[u] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[u] | 0x7f7f7f7fu);
-        const unsigned nib = ((z >> 7) & 1u) | ((z >> 14) & 2u) | ((z >> 21) & 4u) | ((z >> 28) & 8u);
-        hid |= (~nib & 0xfu) << (4 * u);
-      }
-      hid |= tail;
+    for (int u = 0; u < 16; ++u) {
+      const int r = r0 + u;  // band edges are at most 2^30: r + off +- edge fits in 32 bits
+      const bool need = nk > 0 && r <= q1 && key <= r + p.off + p.right && key + nk - 1 >= r + p.off - p.left;
+      any |= need;
+      w[u] = need ? __builtin_amdgcn_raw_buffer_load_b32(rs, r * p.am_ld + key, 0, 0) : ~0u;
     }
-    vis |= ~hid;
-    if (wvalid) brow[(int64_t)r * p.nw] = hid;
+    if (__builtin_amdgcn_ballot_w64(any) == 0) {
+      // no row of this batch reaches the wave's keys: every word is all hidden
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (store && r0 + u <= q1) bcol[(int64_t)(r0 + u) * p.nw] = 0xffffffffu;
+      continue;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      // bit 7 of each byte: set when the byte is nonzero (its low seven bits plus 0x7f carry
+      // into bit 7 unless they are zero, and bit 7 itself comes in through the OR)
+      const unsigned y = (((w[u] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[u]) & 0x80808080u;
+      unsigned word = (y >> (7 - sl)) | tail;  // byte b's flag to bit 8b + sl
+      vis |= ~word & mine;
+      // OR over the eight lanes of the word by DPP moves: swap neighbours and pairs within each
+      // quad (quad_perm [1,0,3,2] and [2,3,0,1]), then mirror within each half-row of eight
+      // lanes (row_half_mirror: lane i takes lane 7 - i, from the other quad)
+      word |= (unsigned)__builtin_amdgcn_mov_dpp((int)word, 0xB1, 0xF, 0xF, false);
+      word |= (unsigned)__builtin_amdgcn_mov_dpp((int)word, 0x4E, 0xF, 0xF, false);
+      word |= (unsigned)__builtin_amdgcn_mov_dpp((int)word, 0x141, 0xF, 0xF, false);
+      if (store && r0 + u <= q1) bcol[(int64_t)(r0 + u) * p.nw] = word;
+    }
   }
   int kmin = 0x7fffffff, kmax = -1;
   if (vis != 0u) {
-    kmin = kw + __builtin_ctz(vis);
-    kmax = kw + 31 - __builtin_clz(vis);
+    kmin = key + (__builtin_ctz(vis) >> 3);
+    kmax = key + ((31 - __builtin_clz(vis)) >> 3);
   }
   // work-group reduction: within each wave, then across the four waves through LDS
 #pragma unroll
