@@ -39,6 +39,7 @@ SIGNATURES = {
                      + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
     "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 2),
+    "fa_bwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 7),
     "fa_bwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 9 + [ctypes.c_float]
                     + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
@@ -157,6 +158,13 @@ def mask_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, n_splits: in
     (0: shared along that axis); 0 for sizes it rejects."""
     return int(load_library().fa_fwd_mask_workspace_bytes(B, Hq, Nq, Nk, d, n_splits, mask_b_stride,
                                                            mask_h_stride))
+
+
+def bwd_mask_workspace_bytes(B: int, Hq: int, Nq: int, Nk: int, d: int, mask_b_stride: int,
+                             mask_h_stride: int) -> int:
+    """Bytes of workspace fa_bwd_mask needs for a mask with these batch and head strides
+    (0: shared along that axis); 0 for sizes it rejects."""
+    return int(load_library().fa_bwd_mask_workspace_bytes(B, Hq, Nq, Nk, d, mask_b_stride, mask_h_stride))
 
 
 def _edges(causal: bool, window) -> Tuple[int, int]:
@@ -290,7 +298,7 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
     the input dtype); dout: the gradient at o, [B, Hq, N, d] in the input
     dtype. causal and window as for ``fwd`` (k and v may have their own
     sequence length). The workspace (a uint8 CUDA tensor of at least
-    ``bwd_workspace_bytes`` bytes) and the outputs (``grads``: contiguous
+    ``bwd_workspace_bytes`` bytes, or ``bwd_mask_workspace_bytes`` with a mask) and the outputs (``grads``: contiguous
     float32 dq [B, Hq, N, d], dk and dv [B, Hkv, N, d]) are allocated when not
     given. mask, as for ``fwd`` (and the same one the forward used), goes to fa_bwd_mask.
     Runs on ``stream`` or torch's current stream.
@@ -321,7 +329,13 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
         scale = 1.0 / math.sqrt(d)
     in_code = FA_F16 if q.dtype == torch.float16 else FA_BF16
     o_code = FA_F32 if o.dtype == torch.float32 else in_code
-    need = bwd_workspace_bytes(B, Hq, N, d)
+    if mask is not None:
+        if mask.device != q.device:
+            raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
+        sb, sh, ld = mask_strides(mask, B, Hq, N, Nk)
+        need = bwd_mask_workspace_bytes(B, Hq, N, Nk, d, sb, sh)
+    else:
+        need = bwd_workspace_bytes(B, Hq, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if workspace.device != q.device or workspace.numel() * workspace.element_size() < need:
@@ -337,9 +351,6 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     if mask is not None:
-        if mask.device != q.device:
-            raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
-        sb, sh, ld = mask_strides(mask, B, Hq, N, Nk)
         _check(bwd_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), mask.data_ptr(), sb, sh,
                             ld, B, Hq, Hkv, N, Nk, d, scale, left, right, in_code, o_code, stream.cuda_stream))

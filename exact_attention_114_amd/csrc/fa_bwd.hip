@@ -11,6 +11,7 @@
 
 #include "../../include/fa.h"
 #include "fa_bwd_kernel.hpp"
+#include "fa_mask.hpp"
 #include "fa_status.hpp"
 
 namespace {
@@ -108,6 +109,10 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  // with a mask, the pre-pass's parts follow the row statistics in the workspace
+  const fa::MaskLayout ml = fa::mask_layout(B * Hq * ws_blk * 64 * 4, B, Hq, Nq, Nk, am ? mask.b_stride : 0,
+                                            am ? mask.h_stride : 0, true);
+  if (am && !fa::mask_prep_fits(ml)) return FA_ERR_SHAPE;
 
   fa::BwdParams p;
   p.q = q;
@@ -139,6 +144,19 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   p.am_sb = mask.b_stride;
   p.am_sh = mask.h_stride;
   p.am_ld = (int)mask.row_stride;
+  char* const wsb = reinterpret_cast<char*>(workspace);
+  p.am_bits = am ? reinterpret_cast<const unsigned*>(wsb + ml.bits_off) : nullptr;
+  p.am_nw = (int)ml.nw;
+  p.bits_sh = ml.planes_h > 1 ? Nq * ml.nw : 0;
+  p.bits_sb = ml.planes_b > 1 ? ml.planes_h * Nq * ml.nw : 0;
+  p.am_hull = am ? reinterpret_cast<const int2*>(wsb + ml.hull_off) : nullptr;
+  p.hull_nch = (int)ml.nch;
+  p.hull_sh = ml.planes_h > 1 ? ml.nq * ml.nch : 0;
+  p.hull_sb = ml.planes_b > 1 ? ml.planes_h * ml.nq * ml.nch : 0;
+  p.am_flags = am ? reinterpret_cast<const unsigned char*>(wsb + ml.flags_off) : nullptr;
+  p.flags_nq = (int)ml.nq;
+  p.flags_sh = ml.planes_h > 1 ? ml.nkt * ml.nq : 0;
+  p.flags_sb = ml.planes_b > 1 ? ml.planes_h * ml.nkt * ml.nq : 0;
 
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const int64_t prep_rows = B * Hq * ws_blk * 32;
@@ -146,6 +164,14 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   const int64_t grid_q = B * Hq * tq;
   const bool bf16 = in_dtype == FA_BF16, o_f32 = o_dtype == FA_F32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (am) {
+    const hipError_t e = fa::launch_mask_prep(ml, true, wsb, mask.data, mask.b_stride, mask.h_stride,
+                                              mask.row_stride, p.Nq, p.Nk, p.left, p.right, s);
+    if (e != hipSuccess) {
+      fa::last_hip_error = (int)e;
+      return FA_ERR_HIP;
+    }
+  }
   switch (d) {
 #define FA_BWD_D(DD)                                                                            \
   case DD:                                                                                      \
@@ -168,6 +194,14 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d) {
   int64_t wb = 0, t = 0, u = 0;
   if (check_bwd(B, Hq, 1, N, 1, d, &wb, &t, &u) != FA_OK) return 0;
   return (size_t)(B * Hq * wb * 64 * (int64_t)sizeof(float));
+}
+
+size_t fa_bwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d,
+                                   int64_t mask_b_stride, int64_t mask_h_stride) {
+  int64_t wb = 0, t = 0, u = 0;
+  if (mask_b_stride < 0 || mask_h_stride < 0) return 0;
+  if (check_bwd(B, Hq, 1, Nq, Nk, d, &wb, &t, &u) != FA_OK) return 0;
+  return (size_t)fa::mask_layout(B * Hq * wb * 64 * 4, B, Hq, Nq, Nk, mask_b_stride, mask_h_stride, true).bytes;
 }
 
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -59,6 +59,18 @@ struct BwdParams {
   const unsigned char* am;
   long long am_sb, am_sh;
   int am_ld;
+  // the mask as fa_mask_prep_kernel leaves it (kernels built with AM; strides 0 along an axis
+  // the mask shares): bits as in the forward's Params (dQ), the key hull of each 128-row Q-tile
+  // (dQ), and a flag per 128-key tile and Q-tile where the block has a visible pair (dK/dV)
+  const unsigned* am_bits;
+  long long bits_sb, bits_sh;
+  int am_nw;
+  const int2* am_hull;
+  long long hull_sb, hull_sh;
+  int hull_nch;
+  const unsigned char* am_flags;  // plane (b, hq) at am_flags + b*flags_sb + hq*flags_sh: [kt][t]
+  long long flags_sb, flags_sh;
+  int flags_nq;                   // Q-tiles per row of flags
 };
 
 // One LDS swizzle for tiles that are read both as rows (ds_read_b128: 16 consecutive rows at one
@@ -284,11 +296,53 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
 
   // query blocks whose band reaches keys [k0, k0 + 32*NW): rows i with
   // i + off - left <= k0 + 32*NW - 1 and i + off + right >= k0
-  const int q_lo = BAND ? max(0, k0 - p.off - p.right) : 0;
-  const int q_hi = BAND ? min(Nq - 1, k0 + 32 * NW - 1 - p.off + p.left) : Nq - 1;
+  int q_lo = BAND ? max(0, k0 - p.off - p.right) : 0;
+  int q_hi = BAND ? min(Nq - 1, k0 + 32 * NW - 1 - p.off + p.left) : Nq - 1;
+  if constexpr (AM) {
+    // narrow to the Q-tiles of 128 rows whose block with this key tile has a visible pair, over
+    // the G query heads' mask planes (one plane when the mask shares the head axis)
+    static_assert(32 * NW == 128, "the flags cover 128-key tiles");
+    // (lanes read 64 flags at a time; the ballot keeps the result wave-uniform)
+    int tmin = 0x7fffffff, tmax = -1;
+    if (q_hi >= q_lo) {
+      const int ng = p.flags_sh != 0 ? G : 1;
+      const int t0 = q_lo / 128, t1 = q_hi / 128;
+      for (int g = 0; g < ng; ++g) {
+        const unsigned char* fl = p.am_flags + b * p.flags_sb + (hkv * G + g) * p.flags_sh + (int64_t)kt * p.flags_nq;
+        for (int tb = t0; tb <= t1; tb += 64) {
+          const int tt = tb + lane;
+          const unsigned long long bal = __builtin_amdgcn_ballot_w64(tt <= t1 && fl[tt] != 0);
+          if (bal != 0) {
+            tmin = min(tmin, tb + (int)__builtin_ctzll(bal));
+            tmax = max(tmax, tb + 63 - (int)__builtin_clzll(bal));
+          }
+        }
+      }
+    }
+    q_lo = max(q_lo, tmin == 0x7fffffff ? Nq : 128 * tmin);
+    q_hi = min(q_hi, 128 * tmax + 127);
+  }
   const int qb0 = q_lo / 32;
   const int nqb = q_hi >= q_lo ? q_hi / 32 - qb0 + 1 : 0;
   const int n_it = G * nqb;
+  // With one mask plane for the G heads, lane l holds the flag of Q-tile q_lo/128 + l: an
+  // iteration whose block the mask leaves wholly visible (flag 2) loads no mask tile and
+  // applies none (the band is still applied). Q-tiles past the first 64 always apply it.
+  int mflag = 1;
+  if constexpr (AM) {
+    const int tt = q_lo / 128 + lane;
+    if (p.flags_sh == 0 && nqb > 0 && tt <= q_hi / 128)
+      mflag = p.am_flags[b * p.flags_sb + (int64_t)kt * p.flags_nq + tt];
+  }
+  auto mask_free = [&](int it) -> bool {
+    if constexpr (!AM) {
+      return false;
+    } else {
+      if (p.flags_sh != 0) return false;
+      const int qt = (qb0 + it % nqb) / 4 - q_lo / 128;  // wave-uniform, >= 0
+      return qt < 64 && __builtin_amdgcn_readlane(mflag, qt) == 2;
+    }
+  };
 
   // Mask tile DMA (4-byte loads): wave w fills rows [8w, 8w + 8) of the 32-row tile, two rows
   // of MROW bytes per instruction; lane l writes row 8w + 2n + l/32, bytes 4(l%32) .. +3. Its
@@ -318,7 +372,8 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     const int64_t head = (int64_t)b * p.Hq + hkv * G + g;
     dma_rows<D, NW>((const char*)((const T*)p.q + head * Nq * D), Nq, qb * 32, dq_, wave, ld_off);
     dma_rows<D, NW>((const char*)((const T*)p.dout + head * Nq * D), Nq, qb * 32, dg_, wave, ld_off);
-    if constexpr (AM) dma_mask(head, qb, dm_);
+    if constexpr (AM)
+      if (!mask_free(it)) dma_mask(head, qb, dm_);
     if (wave == 0) {
       void* wp = (void*)(p.ws + (head * p.ws_blk + qb) * 64);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(wp, (short)0, 256, kBufferWord3);
@@ -348,6 +403,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
                   (lds_char*)(odd ? sM0 : sM1));
     const int qb = qb0 + (it % nqb);
     const int q0 = qb * 32;
+    const bool mfree = mask_free(it);
 
     // S = Q K^T, dP = dO V^T: lane holds key l32 (column), queries 8(i/4) + 4h + i%4 (rows)
     f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -385,11 +441,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
           s1 = (unsigned)(pb - vlo) > width ? -__builtin_inff() : s1;
         }
         if constexpr (AM) {
-          // mask bytes of queries 8g4 + 4h + 2r2 (+1) and this lane's key
-          const int ln = lane_id_here();
-          const lds_char* mp = tm + (8 * g4 + 2 * r2) * MROW + 32 * wave + (ln >> 5) * (4 * MROW) + (ln & 31);
-          s0 = *(const lds_uchar*)mp != 0 ? -__builtin_inff() : s0;
-          s1 = *(const lds_uchar*)(mp + MROW) != 0 ? -__builtin_inff() : s1;
+          if (!mfree) {
+            // mask bytes of queries 8g4 + 4h + 2r2 (+1) and this lane's key
+            const int ln = lane_id_here();
+            const lds_char* mp = tm + (8 * g4 + 2 * r2) * MROW + 32 * wave + (ln >> 5) * (4 * MROW) + (ln & 31);
+            s0 = *(const lds_uchar*)mp != 0 ? -__builtin_inff() : s0;
+            s1 = *(const lds_uchar*)(mp + MROW) != 0 ? -__builtin_inff() : s1;
+          }
         }
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a[2 * r2]));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -a[2 * r2 + 1]));
@@ -489,8 +547,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   for (int db = 0; db < NDB; ++db) toff[db] = tr_off<D>(lane, 0, db);
 
   // the K/V tiles the Q-tile's band touches: [j_lo, j_lo + nt), and the lane's keys [klo, khi]
-  const int lo_t = BAND ? max(0, q0 + p.off - p.left) : 0;
-  const int hi_t = BAND ? min(Nk - 1, min(q0 + BM, Nq) - 1 + p.off + p.right) : Nk - 1;
+  int lo_t = BAND ? max(0, q0 + p.off - p.left) : 0;
+  int hi_t = BAND ? min(Nk - 1, min(q0 + BM, Nq) - 1 + p.off + p.right) : Nk - 1;
+  if constexpr (AM) {
+    // narrow to the mask's key hull for this Q-tile (as the forward)
+    static_assert(BM == 128, "the hull covers 128-row Q-tiles");
+    if (hi_t >= lo_t) {
+      const int2 kr = hull_range(p.am_hull + b * p.hull_sb + hq * p.hull_sh + (int64_t)t * p.hull_nch,
+                                 lo_t / kHullKeys, hi_t / kHullKeys);
+      lo_t = max(lo_t, kr.x);
+      hi_t = min(hi_t, kr.y);
+    }
+  }
   const int j_lo = lo_t / 32;
   const int nt = hi_t >= lo_t ? hi_t / 32 - j_lo + 1 : 0;
   const int khi = BAND ? min(Nk - 1, qr + p.off + p.right) : Nk - 1;
@@ -500,21 +568,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
   const float c = p.c;
 
-  // mask words of the lane's query for a 32-key tile: dword g holds keys 32j + 8g + 4h + (0..3),
-  // i.e. scores 4g .. 4g+3 (as in the forward); loaded one tile ahead, the offset wholly in the
-  // vector operand so reads past the head's plane return zeros
-  unsigned am_w[4] = {0u, 0u, 0u, 0u};
+  // the mask word of the lane's query for a 32-key tile (as in the forward: score 4g + i, key
+  // 32j + 8g + 4h + i, is bit 8i + 2g + h); loaded one tile ahead, the offset wholly in the
+  // vector operand so reads past the plane return zeros
+  unsigned am_w = 0u;
   __amdgpu_buffer_rsrc_t am_rs;
   int am_v0 = 0;
-  auto load_am = [&](int jt) {
-    const int vo = am_v0 + 32 * jt;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) am_w[g4] = __builtin_amdgcn_raw_buffer_load_b32(am_rs, vo + 8 * g4, 0, 0);
-  };
+  auto load_am = [&](int jt) { am_w = __builtin_amdgcn_raw_buffer_load_b32(am_rs, am_v0 + 4 * jt, 0, 0); };
   if constexpr (AM) {
-    const unsigned char* plane = p.am + (long long)b * p.am_sb + (long long)hq * p.am_sh;
-    am_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.am_ld, kBufferWord3);
-    am_v0 = qr * p.am_ld + 4 * h;
+    const unsigned* plane = p.am_bits + b * p.bits_sb + hq * p.bits_sh;
+    am_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.am_nw * 4, kBufferWord3);
+    am_v0 = qr * p.am_nw * 4;
     if (nt > 0) load_am(j_lo);
   }
   if (nt > 0) {
@@ -550,8 +614,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
       }
     }
     if constexpr (AM) {
+      const unsigned x = am_w >> h;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = ((am_w[i >> 2] >> (8 * (i & 3))) & 0xffu) != 0u ? -__builtin_inff() : s[i];
+      for (int i = 0; i < 16; ++i)
+        s[i] = ((x >> (8 * (i & 3) + 2 * (i >> 2))) & 1u) != 0u ? -__builtin_inff() : s[i];
       if (r + 1 < nt) load_am(j + 1);  // the next iteration's opening wait covers it
     }
     u32x4 sw[2];

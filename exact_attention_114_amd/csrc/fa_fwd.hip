@@ -13,6 +13,7 @@
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_mask.hpp"
 #include "fa_status.hpp"
 
 namespace {
@@ -131,29 +132,6 @@ struct MaskArg {
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
 };
 
-// Workspace of a masked call, each part at a 256-byte boundary: the split partials (if any),
-// the mask hull (an int2 per plane, Q-tile and chunk of kHullKeys keys), then the mask as bits
-// (ceil(Nk / 32) words per row of each plane). A plane per batch element and/or head when the
-// mask's stride along that axis is nonzero.
-int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
-int64_t hull_chunks(int64_t Nk) { return (Nk + fa::kHullKeys - 1) / fa::kHullKeys; }
-struct MaskLayout {
-  int64_t planes_b, planes_h, nch, nw, hull_off, bits_off, bytes;
-};
-MaskLayout mask_layout(int ns, int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int64_t nq,
-                       int64_t b_stride, int64_t h_stride) {
-  MaskLayout m;
-  m.planes_b = b_stride ? B : 1;
-  m.planes_h = h_stride ? Hq : 1;
-  m.nch = hull_chunks(Nk);
-  m.nw = (Nk + 31) / 32;
-  const int64_t planes = m.planes_b * m.planes_h;
-  m.hull_off = align256(ns > 1 ? ns * B * Hq * Nq * (d + 1) * 4 : 0);
-  m.bits_off = align256(m.hull_off + planes * nq * m.nch * 8);
-  m.bytes = m.bits_off + planes * Nq * m.nw * 4;
-  return m;
-}
-
 // Every forward entry point: validation, the split plan (n_splits = 1: never split; workspace
 // is then unused unless there is a mask), the mask hull, the attention kernel and, with split
 // keys, the merge.
@@ -188,8 +166,9 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
     return FA_ERR_ALIGN;
   const int64_t rows = B * Hq * Nq;
   if (grid * ns >= ((int64_t)1 << 31) || rows * d * ns >= ((int64_t)1 << 40)) return FA_ERR_SHAPE;
-  const MaskLayout ml = mask_layout(ns, B, Hq, Nq, Nk, d, nq, am ? mask.b_stride : 0, am ? mask.h_stride : 0);
-  if (am && ml.planes_b * ml.planes_h * nq * ml.nch >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;  // prep grid
+  const fa::MaskLayout ml = fa::mask_layout(ns > 1 ? ns * B * Hq * Nq * (d + 1) * 4 : 0, B, Hq, Nq, Nk,
+                                            am ? mask.b_stride : 0, am ? mask.h_stride : 0, false);
+  if (am && !fa::mask_prep_fits(ml)) return FA_ERR_SHAPE;
 
   fa::Params p;
   p.q = q;
@@ -230,25 +209,8 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   const int kb = key_blocks(d, grid * ns);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (am) {
-    fa::PrepParams pp;
-    pp.am = static_cast<const unsigned char*>(mask.data);
-    pp.am_sb = mask.b_stride;
-    pp.am_sh = mask.h_stride;
-    pp.am_ld = (int)mask.row_stride;
-    pp.hull = hull;
-    pp.bits = bits;
-    pp.planes_h = (int)ml.planes_h;
-    pp.Nq = p.Nq;
-    pp.Nk = p.Nk;
-    pp.off = p.off;
-    pp.left = p.left;
-    pp.right = p.right;
-    pp.n_qtiles = p.n_qtiles;
-    pp.nch = (int)ml.nch;
-    pp.nw = (int)ml.nw;
-    hipLaunchKernelGGL(fa::fa_mask_prep_kernel<kBlockM>, dim3((unsigned)(ml.planes_b * ml.planes_h * nq * ml.nch)),
-                       dim3(256), 0, s, pp);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = fa::launch_mask_prep(ml, false, wsb, mask.data, mask.b_stride, mask.h_stride,
+                                              mask.row_stride, p.Nq, p.Nk, p.left, p.right, s);
     if (e != hipSuccess) {
       fa::last_hip_error = (int)e;
       return FA_ERR_HIP;
@@ -318,7 +280,9 @@ size_t fa_fwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk
   if (check_problem(B, Hq, 1, Nq, Nk, d, FA_F16, &nq, &grid) != FA_OK) return 0;
   int ns = 1, kc = 0;
   split_plan(grid, Nk, n_splits, &ns, &kc);
-  return (size_t)mask_layout(ns, B, Hq, Nq, Nk, d, nq, mask_b_stride, mask_h_stride).bytes;
+  return (size_t)fa::mask_layout(ns > 1 ? ns * B * Hq * Nq * (d + 1) * 4 : 0, B, Hq, Nq, Nk, mask_b_stride,
+                                 mask_h_stride, false)
+      .bytes;
 }
 
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,

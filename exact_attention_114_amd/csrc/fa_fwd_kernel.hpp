@@ -136,15 +136,38 @@ struct Params {
   int hull_nch;
 };
 
-// Keys per chunk of the mask hull.
-constexpr int kHullKeys = 1024;
-
 // The lane id, formed where it is used by an opaque instruction sequence: it cannot be hoisted
 // out of a loop, so it holds no register across the loop.
 __device__ inline int lane_id_here() {
   int v;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
   return v;
+}
+
+// Keys per chunk of the mask hull.
+constexpr int kHullKeys = 1024;
+
+// The key range a mask leaves to a Q-tile: the least first key and the greatest last key over
+// its hull entries [c0, c1], {INT_MAX, -1} when none has a visible key. The wave's lanes load
+// the entries in parallel and reduce them; the results are made wave-uniform, so the loop
+// bounds built from them stay scalar. Every lane of the wave must call it.
+__device__ inline int2 hull_range(const int2* hl, int c0, int c1) {
+  int kmin = 0x7fffffff, kmax = -1;
+  const int lane = (int)(threadIdx.x & 63);
+  for (int cb = c0; cb <= c1; cb += 64) {
+    const int c = cb + lane;
+    if (c <= c1) {
+      const int2 e = hl[c];
+      kmin = min(kmin, e.x);
+      kmax = max(kmax, e.y);
+    }
+  }
+#pragma unroll
+  for (int sft = 32; sft >= 1; sft >>= 1) {
+    kmin = min(kmin, __shfl_xor(kmin, sft));
+    kmax = max(kmax, __shfl_xor(kmax, sft));
+  }
+  return make_int2(__builtin_amdgcn_readfirstlane(kmin), __builtin_amdgcn_readfirstlane(kmax));
 }
 
 // ---- element-type traits ------------------------------------------------------------------
@@ -425,15 +448,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   if constexpr (AM) {
     // narrow to the mask's hull for this Q-tile: keys outside it are hidden from every row
     if (hi_t >= lo_t) {
-      const int2* hl = p.am_hull + b * p.hull_sb + hq * p.hull_sh + (int64_t)t * p.hull_nch;
-      int kmin = 0x7fffffff, kmax = -1;
-      for (int ch = lo_t / kHullKeys; ch <= hi_t / kHullKeys; ++ch) {
-        const int2 e = hl[ch];
-        kmin = min(kmin, e.x);
-        kmax = max(kmax, e.y);
-      }
-      lo_t = max(lo_t, kmin);
-      hi_t = min(hi_t, kmax);
+      const int2 kr = hull_range(p.am_hull + b * p.hull_sb + hq * p.hull_sh + (int64_t)t * p.hull_nch,
+                                 lo_t / kHullKeys, hi_t / kHullKeys);
+      lo_t = max(lo_t, kr.x);
+      hi_t = min(hi_t, kr.y);
     }
   }
   const int j_lo = lo_t / BN;
@@ -773,7 +791,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
 //   - records the chunk's hull: the first and last key some row of the tile may see, or
 //     {INT_MAX, -1} when there is none (a group of four keys counts whole when the band reaches
 //     it: the hull only has to contain the visible keys, and the attention kernel intersects
-//     it with the Q-tile's band).
+//     it with the Q-tile's band);
+//   - optionally flags each 128-key tile of the chunk: 0 where no row of the tile may see it, 2
+//     where the mask hides none of the block's pairs inside the band, else 1 (the backward's
+//     dK/dV kernel takes its query range from these flags and skips the mask on blocks of 2).
 // 256 threads: thread x reads dword x of the chunk (keys k0 + 4x .. + 3) of every row of the
 // tile whose band reaches it (a wave reads 256 consecutive bytes of a row; every read lies
 // inside the plane), and the eight threads of one word gather its bits by DPP moves.
@@ -783,9 +804,12 @@ struct PrepParams {
   int am_ld;
   int2* hull;                // [planes][n_qtiles][nch]
   unsigned* bits;            // [planes][Nq][nw]
+  unsigned char* flags;      // optional (nullptr: not written): [planes][n_ktiles][n_qtiles]: 0
+                             // where no row of Q-tile t may see a key of 128-key tile kt, 2 where
+                             // the mask hides none of the block's pairs inside the band, else 1
   int planes_h;              // Hq or 1 (planes are numbered pb * planes_h + ph)
   int Nq, Nk, off, left, right;
-  int n_qtiles, nch, nw;
+  int n_qtiles, nch, nw, n_ktiles;
 };
 
 template <int BM>
@@ -810,15 +834,17 @@ __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
                                                                       kBufferWord3);
   unsigned* const bcol = p.bits + (int64_t)plane * p.Nq * p.nw + wi;
   unsigned vis = 0u;  // bits (8b + sl) of this thread's keys that some row may see
+  unsigned hidm = 0u;  // bits of its keys below Nk that the mask hides from some row it read
   for (int r0 = q0; r0 <= q1; r0 += 16) {
     unsigned w[16];
+    bool need[16];
     bool any = false;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int r = r0 + u;  // band edges are at most 2^30: r + off +- edge fits in 32 bits
-      const bool need = nk > 0 && r <= q1 && key <= r + p.off + p.right && key + nk - 1 >= r + p.off - p.left;
-      any |= need;
-      w[u] = need ? __builtin_amdgcn_raw_buffer_load_b32(rs, r * p.am_ld + key, 0, 0) : ~0u;
+      need[u] = nk > 0 && r <= q1 && key <= r + p.off + p.right && key + nk - 1 >= r + p.off - p.left;
+      any |= need[u];
+      w[u] = need[u] ? __builtin_amdgcn_raw_buffer_load_b32(rs, r * p.am_ld + key, 0, 0) : ~0u;
     }
     if (__builtin_amdgcn_ballot_w64(any) == 0) {
       // no row of this batch reaches the wave's keys: every word is all hidden
@@ -834,6 +860,7 @@ __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
       const unsigned y = (((w[u] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[u]) & 0x80808080u;
       unsigned word = (y >> (7 - sl)) | tail;  // byte b's flag to bit 8b + sl
       vis |= ~word & mine;
+      hidm |= need[u] ? word & ~tail : 0u;
       // OR over the eight lanes of the word by DPP moves: swap neighbours and pairs within each
       // quad (quad_perm [1,0,3,2] and [2,3,0,1]), then mirror within each half-row of eight
       // lanes (row_half_mirror: lane i takes lane 7 - i, from the other quad)
@@ -847,6 +874,18 @@ __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
   if (vis != 0u) {
     kmin = key + (__builtin_ctz(vis) >> 3);
     kmax = key + ((31 - __builtin_clz(vis)) >> 3);
+  }
+  if (p.flags != nullptr) {
+    // a wave covers 256 keys, two 128-key tiles: lanes 0..31 and 32..63
+    const unsigned long long bv = __builtin_amdgcn_ballot_w64(vis != 0u);
+    const unsigned long long bh = __builtin_amdgcn_ballot_w64(hidm != 0u);
+    const int lane = x & 63;
+    const int kt = ch * (kHullKeys / 128) + (x >> 5);
+    if ((lane & 31) == 0 && kt < p.n_ktiles) {
+      const bool v = (lane == 0 ? (unsigned)bv : (unsigned)(bv >> 32)) != 0u;
+      const bool hd = (lane == 0 ? (unsigned)bh : (unsigned)(bh >> 32)) != 0u;
+      p.flags[((int64_t)plane * p.n_ktiles + kt) * p.n_qtiles + t] = !v ? 0 : hd ? 1 : 2;
+    }
   }
   // work-group reduction: within each wave, then across the four waves through LDS
 #pragma unroll

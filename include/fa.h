@@ -276,6 +276,12 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
  * fa_bwd_mask — fa_bwd_ex for a forward run with fa_fwd_mask: the same mask
  * (arguments and layout as fa_fwd_mask) hides the same scores, so P and dS
  * are zero there. The LSE must come from the masked forward.
+ *   workspace  device pointer to fa_bwd_mask_workspace_bytes(..., mask_b_stride,
+ *              mask_h_stride) bytes (the row statistics, then the mask packed
+ *              to bits and its summaries), 16-byte aligned, owned by the caller
+ * A pre-pass reads the mask once, as in fa_fwd_mask; the dQ kernel then visits
+ * only the key tiles inside each Q-tile's hull, and the dK/dV kernel only the
+ * Q-tiles whose block with its key tile has a visible pair.
  * Other arguments, errors and execution as fa_bwd_ex; a NULL mask is
  * FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN.
  */
@@ -286,6 +292,17 @@ fa_status fa_bwd_mask(const void* q, const void* k, const void* v, const void* o
                       int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
                       int64_t window_left, int64_t window_right, fa_dtype in_dtype,
                       fa_dtype o_dtype, void* stream);
+
+/*
+ * fa_bwd_mask_workspace_bytes — bytes of workspace fa_bwd_mask needs for a mask
+ * with these batch and head strides (0: shared along that axis): the row
+ * statistics of fa_bwd_workspace_bytes(B, Hq, Nq, d), then, each at a 256-byte
+ * boundary, the key hull and the packed mask as for fa_fwd_mask_workspace_bytes,
+ * then P x ceil(Nk / 128) x ceil(Nq / 128) flag bytes (P mask planes).
+ * 0 when the arguments are invalid. Makes no HIP call.
+ */
+size_t fa_bwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d,
+                                   int64_t mask_b_stride, int64_t mask_h_stride);
 
 /*
  * fa_bwd_workspace_bytes — size in bytes of the workspace fa_bwd (or

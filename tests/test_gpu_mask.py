@@ -301,3 +301,35 @@ def test_bwd_mask_with_band_and_hidden_rows(band, d, dt):
     mask = make_mask("random", (1, 4, 200, 200), 1620 + d)
     mask[:, 1, 7] = 1
     run_bwd(1, 4, 2, 200, 200, d, dt, band, mask, 1630 + d)
+
+
+# ---------------------------------------------------------------- backward over the mask's summaries
+# fa_bwd_mask runs the same pre-pass: the dQ kernel reads the packed bits and stays inside each
+# Q-tile's key hull, and the dK/dV kernel visits only the Q-tiles flagged for its key tile.
+
+
+@pytest.mark.parametrize("band", [(None, 0), (None, None)])
+@pytest.mark.parametrize("d,dt", [(64, I.F16), (128, I.BF16)])
+def test_bwd_document_mask(band, d, dt):
+    """Documents of 37..600 tokens in sequences of 1300 (two hull chunks, a ragged end)."""
+    B, Hq, Hkv, N = 2, 4, 2, 1300
+    mask = I.document_mask(I.document_lengths(B, N, 1700 + d, 37, 600), N)
+    run_bwd(B, Hq, Hkv, N, N, d, dt, band, mask, 1710 + d)
+
+
+def test_bwd_document_mask_per_head_planes():
+    """A plane per (batch, head), GQA 2:1 (the dK/dV flags are merged over the sibling heads),
+    Nq < Nk."""
+    B, Hq, Hkv, Nq, Nk = 1, 4, 2, 300, 1100
+    planes = [I.document_mask(I.document_lengths(1, Nk, 1720 + i, 40, 500), Nk)[0, 0, Nk - Nq:]
+              for i in range(B * Hq)]
+    run_bwd(B, Hq, Hkv, Nq, Nk, 64, I.BF16, (None, 0), np.stack(planes).reshape(B, Hq, Nq, Nk), 1730)
+
+
+def test_bwd_mask_hidden_q_tiles_and_keys():
+    """A Q-tile whose rows see nothing (zero dQ) and a key range no query sees (zero dK, dV)."""
+    B, Hq, Hkv, N = 1, 2, 1, 700
+    mask = np.zeros((1, 1, N, N), np.uint8)
+    mask[..., 128:256, :] = 1   # rows of the second Q-tile see nothing
+    mask[..., 384:640] = 1      # keys 384..639 are hidden from every query
+    run_bwd(B, Hq, Hkv, N, N, 128, I.F16, (None, None), mask, 1740)
