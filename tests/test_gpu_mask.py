@@ -333,3 +333,19 @@ def test_bwd_mask_hidden_q_tiles_and_keys():
     mask[..., 128:256, :] = 1   # rows of the second Q-tile see nothing
     mask[..., 384:640] = 1      # keys 384..639 are hidden from every query
     run_bwd(B, Hq, Hkv, N, N, 128, I.F16, (None, None), mask, 1740)
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 1), (3, 7), (1, 33), (5, 1024), (130, 1025), (64, 2048)])
+def test_mask_small_and_chunk_edges(nq, nk):
+    """Tiny and ragged key counts and Nk on the 1024-key chunk edge (forward, causal and not)."""
+    for band in ((None, None), (None, 0)):
+        run(1, 2, 1, nq, nk, 64, I.F16, band, make_mask("random", (1, 2, nq, nk), 1750 + nk), 1760 + nk)
+
+
+def test_mask_all_hidden_forward_and_backward():
+    """Every key hidden: O = 0 and LSE = -inf for every row, and all three gradients zero."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 300, 128
+    mask = np.ones((1, 1, N, N), np.uint8)
+    O, L = run(B, Hq, Hkv, N, N, d, I.BF16, (None, None), mask, 1770)
+    assert np.isneginf(L).all() and (O == 0).all()
+    run_bwd(B, Hq, Hkv, N, N, d, I.BF16, (None, None), mask, 1771)
