@@ -482,9 +482,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   load_k(j_lo, K0);
   load_k(j_lo + 1, K1);
   // Mask bits: am_w[kb] is the word of keys kbase + 32kb .. + 31 of this lane's query row; the
-  // lane's score 4g + i of block kb (key 32kb + 8g + 4h + i) is bit 8i + 2g + h. One descriptor spans the
-  // plane (a read past it gives zeros); the whole offset goes into the vector operand (the
-  // scalar one stays 0), so the range check covers it and a prefetch past the plane reads zeros.
+  // lane's score 4g + i of block kb (key 32kb + 8g + 4h + i) is bit 8i + 2g + h. One
+  // descriptor spans the plane; the whole offset goes into the vector operand (the scalar one
+  // stays 0), so the range check covers it and a prefetch past the plane reads zeros.
   // The lane's row offset is formed at each load from an opaque lane id (the masked d = 128
   // kernel has no register to keep it in); rows past Nq read the last row.
   unsigned am_w[AM ? KB : 1];
