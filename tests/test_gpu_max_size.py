@@ -1,0 +1,50 @@
+"""GPU parity at the largest head plane the C ABI accepts: N * d = 2^30 - 2^16 elements (a
+2 GiB bf16 plane per tensor), where the kernel's 32-bit byte offsets within a plane and its
+prefetches past the plane's end come closest to 2^31.
+
+A causal sliding window of 256 keys keeps the work small (every row sees at most 257 keys),
+so the whole sequence runs in one launch of 65532 work-groups; rows at both ends and in the
+middle are compared with the fp64 oracle on the key slice each row can see. Bars as in
+test_gpu_parity.py: O within 1e-2 (bf16 inputs), LSE within 1e-4 relative with a floor of 1.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_114_amd as fa
+from exact_attention_114_amd import inputs as I
+from oracle.attention import head_attention_band_fp64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MAX_PLANE = (1 << 30) - (1 << 16)
+
+
+def test_largest_plane_d128_window():
+    d, dt, left = 128, I.BF16, 256
+    N = MAX_PLANE // d
+    assert N * d == MAX_PLANE
+    print(f"[gpu] fa_fwd largest plane N={N} d={d} {dt} window=({left}, 0)", flush=True)
+    qkv = I.draw_qkv(1, 1, 1, N, d, dt, 1800)
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV) for x in (qkv.q, qkv.k, qkv.v))
+    scale = d ** -0.5
+    O, L = fa.fwd(q, k, v, scale=scale, window=(left, 0))
+    torch.cuda.synchronize()
+    del q, k, v
+    rng = np.random.Generator(np.random.PCG64(1801))
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 257, N // 2, N - 129, N - 128, N - 33, N - 2, N - 1],
+                                     rng.integers(0, N, 24)]))
+    Og = O[0, 0, torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    Lg = L[0, 0, torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    for idx, r in enumerate(rows):
+        s = max(0, int(r) - left)  # the row's keys: s .. r
+        qr = I.bits_to_f64(qkv.q[0, 0, r:r + 1], dt)
+        ks = I.bits_to_f64(qkv.k[0, 0, s:r + 1], dt)
+        vs = I.bits_to_f64(qkv.v[0, 0, s:r + 1], dt)
+        O_ref, L_ref = head_attention_band_fp64(qr, ks, vs, I.scale_f32(scale), left, 0,
+                                                q_pos=np.array([r - s]))
+        err_o = np.abs(Og[idx] - O_ref[0]).max()
+        assert err_o <= 1e-2, f"row {r}: max|dO| {err_o:.3e}"
+        err_l = abs(Lg[idx] - L_ref[0]) / max(1.0, abs(L_ref[0]))
+        assert err_l <= 1e-4, f"row {r}: LSE rel err {err_l:.3e}"
