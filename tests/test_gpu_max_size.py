@@ -48,3 +48,45 @@ def test_largest_plane_d128_window():
         assert err_o <= 1e-2, f"row {r}: max|dO| {err_o:.3e}"
         err_l = abs(Lg[idx] - L_ref[0]) / max(1.0, abs(L_ref[0]))
         assert err_l <= 1e-4, f"row {r}: LSE rel err {err_l:.3e}"
+
+
+def test_largest_plane_d128_window_backward():
+    """fa_bwd_ex at the same size. The gradients of the last 1024 query rows, and of the keys
+    among the last 1024, depend only on those rows (each sees 257 keys, each key is seen by at
+    most 257 rows): their O and LSE are set to the oracle's before the call, and dQ, dK, dV there
+    are checked against the oracle's gradients of that slice within twice the first-order bound
+    (as tests/test_gpu_bwd.py)."""
+    from oracle.backward import head_attention_bwd_band_fp64, head_attention_bwd_bound_fp64
+
+    d, dt, left, blk = 128, I.BF16, 256, 1024
+    N = MAX_PLANE // d
+    print(f"[gpu] fa_bwd largest plane N={N} d={d} {dt} window=({left}, 0)", flush=True)
+    qkv = I.draw_qkv(1, 1, 1, N, d, dt, 1810)
+    dob = I.draw_dout(1, 1, N, d, dt, 1811)
+    to = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV)
+    q, k, v, do = to(qkv.q), to(qkv.k), to(qkv.v), to(dob)
+    scale = d ** -0.5
+    sc = I.scale_f32(scale)
+    O, L = fa.fwd(q, k, v, scale=scale, window=(left, 0))
+    # the oracle's O and LSE for the last blk rows (keys from N - blk - left)
+    r0, k0 = N - blk, N - blk - left
+    qs = I.bits_to_f64(qkv.q[0, 0, r0:], dt)
+    ks = I.bits_to_f64(qkv.k[0, 0, k0:], dt)
+    vs = I.bits_to_f64(qkv.v[0, 0, k0:], dt)
+    dos = I.bits_to_f64(dob[0, 0, r0:], dt)
+    O_ref, L_ref = head_attention_band_fp64(qs, ks, vs, sc, left, 0, off=r0 - k0)
+    O[0, 0, r0:] = torch.from_numpy(O_ref.astype(np.float32)).to(DEV)
+    L[0, 0, r0:] = torch.from_numpy(L_ref.astype(np.float32)).to(DEV)
+    dq, dk, dv = fa.bwd(q, k, v, O, L, do, scale=scale, window=(left, 0))
+    torch.cuda.synchronize()
+    got = (dq[0, 0, r0:].cpu().numpy().astype(np.float64), dk[0, 0, r0:].cpu().numpy().astype(np.float64),
+           dv[0, 0, r0:].cpu().numpy().astype(np.float64))
+    gq, gk, gv = head_attention_bwd_band_fp64(qs, ks, vs, dos, sc, left, 0, off=r0 - k0)
+    bq, bk, bv = head_attention_bwd_bound_fp64(qs, ks, vs, dos, O_ref.astype(np.float32).astype(np.float64), sc,
+                                               False, 2.0 ** -8, band=(left, 0, r0 - k0))
+    # keys k0 .. r0 - 1 are also seen by rows before r0: only keys from r0 on are complete here
+    for name, g, r, bb in (("dQ", got[0], gq, bq), ("dK", got[1], gk[left:], bk[left:]),
+                           ("dV", got[2], gv[left:], bv[left:])):
+        assert np.isfinite(g).all(), f"non-finite {name}"
+        ratio = (np.abs(g - r) / np.maximum(2.0 * bb, 1e-300)).max()
+        assert ratio <= 1.0, f"{name} error reaches {ratio:.3f} of the bar"
