@@ -138,6 +138,13 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   p.ws_blk = (int)ws_blk;
   p.n_tiles = 0;
   p.total_wg = 0;
+  {
+    // interleave the tiles of up to 4 (b, hkv) groups where their lengths vary widely, as the
+    // forward does (causal-like bands and masks)
+    const bool varied = (p.left == kUnlimited && p.right != kUnlimited) || am;
+    const int64_t groups = B * Hkv;
+    p.ilv = !varied ? 1 : groups % 4 == 0 ? 4 : groups % 2 == 0 ? 2 : 1;
+  }
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   p.scale = scale;
   p.am = static_cast<const unsigned char*>(mask.data);

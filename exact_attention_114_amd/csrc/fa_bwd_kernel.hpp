@@ -52,6 +52,7 @@ struct BwdParams {
                  // wave of a dQ work-group finds its block (rows past Nq hold zeros)
   int n_tiles;   // work-group tiles along the sequence: ceil(Nk / 128) for dK/dV, ceil(Nq / 128) for dQ
   int total_wg;
+  int ilv;       // (b, hkv) groups whose tiles are interleaved longest first (1, 2 or 4)
   float c;       // scale * log2(e)
   float scale;
   // optional byte mask (kernels built with AM), as in the forward's Params: nonzero hides key j
@@ -262,8 +263,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   const int Nq = p.Nq, Nk = p.Nk, G = p.group;
 
   const int L = xcd_remap(blockIdx.x, p.total_wg);
-  const int bk = L / p.n_tiles;  // b * Hkv + hkv
-  const int kt = L - bk * p.n_tiles;
+  // key tiles in order (the first ones see the most queries under a causal band), ilv (b, hkv)
+  // groups interleaved
+  const int per_blk = p.ilv * p.n_tiles;
+  const int blk = L / per_blk;
+  const int r0 = L - blk * per_blk;
+  const int kt = r0 / p.ilv;
+  const int bk = blk * p.ilv + (r0 - kt * p.ilv);  // b * Hkv + hkv
   const int b = bk / p.Hkv, hkv = bk - b * p.Hkv;
   const int k0 = kt * 32 * NW, k0w = k0 + 32 * wave;
 
@@ -512,9 +518,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   // (b, hkv) groups with the G sibling query heads side by side, longest Q-tiles first
   const int L = xcd_remap(blockIdx.x, p.total_wg);
   const int per_kv = p.n_tiles * G;
-  const int bk = L / per_kv;
-  const int r0 = L - bk * per_kv;
-  const int t_ord = r0 / G, g = r0 - t_ord * G;
+  const int per_blk = p.ilv * per_kv;  // ilv (b, hkv) groups interleaved, as in the forward
+  const int blk = L / per_blk;
+  const int r0 = L - blk * per_blk;
+  const int t_ord = r0 / (p.ilv * G);
+  const int r1 = r0 - t_ord * (p.ilv * G);
+  const int sub = r1 / G, g = r1 - sub * G;
+  const int bk = blk * p.ilv + sub;
   const int t = BAND ? (p.n_tiles - 1 - t_ord) : t_ord;
   const int b = bk / p.Hkv, hkv = bk - b * p.Hkv, hq = hkv * G + g;
   const int64_t head = (int64_t)b * p.Hq + hq;

@@ -189,6 +189,17 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   p.nsplit = ns;
   p.kchunk = kc;
   p.total_wg = (int)(grid * ns);
+  // Where Q-tile lengths vary widely (causal-like bands: no left edge, and masked calls, whose
+  // hulls differ), interleave the Q-tiles of up to 4 (b, hkv) groups, longest first, so that
+  // no group's long tiles start near the end of the grid; the count must divide the groups so
+  // that every block is whole. Measured on MI355X: causal d = 64 N = 4096 4.5% faster, N = 8192
+  // 3.2%, a document mask 1.3%, GQA causal unchanged; a sliding window (near-equal lengths)
+  // 2.4% slower, so it keeps one group at a time.
+  {
+    const bool varied = (p.left == kUnlimited && p.right != kUnlimited) || am;
+    const int64_t groups = B * Hkv;
+    p.ilv = !varied ? 1 : groups % 4 == 0 ? 4 : groups % 2 == 0 ? 2 : 1;
+  }
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   char* const wsb = reinterpret_cast<char*>(workspace);
   int2* const hull = am ? reinterpret_cast<int2*>(wsb + ml.hull_off) : nullptr;

@@ -122,6 +122,7 @@ struct Params {
   int nsplit;    // key chunks per Q-tile (1: none); chunk s covers keys [s*kchunk, (s+1)*kchunk)
   int kchunk;    // keys per chunk, a multiple of 64 (every key-tile size)
   int total_wg;  // B * Hq * n_qtiles * nsplit
+  int ilv;       // (b, hkv) groups whose Q-tiles are interleaved longest first (1, 2 or 4)
   float c;       // scale * log2(e)
   // optional mask (kernels built with AM), as fa_mask_prep_kernel leaves it: one bit per
   // (query, key), set where the key is hidden, in rows of am_nw 32-bit words; the (b, hq)
@@ -324,11 +325,17 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const int split = LS % p.nsplit;  // the key chunk (0 when keys are not split)
   const int L = LS / p.nsplit;
   const int G = p.group;
+  // With bands, Q-tiles differ in length: ilv consecutive (b, hkv) groups are taken together,
+  // longest Q-tiles of all of them first, so that no group's long tiles start near the end.
   const int per_kv = p.n_qtiles * G;
-  const int bk = L / per_kv;  // b * Hkv + hkv
-  const int r0 = L - bk * per_kv;
-  const int t_ord = r0 / G;
-  const int g = r0 - t_ord * G;
+  const int per_blk = p.ilv * per_kv;
+  const int blk = L / per_blk;
+  const int r0 = L - blk * per_blk;
+  const int t_ord = r0 / (p.ilv * G);
+  const int r1 = r0 - t_ord * (p.ilv * G);
+  const int sub = r1 / G;
+  const int g = r1 - sub * G;
+  const int bk = blk * p.ilv + sub;  // b * Hkv + hkv
   const int t = BAND ? (p.n_qtiles - 1 - t_ord) : t_ord;
   const int b = bk / p.Hkv;
   const int hkv = bk - b * p.Hkv;
