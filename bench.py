@@ -48,11 +48,19 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_114_amd", "csrc", f)
                   for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the forward kernel's sources with comments and blank lines removed, so that a
+    change to the code (not to its comments) marks the recorded counters stale."""
+    import re
+
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for p in sources or KERNEL_SOURCES:
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 
