@@ -45,7 +45,7 @@ DEFAULT_WORKLOAD = "gqa_causal_b4_hq32_hkv8_n8192_d128_bf16"
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, fp16 / bf16
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_hbm_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_114_amd", "csrc", f)
-                  for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip")]
+                  for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip", "fa_status.hpp")]
 
 
 def kernel_source_hash(sources=None) -> str:

@@ -138,15 +138,7 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   p.ws_blk = (int)ws_blk;
   p.n_tiles = 0;
   p.total_wg = 0;
-  {
-    // interleave the tiles of up to 4 (b, hkv) groups where their lengths vary widely, under
-    // the forward's rule (causal-like bands and masks; the groups' K and V within 4 MiB)
-    const bool varied = (p.left == kUnlimited && p.right != kUnlimited) || am;
-    const int64_t groups = B * Hkv, kv_bytes = 2 * Nk * d * 2;
-    p.ilv = 1;
-    for (int ilv = 4; varied && ilv > 1 && p.ilv == 1; ilv /= 2)
-      if (groups % ilv == 0 && ilv * kv_bytes <= ((int64_t)4 << 20)) p.ilv = ilv;
-  }
+  p.ilv = fa::interleave_groups(p.left, p.right, kUnlimited, am, B * Hkv, Nk, d);
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   p.scale = scale;
   p.am = static_cast<const unsigned char*>(mask.data);

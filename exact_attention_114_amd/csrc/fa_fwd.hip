@@ -132,23 +132,6 @@ struct MaskArg {
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
 };
 
-// Where Q-tile lengths vary widely (causal-like bands: no left edge, and masked calls, whose
-// hulls differ), the Q-tiles of up to 4 (b, hkv) groups are interleaved, longest first, so that
-// no group's long tiles start near the end of the grid. The groups taken together must keep
-// their K and V within one XCD's 4 MiB L2 (more streams them from HBM again: 2.7x the reads on
-// the GQA workload, 4 MiB per group), and their count must divide the groups so that every
-// block is whole. Measured on MI355X against one group at a time: causal d = 64 N = 4096 4.7%
-// faster (4 groups), N = 8192 1.9% (2 groups); a sliding window (near-equal lengths) was 2.4%
-// slower interleaved and keeps one group.
-int interleave_groups(int left, int right, bool masked, int64_t groups, int64_t Nk, int64_t d) {
-  const bool varied = (left == kUnlimited && right != kUnlimited) || masked;
-  if (!varied) return 1;
-  const int64_t kv_bytes = 2 * Nk * d * 2;  // K and V of one (b, hkv) in 16-bit
-  for (int ilv = 4; ilv > 1; ilv /= 2)
-    if (groups % ilv == 0 && ilv * kv_bytes <= ((int64_t)4 << 20)) return ilv;
-  return 1;
-}
-
 // Every forward entry point: validation, the split plan (n_splits = 1: never split; workspace
 // is then unused unless there is a mask), the mask hull, the attention kernel and, with split
 // keys, the merge.
@@ -206,7 +189,7 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   p.nsplit = ns;
   p.kchunk = kc;
   p.total_wg = (int)(grid * ns);
-  p.ilv = interleave_groups(p.left, p.right, am, B * Hkv, Nk, d);
+  p.ilv = fa::interleave_groups(p.left, p.right, kUnlimited, am, B * Hkv, Nk, d);
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   char* const wsb = reinterpret_cast<char*>(workspace);
   int2* const hull = am ? reinterpret_cast<int2*>(wsb + ml.hull_off) : nullptr;
