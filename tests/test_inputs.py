@@ -76,3 +76,21 @@ def test_chunk_workload_shapes():
     assert w.q_shape() == (1, 32, 512, 128) and w.kv_shape() == (1, 8, 32768, 128)
     qkv = I.draw_qkv(1, 2, 1, 8, 4, I.BF16, 5, Nk=24)
     assert qkv.q.shape == (1, 2, 8, 4) and qkv.k.shape == (1, 1, 24, 4) and qkv.v.shape == (1, 1, 24, 4)
+
+
+def test_document_lengths_and_mask():
+    """Packed documents: lengths drawn in [min, max] (the last one cut), summing to N per
+    sequence, reproducible from the seed; the mask is block diagonal over them (0 inside a
+    document, 1 across documents) and shared by the heads."""
+    lens = I.document_lengths(3, 1000, 17, 100, 400)
+    assert lens == I.document_lengths(3, 1000, 17, 100, 400)
+    assert lens != I.document_lengths(3, 1000, 18, 100, 400)
+    for row in lens:
+        assert sum(row) == 1000
+        assert all(100 <= n <= 400 for n in row[:-1]) and 1 <= row[-1] <= 400
+    m = I.document_mask(lens, 1000)
+    assert m.shape == (3, 1, 1000, 1000) and m.dtype == np.uint8
+    for b, row in enumerate(lens):
+        doc = np.repeat(np.arange(len(row)), row)  # document of each position
+        expect = (doc[:, None] != doc[None, :]).astype(np.uint8)
+        assert np.array_equal(m[b, 0], expect)
