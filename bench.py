@@ -177,8 +177,10 @@ def bench_mask(w, kind: str):
 BWD_METRIC = "attention bwd TFLOP/s (10·B·H·N²·d, causal halved) and % of MFMA peak, 1 GPU"
 
 
-def time_gpu_bwd(w, steps: int, warmup: int):
-    """Seconds of wall time for `steps` fa_bwd calls, and the HIP-event average per call."""
+def time_gpu_bwd(w, steps: int, warmup: int, mask=None):
+    """Seconds of wall time for `steps` fa_bwd calls, and the HIP-event average per call.
+    mask: an optional uint8 [B or 1, Hq or 1, N, Nk] array, passed to the forward that makes O
+    and LSE and to fa_bwd_mask."""
     import torch
 
     import exact_attention_114_amd as fa
@@ -190,15 +192,22 @@ def time_gpu_bwd(w, steps: int, warmup: int):
     q, k, v = (to_device(x, w.dtype, dev) for x in (qkv.q, qkv.k, qkv.v))
     del qkv
     dout = to_device(I.draw_dout(w.B, w.Hq, w.N, w.d, w.dtype, w.seed + 1000), w.dtype, dev)
-    o, lse = fa.fwd(q, k, v, scale=w.scale, window=w.band)
-    ws = torch.empty(binding.bwd_workspace_bytes(w.B, w.Hq, w.N, w.d), dtype=torch.uint8, device=dev)
+    tm = None if mask is None else torch.from_numpy(mask).to(dev)
+    o, lse = fa.fwd(q, k, v, scale=w.scale, window=w.band, mask=tm)
+    if tm is None:
+        ws_bytes = binding.bwd_workspace_bytes(w.B, w.Hq, w.N, w.d)
+    else:
+        ws_bytes = binding.bwd_mask_workspace_bytes(w.B, w.Hq, w.N, w.nk, w.d, int(mask.shape[0] > 1),
+                                                    int(mask.shape[1] > 1))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     grads = (torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev),
              torch.empty((w.B, w.Hkv, w.nk, w.d), dtype=torch.float32, device=dev),
              torch.empty((w.B, w.Hkv, w.nk, w.d), dtype=torch.float32, device=dev))
     stream = torch.cuda.current_stream(dev)
 
     def call():
-        fa.bwd(q, k, v, o, lse, dout, scale=w.scale, window=w.band, workspace=ws, grads=grads, stream=stream)
+        fa.bwd(q, k, v, o, lse, dout, scale=w.scale, window=w.band, workspace=ws, grads=grads, mask=tm,
+               stream=stream)
 
     for _ in range(warmup):
         call()
@@ -225,12 +234,13 @@ def bwd_algorithmic_bytes(w) -> float:
 
 
 def bwd_line(w, args):
-    wall, ms = time_gpu_bwd(w, args.steps, args.warmup)
-    flops = 2.5 * w.flops  # five products of the forward's size: S, dP, dV, dK, dQ
+    mask, fwd_flops, doc_lens = (None, w.flops, None) if not args.mask else bench_mask(w, args.mask)
+    wall, ms = time_gpu_bwd(w, args.steps, args.warmup, mask)
+    flops = 2.5 * fwd_flops  # five products of the forward's size: S, dP, dV, dK, dQ
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    return {
+    line = {
         "metric": BWD_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
@@ -244,8 +254,13 @@ def bwd_line(w, args):
                      "frac": round(achieved / peak, 4), "traffic": None,
                      "algorithmic_hbm_bytes": bwd_algorithmic_bytes(w), "call_ms": round(ms, 5),
                      "note": "achieved = algorithmic FLOP / HIP-event time of the whole fa_bwd call "
-                             "(its three kernels); per-kernel times are in the rocprofv3 summary"},
+                             "(its kernels); per-kernel times are in the rocprofv3 summary"},
     }
+    if mask is not None:
+        line["config"]["mask"] = {"kind": args.mask, "shape": list(mask.shape),
+                                  "documents_per_sequence": [len(r) for r in doc_lens],
+                                  "visible_fraction": round(fwd_flops / w.flops, 5)}
+    return line
 
 
 COPY_BYTES = 64 * 1024 * 1024 * 4  # the calibration copy reads and writes this many bytes
