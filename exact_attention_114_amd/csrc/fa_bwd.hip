@@ -158,6 +158,10 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   p.flags_nq = (int)ml.nq;
   p.flags_sh = ml.planes_h > 1 ? ml.nkt * ml.nq : 0;
   p.flags_sb = ml.planes_b > 1 ? ml.planes_h * ml.nkt * ml.nq : 0;
+  p.am_cbits = am ? reinterpret_cast<const unsigned*>(wsb + ml.cbits_off) : nullptr;
+  p.cbits_nqb = (int)ml.nqb;
+  p.cbits_sh = ml.planes_h > 1 ? Nk * ml.nqb : 0;
+  p.cbits_sb = ml.planes_b > 1 ? ml.planes_h * Nk * ml.nqb : 0;
 
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const int64_t prep_rows = B * Hq * ws_blk * 32;

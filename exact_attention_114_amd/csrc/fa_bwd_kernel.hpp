@@ -72,6 +72,11 @@ struct BwdParams {
   const unsigned char* am_flags;  // plane (b, hq) at am_flags + b*flags_sb + hq*flags_sh: [kt][t]
   long long flags_sb, flags_sh;
   int flags_nq;                   // Q-tiles per row of flags
+  // the mask as column words (dK/dV): plane (b, hq) at am_cbits + b*cbits_sb + hq*cbits_sh,
+  // word [j][qb] with bit r set where key j is hidden from query 32 qb + r
+  const unsigned* am_cbits;
+  long long cbits_sb, cbits_sh;
+  int cbits_nqb;                  // 32-row query blocks per key
 };
 
 // One LDS swizzle for tiles that are read both as rows (ds_read_b128: 16 consecutive rows at one
@@ -251,11 +256,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   __shared__ __attribute__((aligned(256))) float sW1[64];
   constexpr bool VL = bwd_v_in_lds(D);
   __shared__ __attribute__((aligned(1024))) char sV[VL ? NW * TB : 16];
-  // mask tiles: 32 query rows x the work-group's 32*NW keys, one byte each, double-buffered
   static_assert(!AM || BAND, "the masked kernels are built on the banded ones");
-  constexpr int MROW = 32 * NW, MTB = 32 * MROW;
-  __shared__ __attribute__((aligned(1024))) char sM0[AM ? MTB : 16];
-  __shared__ __attribute__((aligned(1024))) char sM1[AM ? MTB : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -350,36 +351,23 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     }
   };
 
-  // Mask tile DMA (4-byte loads): wave w fills rows [8w, 8w + 8) of the 32-row tile, two rows
-  // of MROW bytes per instruction; lane l writes row 8w + 2n + l/32, bytes 4(l%32) .. +3. Its
-  // offset within the instruction's rows is loop invariant; the instruction's first row goes into
-  // the descriptor base. Bytes past the head's plane read as zero; bytes of keys past Nk or rows
-  // past Nq only meet scores whose results are never stored (or multiply zero rows of dO).
-  constexpr int MRPW = 32 / NW;               // mask rows per wave
-  constexpr int MNI = MRPW * MROW / 256;      // 4-byte DMA instructions per wave per tile
-  static_assert(MROW == 128 && MNI * 256 == MRPW * MROW, "two 128-byte rows per instruction");
-  auto dma_mask = [&](int64_t head, int qb, lds_char* dm_) {
-    const int ln = lane_id_here();
-    const int am_off = (ln >> 5) * p.am_ld + 4 * (ln & 31);
-    const int64_t hb = head / p.Hq, hh = head - hb * p.Hq;
-    const unsigned char* plane = p.am + hb * p.am_sb + hh * p.am_sh;
-    const int64_t plane_bytes = (int64_t)Nq * p.am_ld;
-#pragma unroll
-    for (int n = 0; n < MNI; ++n) {
-      const int64_t first = (int64_t)(qb * 32 + MRPW * wave + 2 * n) * p.am_ld + k0;
-      const int64_t left = plane_bytes - first;
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(plane + (left > 0 ? first : 0)), (short)0, left > 0 ? (int)left : 0, kBufferWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dm_ + (MRPW * wave + 2 * n) * MROW), 4, am_off, 0, 0, 0);
-    }
+  // The lane's mask column word for iteration it (query block qb of head g, its key), loaded
+  // one iteration ahead; the key's offset is formed from an opaque lane id where it is used (no
+  // register holds it across the loop). Keys past Nk read the last key's word: their results
+  // are never stored.
+  unsigned mw = 0u, mw_next = 0u;
+  auto load_mw = [&](int it) {
+    const int g = it / nqb, qb = qb0 + (it - g * nqb);
+    const int key = min(k0w + (lane_id_here() & 31), Nk - 1);
+    mw_next = p.am_cbits[b * p.cbits_sb + (hkv * G + g) * p.cbits_sh + (int64_t)key * p.cbits_nqb + qb];
   };
-  auto issue_loads = [&](int it, lds_char* dq_, lds_char* dg_, float* dw_, lds_char* dm_) {
+  auto issue_loads = [&](int it, lds_char* dq_, lds_char* dg_, float* dw_) {
     const int g = it / nqb, qb = qb0 + (it - g * nqb);
     const int64_t head = (int64_t)b * p.Hq + hkv * G + g;
     dma_rows<D, NW>((const char*)((const T*)p.q + head * Nq * D), Nq, qb * 32, dq_, wave, ld_off);
     dma_rows<D, NW>((const char*)((const T*)p.dout + head * Nq * D), Nq, qb * 32, dg_, wave, ld_off);
     if constexpr (AM)
-      if (!mask_free(it)) dma_mask(head, qb, dm_);
+      if (!mask_free(it)) load_mw(it);
     if (wave == 0) {
       void* wp = (void*)(p.ws + (head * p.ws_blk + qb) * 64);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(wp, (short)0, 256, kBufferWord3);
@@ -395,7 +383,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   }
   const float c = p.c;
 
-  if (n_it > 0) issue_loads(0, (lds_char*)sQ0, (lds_char*)sG0, sW0, (lds_char*)sM0);
+  if (n_it > 0) issue_loads(0, (lds_char*)sQ0, (lds_char*)sG0, sW0);
   for (int it = 0; it < n_it; ++it) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -403,10 +391,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     const lds_char* tq = (const lds_char*)(odd ? sQ1 : sQ0);
     const lds_char* tg = (const lds_char*)(odd ? sG1 : sG0);
     const float* tw = odd ? sW1 : sW0;
-    const lds_char* tm = (const lds_char*)(odd ? sM1 : sM0);
+    if constexpr (AM) mw = mw_next;  // loaded during the previous iteration (or before the loop)
     if (it + 1 < n_it)
-      issue_loads(it + 1, (lds_char*)(odd ? sQ0 : sQ1), (lds_char*)(odd ? sG0 : sG1), odd ? sW0 : sW1,
-                  (lds_char*)(odd ? sM0 : sM1));
+      issue_loads(it + 1, (lds_char*)(odd ? sQ0 : sQ1), (lds_char*)(odd ? sG0 : sG1), odd ? sW0 : sW1);
     const int qb = qb0 + (it % nqb);
     const int q0 = qb * 32;
     const bool mfree = mask_free(it);
@@ -448,11 +435,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
         }
         if constexpr (AM) {
           if (!mfree) {
-            // mask bytes of queries 8g4 + 4h + 2r2 (+1) and this lane's key
-            const int ln = lane_id_here();
-            const lds_char* mp = tm + (8 * g4 + 2 * r2) * MROW + 32 * wave + (ln >> 5) * (4 * MROW) + (ln & 31);
-            s0 = *(const lds_uchar*)mp != 0 ? -__builtin_inff() : s0;
-            s1 = *(const lds_uchar*)(mp + MROW) != 0 ? -__builtin_inff() : s1;
+            // the bits of queries 8g4 + 4h + 2r2 (+1) in the lane's column word
+            const unsigned x = mw >> (4 * h + 8 * g4 + 2 * r2);
+            s0 = (x & 1u) != 0u ? -__builtin_inff() : s0;
+            s1 = (x & 2u) != 0u ? -__builtin_inff() : s1;
           }
         }
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a[2 * r2]));

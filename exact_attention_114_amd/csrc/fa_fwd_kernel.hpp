@@ -818,13 +818,16 @@ struct PrepParams {
   unsigned char* flags;      // optional (nullptr: not written): [planes][n_ktiles][n_qtiles]: 0
                              // where no row of Q-tile t may see a key of 128-key tile kt, 2 where
                              // the mask hides none of the block's pairs inside the band, else 1
+  unsigned* cbits;           // kernels built with COLS: [planes][Nk][nqb] column words, bit r of
+                             // word (j, qb) set where key j is hidden from query 32 qb + r
   int planes_h;              // Hq or 1 (planes are numbered pb * planes_h + ph)
   int Nq, Nk, off, left, right;
-  int n_qtiles, nch, nw, n_ktiles;
+  int n_qtiles, nch, nw, n_ktiles, nqb;
 };
 
-template <int BM>
+template <int BM, bool COLS>
 __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
+  static_assert(BM % 32 == 0, "whole 32-row query blocks per tile");
   int wg = blockIdx.x;
   const int ch = wg % p.nch;
   wg /= p.nch;
@@ -846,6 +849,10 @@ __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
   unsigned* const bcol = p.bits + (int64_t)plane * p.Nq * p.nw + wi;
   unsigned vis = 0u;  // bits (8b + sl) of this thread's keys that some row may see
   unsigned hidm = 0u;  // bits of its keys below Nk that the mask hides from some row it read
+  // COLS: the column words of this thread's four keys for the current 32-row block, all hidden
+  // until a row shows a key visible (rows past q1, or whose band misses the key, stay hidden)
+  unsigned cw[4] = {~0u, ~0u, ~0u, ~0u};
+  const unsigned vbytes = nk >= 4 ? 0x80808080u : nk <= 0 ? 0u : (0x80808080u >> (8 * (4 - nk)));  // below Nk
   for (int r0 = q0; r0 <= q1; r0 += 16) {
     unsigned w[16];
     bool need[16];
@@ -862,8 +869,7 @@ __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
 #pragma unroll
       for (int u = 0; u < 16; ++u)
         if (store && r0 + u <= q1) bcol[(int64_t)(r0 + u) * p.nw] = 0xffffffffu;
-      continue;
-    }
+    } else {
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       // bit 7 of each byte: set when the byte is nonzero (its low seven bits plus 0x7f carry
@@ -879,6 +885,24 @@ __global__ __launch_bounds__(256) void fa_mask_prep_kernel(const PrepParams p) {
       word |= (unsigned)__builtin_amdgcn_mov_dpp((int)word, 0x4E, 0xF, 0xF, false);
       word |= (unsigned)__builtin_amdgcn_mov_dpp((int)word, 0x141, 0xF, 0xF, false);
       if (store && r0 + u <= q1) bcol[(int64_t)(r0 + u) * p.nw] = word;
+      if constexpr (COLS) {
+        // bit 8b + 7 of `seen`: key + b is visible to this row
+        const unsigned seen = need[u] ? ~y & vbytes : 0u;
+        const unsigned rb = 1u << ((r0 + u) & 31);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cw[b] = (seen >> (8 * b + 7)) & 1u ? cw[b] & ~rb : cw[b];
+      }
+    }
+    }
+    if constexpr (COLS) {
+      // a 32-row block ends with this batch: store the four keys' column words
+      if ((r0 & 31) == 16 || r0 + 16 > q1) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b < nk) p.cbits[((int64_t)plane * p.Nk + key + b) * p.nqb + (r0 >> 5)] = cw[b];
+          cw[b] = ~0u;
+        }
+      }
     }
   }
   int kmin = 0x7fffffff, kmax = -1;

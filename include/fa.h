@@ -279,9 +279,10 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
  *   workspace  device pointer to fa_bwd_mask_workspace_bytes(..., mask_b_stride,
  *              mask_h_stride) bytes (the row statistics, then the mask packed
  *              to bits and its summaries), 16-byte aligned, owned by the caller
- * A pre-pass reads the mask once, as in fa_fwd_mask; the dQ kernel then visits
- * only the key tiles inside each Q-tile's hull, and the dK/dV kernel only the
- * Q-tiles whose block with its key tile has a visible pair.
+ * A pre-pass reads the mask once, as in fa_fwd_mask, and also writes it by key
+ * columns; the dQ kernel then visits only the key tiles inside each Q-tile's
+ * hull, and the dK/dV kernel only the Q-tiles whose block with its key tile has
+ * a visible pair, reading one column word per key and 32-query block.
  * Other arguments, errors and execution as fa_bwd_ex; a NULL mask is
  * FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN.
  */
@@ -298,7 +299,8 @@ fa_status fa_bwd_mask(const void* q, const void* k, const void* v, const void* o
  * with these batch and head strides (0: shared along that axis): the row
  * statistics of fa_bwd_workspace_bytes(B, Hq, Nq, d), then, each at a 256-byte
  * boundary, the key hull and the packed mask as for fa_fwd_mask_workspace_bytes,
- * then P x ceil(Nk / 128) x ceil(Nq / 128) flag bytes (P mask planes).
+ * then P x ceil(Nk / 128) x ceil(Nq / 128) flag bytes, then P x Nk x ceil(Nq / 32)
+ * words of 32 bits (the mask by key columns) (P mask planes).
  * 0 when the arguments are invalid. Makes no HIP call.
  */
 size_t fa_bwd_mask_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d,

@@ -315,14 +315,16 @@ def test_mask_workspace_bytes():
 
 
 def test_bwd_mask_workspace_bytes():
-    # the row statistics (fa_bwd_workspace_bytes), then at 256-byte boundaries the hull, the bits
-    # and a flag byte per (plane, 128-key tile, 128-row Q-tile)
-    assert bnd.bwd_mask_workspace_bytes(1, 2, 64, 80, 64, 0, 0) == 3072 + 1
+    # the row statistics (fa_bwd_workspace_bytes), then at 256-byte boundaries the hull, the bits,
+    # a flag byte per (plane, 128-key tile, 128-row Q-tile) and a column word per (plane, key,
+    # 32-row query block)
+    assert bnd.bwd_mask_workspace_bytes(1, 2, 64, 80, 64, 0, 0) == 3328 + 80 * 2 * 4
     assert bnd.bwd_workspace_bytes(1, 2, 64, 64) == 2048
     base = bnd.bwd_workspace_bytes(4, 32, 8192, 128)
     hull = 4 * 64 * 8 * 8
     bits = 4 * 8192 * 256 * 4
-    assert bnd.bwd_mask_workspace_bytes(4, 32, 8192, 8192, 128, 1, 0) == base + hull + bits + 4 * 64 * 64
+    cols = 4 * 8192 * 256 * 4
+    assert bnd.bwd_mask_workspace_bytes(4, 32, 8192, 8192, 128, 1, 0) == base + hull + bits + 4 * 64 * 64 + cols
     assert bnd.bwd_mask_workspace_bytes(1, 2, 64, 80, 64, -4, 0) == 0
     assert bnd.bwd_mask_workspace_bytes(1, 2, 64, 80, 80, 0, 0) == 0
 
