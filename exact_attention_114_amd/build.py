@@ -9,6 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip")]
 DEPENDS = [os.path.join(HERE, "csrc", "fa_fwd_kernel.hpp"), os.path.join(HERE, "csrc", "fa_bwd_kernel.hpp"),
            os.path.join(HERE, "csrc", "fa_status.hpp"), os.path.join(HERE, "csrc", "fa_mask.hpp"),
+           os.path.join(HERE, "csrc", "fa_mask_kernel.hpp"),
            os.path.join(os.path.dirname(HERE), "include", "fa.h")]
 OUTPUT = os.path.join(HERE, "libfa.so")
 ARCH = "gfx950"

@@ -6,7 +6,7 @@
 
 #include <cstdint>
 
-#include "fa_fwd_kernel.hpp"
+#include "fa_mask_kernel.hpp"
 
 namespace fa {
 
