@@ -18,7 +18,8 @@ Contents
                math.fsum) for tiny shapes.
   backward.py  the gradients dQ, dK, dV of that definition (the chain rule
                written out in fp64, P recomputed from the saved LSE), summed
-               over each K/V head's query-head group.
+               over each K/V head's query-head group; the magnitude sums of
+               their terms and the parity bar stated from them.
   attention.py and backward.py also hold the banded forms: a sliding window
                (left and right edges) with separate query and key lengths.
   pool.py      a process pool over (batch, head) units for big shapes.
@@ -29,9 +30,10 @@ All functions are pinned by tests that do not re-type them (closed forms,
 invariants, library routines, brute force); none is "parity unpinned".
 """
 from .softmax import safe_softmax, online_softmax, logsumexp  # noqa: F401
-from .attention import (attention_fp64, head_attention_fp64, attention_probs_fp64,  # noqa: F401
+from .attention import (attention_fp64, head_attention_fp64,  # noqa: F401
                         tiled_kv_outer_normalised, tiled_q_outer_deferred, kv_head_of,
                         band_visible, head_attention_band_fp64, attention_band_fp64)
 from .brute import attention_brute  # noqa: F401
 from .backward import (attention_bwd_fp64, head_attention_bwd_fp64,  # noqa: F401
-                       attention_bwd_band_fp64, head_attention_bwd_band_fp64)
+                       attention_bwd_band_fp64, head_attention_bwd_band_fp64,
+                       head_attention_bwd_magnitude_fp64, bwd_parity_bar)

@@ -36,7 +36,6 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .softmax import safe_softmax
 
 ROW_BLOCK = 1024  # query rows per block in the definition (bounds memory only)
 
@@ -106,14 +105,6 @@ def attention_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
             hk = kv_head_of(hq, Hq, Hkv)
             O[b, hq], LSE[b, hq] = head_attention_fp64(q[b, hq], k[b, hk], v[b, hk], scale, causal)
     return O, LSE
-
-
-def attention_probs_fp64(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
-    """The probability matrix P of one head (tiny shapes only; [n, N])."""
-    S = _scores(np.asarray(q, np.float64), np.asarray(k, np.float64), scale)
-    if causal:
-        S = _mask_causal(S, np.arange(S.shape[0]), np.arange(S.shape[1]))
-    return safe_softmax(S, axis=1)
 
 
 def tiled_kv_outer_normalised(q, k, v, scale: float, causal: bool, block_q: int, block_kv: int):

@@ -95,47 +95,38 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     return dq, dk, dv
 
 
-def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-                                  o_used: np.ndarray, scale: float, causal: bool, u: float,
-                                  e32: float = 2.0 ** -24, band: Optional[Tuple] = None,
-                                  hidden: Optional[np.ndarray] = None
-                                  ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """First-order elementwise error bounds (Bq [n,d], Bk [N,d], Bv [N,d]) for one head's
-    gradients computed the way a tiled kernel does: S, dP and D accumulated in fp32 (unit
-    roundoff ``e32``), D formed from ``o_used`` (the O it is given, e.g. stored in fp32 or in
-    16 bits), P = exp(S - LSE) in fp32, P and dS rounded to a 16-bit type of unit roundoff ``u``
-    before the products that consume them, and those products accumulated in fp32. The test
-    suite sizes its parity bar from these; they are not part of the result.
-
-    With d the head dimension, n the rows and N the keys, per element:
-      rho_ij = d e32 s (|Q||K|^T)_ij + 4 e32              relative error of P (S, fma, exp)
-      eta_ij = d e32 ((|dO||V|^T)_ij + sum_c |dO_ic O_ic|) + |sum_c dO_ic (O_used - O)_ic|
-                                                           absolute error of dP - D
-      Bv = sum_i (u + rho_ij + n e32) P_ij |dO_ic|
-      Bq = s sum_j [(u + rho_ij + N e32) |dS_ij| + P_ij eta_ij] |K_jc|
-      Bk = s sum_i [(u + rho_ij + n e32) |dS_ij| + P_ij eta_ij] |Q_ic|
-    (a product sum_k a_k b_k whose factor a_k carries a relative error e moves by at most
-    e sum_k |a_k b_k|; an fp32 sum of m terms by at most m e32 times the sum of magnitudes).
-    ``band`` = (left, right, off) replaces ``causal`` by the band of ``attention.band_visible``,
-    and ``hidden`` [n, N] (with a band) hides further keys where nonzero.
+def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                                      scale: float, causal: bool, band: Optional[Tuple] = None,
+                                      hidden: Optional[np.ndarray] = None
+                                      ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Magnitude sums (Mq [n,d], Mk [N,d], Mv [N,d]) of one head's gradients: each gradient
+    element written out as a sum of products of the inputs (Q, K, V, dO), the probabilities P
+    and the output O, with every term replaced by its magnitude. With A_ij = sum_c |dO_ic||V_jc|
+    (the terms of dP_ij) and E_i = sum_c |dO_ic O_ic| (the terms of D_i):
+      dV_jc = sum_i P_ij dO_ic                        Mv_jc = sum_i P_ij |dO_ic|
+      dQ_ic = s sum_j P_ij (dP_ij - D_i) K_jc         Mq_ic = s sum_j P_ij (A_ij + E_i) |K_jc|
+      dK_jc = s sum_i P_ij (dP_ij - D_i) Q_ic         Mk_jc = s sum_i P_ij (A_ij + E_i) |Q_ic|
+    (P >= 0, so |P| = P.) These sums measure how far roundings of relative size u inside any
+    evaluation of the chain rule can move each element: to first order by at most u per rounding
+    a term passes through, times M. They depend on the problem only, not on how an
+    implementation orders or tiles the sums. The test suite sizes its GPU bar from them; they are
+    not part of the result. ``band`` = (left, right, off) replaces ``causal`` by the band of
+    ``attention.band_visible``, and ``hidden`` [n, N] (with a band) hides further keys where
+    nonzero; hidden keys and rows that see no key have P = 0.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    o_used = np.asarray(o_used, dtype=np.float64)
     n, N = q.shape[0], k.shape[0]
-    d = q.shape[1]
     if band is None:
         O, lse = head_attention_fp64(q, k, v, scale, causal)
     else:
         O, lse = head_attention_band_fp64(q, k, v, scale, *band, hidden=hidden)
-    d_dev = np.abs(np.sum(do * (o_used - O), axis=1))
-    d_mag = np.sum(np.abs(do * O), axis=1)
-    bq = np.zeros(q.shape)
-    bk = np.zeros(k.shape)
-    bv = np.zeros(v.shape)
-    g_d = d * e32
+    E = np.sum(np.abs(do * O), axis=1)
+    mq = np.zeros(q.shape)
+    mk = np.zeros(k.shape)
+    mv = np.zeros(v.shape)
     for r0 in range(0, n, ROW_BLOCK):
         r1 = min(n, r0 + ROW_BLOCK)
         kend = N if (band is not None or not causal) else min(N, r1)
@@ -149,19 +140,39 @@ def head_attention_bwd_bound_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, d
                          np.exp(np.where(vis, S, 0.0) - np.where(seen, lse[r0:r1], 0.0)[:, None]), 0.0)
         else:
             if causal:
-                hidden = np.arange(kend)[None, :] > np.arange(r0, r1)[:, None]
-                S = np.where(hidden, -np.inf, S)
+                S = np.where(np.arange(kend)[None, :] > np.arange(r0, r1)[:, None], -np.inf, S)
             P = np.exp(S - lse[r0:r1, None])
-        dP = do[r0:r1] @ v[:kend].T
-        D = np.sum(P * dP, axis=1)
-        dS = np.abs(P * (dP - D[:, None]))
-        rho = g_d * scale * (np.abs(q[r0:r1]) @ np.abs(k[:kend]).T) + 4 * e32
-        eta = g_d * (np.abs(do[r0:r1]) @ np.abs(v[:kend]).T + d_mag[r0:r1, None]) + d_dev[r0:r1, None]
-        bv[:kend] += ((u + rho + n * e32) * P).T @ np.abs(do[r0:r1])
-        bq[r0:r1] = scale * (((u + rho + N * e32) * dS + P * eta) @ np.abs(k[:kend]))
-        bk[:kend] += scale * (((u + rho + n * e32) * dS + P * eta).T @ np.abs(q[r0:r1]))
-    return bq, bk, bv
+        A = np.abs(do[r0:r1]) @ np.abs(v[:kend]).T
+        W = P * (A + E[r0:r1, None])
+        mv[:kend] += P.T @ np.abs(do[r0:r1])
+        mq[r0:r1] = scale * (W @ np.abs(k[:kend]))
+        mk[:kend] += scale * (W.T @ np.abs(q[r0:r1]))
+    return mq, mk, mv
 
+
+# Unit roundoff of fp32, the precision of every sum and of the softmax statistics.
+E32 = 2.0 ** -24
+
+
+def bwd_parity_bar(m: np.ndarray, u: float, d: int, n_terms: int) -> np.ndarray:
+    """Elementwise bar |g - g_ref| <= (2u + (d + n_terms) e32) * M for a gradient computed with
+    16-bit operands in its products and fp32 everywhere else, M from
+    ``head_attention_bwd_magnitude_fp64``.
+
+    The precision is the method's, not one implementation's: the pages' kernels multiply
+    fp16/bf16 operands and accumulate in fp32, with fp32 softmax statistics (intelliparadigm
+    page, section 2.2: fp16/bf16 inputs with fp32 max and sum outputs; zyxy lecture, section 5:
+    the FA2 kernels run in fp16/bf16). A term of a gradient passes through at most two roundings
+    to the input type (unit roundoff u: 2^-11 for fp16, 2^-8 for bf16): its probability or
+    score-gradient factor as a product operand, and O when the caller stored it in 16 bits
+    (D then comes from that O). Its fp32 parts are a dot product over the head dimension d
+    (S, dP, D) and a sum over the n_terms terms of the element (keys per row for dQ, rows of
+    every query head of the group for dK and dV), each adding at most e32 per step. Every
+    term's relative error is therefore at most 2u + (d + n_terms) e32 to first order; the
+    second-order remainder (products of two of these) is below 2^-14 of the bar at the sizes
+    tested.
+    """
+    return (2.0 * u + (d + n_terms) * E32) * np.asarray(m, dtype=np.float64)
 
 
 def head_attention_bwd_band_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,

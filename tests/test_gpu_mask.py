@@ -246,14 +246,11 @@ def test_mask_errors_raise():
 
 # ---------------------------------------------------------------- gradients
 
-UNIT = {I.F16: 2.0 ** -11, I.BF16: 2.0 ** -8}
-
-
 def run_bwd(B, Hq, Hkv, Nq, Nk, d, dt, band, mask, seed):
-    """fa_bwd_mask against the fp64 gradients, within twice the first-order bound of the
-    oracle's error model (as the unmasked backward tests)."""
-    from oracle.attention import kv_head_of
-    from oracle.backward import attention_bwd_band_fp64, head_attention_bwd_bound_fp64
+    """fa_bwd_mask against the fp64 gradients, within the bar of the unmasked backward tests
+    (bwd_check.py)."""
+    import bwd_check
+    from oracle.backward import attention_bwd_band_fp64
 
     g = np.random.Generator(np.random.PCG64(seed))
     qb, kb, vb, dob = (I.to_bits(g.standard_normal(s, dtype=np.float32), dt)
@@ -270,22 +267,9 @@ def run_bwd(B, Hq, Hkv, Nq, Nk, d, dt, band, mask, seed):
     torch.cuda.synchronize()
     got = [t.cpu().numpy().astype(np.float64) for t in grads]
     ref = attention_bwd_band_fp64(q, k, v, do, sc, *band, mask=mask)
-    bq = np.empty(q.shape)
-    bk = np.zeros(k.shape)
-    bv = np.zeros(v.shape)
-    for b in range(B):
-        for h in range(Hq):
-            hk = kv_head_of(h, Hq, Hkv)
-            hid = mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]
-            x, y, z = head_attention_bwd_bound_fp64(q[b, h], k[b, hk], v[b, hk], do[b, h], o32[b, h].astype(np.float64),
-                                                    sc, False, UNIT[dt], band=(band[0], band[1], Nk - Nq), hidden=hid)
-            bq[b, h] = x
-            bk[b, hk] += y
-            bv[b, hk] += z
-    for name, gg, r, bb in zip(("dQ", "dK", "dV"), got, ref, (bq, bk, bv)):
-        assert np.isfinite(gg).all(), f"non-finite {name}"
-        ratio = (np.abs(gg - r) / np.maximum(2.0 * bb, 1e-300)).max()
-        assert ratio <= 1.0, f"{name} error reaches {ratio:.3f} of the bar"
+    mags = bwd_check.magnitudes(q, k, v, do, sc, band=band, mask=mask)
+    bwd_check.check(f"mask B={B} Hq={Hq} Nq={Nq} Nk={Nk} d={d} {dt} band={band}", got, ref, mags, dt, d, Nk,
+                    (Hq // Hkv) * Nq)
 
 
 @pytest.mark.parametrize("kind", ["random", "blocks", "padding"])

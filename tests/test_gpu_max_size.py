@@ -54,9 +54,10 @@ def test_largest_plane_d128_window_backward():
     """fa_bwd_ex at the same size. The gradients of the last 1024 query rows, and of the keys
     among the last 1024, depend only on those rows (each sees 257 keys, each key is seen by at
     most 257 rows): their O and LSE are set to the oracle's before the call, and dQ, dK, dV there
-    are checked against the oracle's gradients of that slice within twice the first-order bound
-    (as tests/test_gpu_bwd.py)."""
-    from oracle.backward import head_attention_bwd_band_fp64, head_attention_bwd_bound_fp64
+    are checked against the oracle's gradients of that slice within the backward bar
+    (bwd_check.py)."""
+    import bwd_check
+    from oracle.backward import head_attention_bwd_band_fp64, head_attention_bwd_magnitude_fp64
 
     d, dt, left, blk = 128, I.BF16, 256, 1024
     N = MAX_PLANE // d
@@ -82,11 +83,9 @@ def test_largest_plane_d128_window_backward():
     got = (dq[0, 0, r0:].cpu().numpy().astype(np.float64), dk[0, 0, r0:].cpu().numpy().astype(np.float64),
            dv[0, 0, r0:].cpu().numpy().astype(np.float64))
     gq, gk, gv = head_attention_bwd_band_fp64(qs, ks, vs, dos, sc, left, 0, off=r0 - k0)
-    bq, bk, bv = head_attention_bwd_bound_fp64(qs, ks, vs, dos, O_ref.astype(np.float32).astype(np.float64), sc,
-                                               False, 2.0 ** -8, band=(left, 0, r0 - k0))
+    mq, mk, mv = head_attention_bwd_magnitude_fp64(qs, ks, vs, dos, sc, False, band=(left, 0, r0 - k0))
     # keys k0 .. r0 - 1 are also seen by rows before r0: only keys from r0 on are complete here
-    for name, g, r, bb in (("dQ", got[0], gq, bq), ("dK", got[1], gk[left:], bk[left:]),
-                           ("dV", got[2], gv[left:], bv[left:])):
-        assert np.isfinite(g).all(), f"non-finite {name}"
-        ratio = (np.abs(g - r) / np.maximum(2.0 * bb, 1e-300)).max()
-        assert ratio <= 1.0, f"{name} error reaches {ratio:.3f} of the bar"
+    for name, g, r, m, n in (("dQ", got[0], gq, mq, left + 1), ("dK", got[1], gk[left:], mk[left:], left + 1),
+                             ("dV", got[2], gv[left:], mv[left:], left + 1)):
+        ratio = bwd_check.check_one("largest plane", name, g, r, m, dt, d, n)
+        print(f"[bar] largest plane {name}: worst error/bar {ratio:.4f}", flush=True)

@@ -16,7 +16,7 @@ import torch
 
 from oracle import attention_fp64, head_attention_fp64
 from oracle.attention import attention_band_fp64, head_attention_band_fp64
-from oracle.backward import attention_bwd_band_fp64, attention_bwd_fp64, head_attention_bwd_bound_fp64
+from oracle.backward import attention_bwd_band_fp64, attention_bwd_fp64, head_attention_bwd_magnitude_fp64
 
 
 def draw(B, Hq, Hkv, Nq, Nk, d, seed):
@@ -135,18 +135,15 @@ def test_rows_without_keys_have_zero_gradients():
     assert np.isfinite(O).all()
 
 
-def test_bound_helper_band_matches_causal_and_covers_empty_rows():
+def test_magnitudes_band_match_causal_and_cover_empty_rows():
     q, k, v, do = draw(1, 1, 1, 30, 30, 8, 51)
-    O, _ = head_attention_fp64(q[0, 0], k[0, 0], v[0, 0], 0.5, True)
-    a = head_attention_bwd_bound_fp64(q[0, 0], k[0, 0], v[0, 0], do[0, 0], O, 0.5, True, 2.0 ** -8)
-    b = head_attention_bwd_bound_fp64(q[0, 0], k[0, 0], v[0, 0], do[0, 0], O, 0.5, False, 2.0 ** -8,
-                                      band=(None, 0, 0))
+    a = head_attention_bwd_magnitude_fp64(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.5, True)
+    b = head_attention_bwd_magnitude_fp64(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.5, False, band=(None, 0, 0))
     for x, y in zip(a, b):
         np.testing.assert_allclose(y, x, rtol=1e-12, atol=0)
-    # Nq > Nk with the band (None, 0): rows 0..9 see no key, their dQ bound is 0 and all finite
+    # Nq > Nk with the band (None, 0): rows 0..9 see no key, their dQ magnitudes are 0 and all finite
     q, k, v, do = draw(1, 1, 1, 20, 10, 4, 52)
-    Ob, _ = head_attention_band_fp64(q[0, 0], k[0, 0], v[0, 0], 0.5, None, 0, off=-10)
-    bq, bk, bv = head_attention_bwd_bound_fp64(q[0, 0], k[0, 0], v[0, 0], do[0, 0], Ob, 0.5, False, 2.0 ** -8,
-                                               band=(None, 0, -10))
-    assert np.isfinite(bq).all() and np.isfinite(bk).all() and np.isfinite(bv).all()
-    assert (bq[:10] == 0).all()
+    mq, mk, mv = head_attention_bwd_magnitude_fp64(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.5, False,
+                                                   band=(None, 0, -10))
+    assert np.isfinite(mq).all() and np.isfinite(mk).all() and np.isfinite(mv).all()
+    assert (mq[:10] == 0).all()

@@ -18,7 +18,7 @@ import torch
 
 from oracle import attention_fp64
 from oracle.attention import attention_band_fp64, head_attention_fp64
-from oracle.backward import attention_bwd_band_fp64, head_attention_bwd_bound_fp64
+from oracle.backward import attention_bwd_band_fp64, head_attention_bwd_magnitude_fp64
 
 
 def draw(B, Hq, Hkv, Nq, Nk, d, seed):
@@ -126,8 +126,8 @@ def test_fully_hidden_rows():
     assert (O[0, 1, 3] == 0).all() and L[0, 1, 3] == -np.inf and np.isfinite(L[0, 0]).all()
     dq, dk, dv = attention_bwd_band_fp64(q, k, v, do, 0.5, None, None, mask=mask)
     assert (dq[0, 1, 3] == 0).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
-    bq, bk, bv = head_attention_bwd_bound_fp64(q[0, 1], k[0, 1], v[0, 1], do[0, 1], O[0, 1], 0.5, False,
-                                               2.0 ** -8, band=(None, None, 0), hidden=mask[0, 1])
+    bq, bk, bv = head_attention_bwd_magnitude_fp64(q[0, 1], k[0, 1], v[0, 1], do[0, 1], 0.5, False,
+                                                   band=(None, None, 0), hidden=mask[0, 1])
     assert (bq[3] == 0).all() and np.isfinite(bk).all() and np.isfinite(bv).all()
 
 
