@@ -34,11 +34,11 @@
 //      accumulator registers (packed to fp16/bf16 with round-to-nearest-even),
 //      A = V^T is read from the row-major V tile with ds_read_b64_tr_b16
 //      (gfx950's transposing LDS read), so V is never transposed in memory.
-//      Row sums are kept in fp32: l of the unrounded exponentials, for the LSE, and, with
-//      bf16 inputs, l~ of the rounded values that enter the MFMA (one v_dot2 per packed
-//      pair), which normalises O. The weights that multiply V then sum to one, so the
-//      rounding of a dominant weight (up to 2^-9 relative in bf16) cancels rather than
-//      scaling the row. With fp16 inputs (rounding 8 times finer) O is normalised by l.
+//      Row sums are kept in fp32: l of the unrounded exponentials, for the LSE, and l~ of
+//      the rounded values that enter the MFMA (one v_dot2 per packed pair), which
+//      normalises O. The weights that multiply V then sum to one, so the rounding of a
+//      dominant weight (up to 2^-9 relative in bf16, 2^-11 in fp16) cancels rather than
+//      scaling the row.
 //   5. Masks. Causal attention (intelliparadigm page, section 1.3: skip the masked half) is one
 //      case of a band: the operator on that page bounds a sliding window by pre_tokens and
 //      next_tokens (section 2.2), and its tiling takes separate query and key lengths (2.3).
@@ -284,8 +284,6 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
   constexpr int BM = 32 * NW;
   constexpr int BN = 32 * KB;
-  // O's normaliser: the sum of the rounded P values with bf16 inputs, the unrounded one with fp16
-  constexpr bool RSUM = BF16;
   constexpr int DP = lds_pitch(D);        // LDS row pitch (elements)
   constexpr int KCH = D / 8;              // 16-byte chunks per row in HBM
   constexpr int KCHP = DP / 8;            // 16-byte chunks per row in LDS
@@ -654,12 +652,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
           pcur[q >> 2][q & 3] = w;
           const float s2 = ex[e - 1] + ex[e];
           part[q & 1] = q < 2 ? s2 : part[q & 1] + s2;
-          if constexpr (RSUM) tile_rsum = E::sum2(w, q == 0 ? 0.f : tile_rsum);
+          tile_rsum = E::sum2(w, q == 0 ? 0.f : tile_rsum);
         }
       } else {
         tile_sum = part[0] + part[1];
         pin(tile_sum);
-        if constexpr (RSUM) pin(tile_rsum);
+        pin(tile_rsum);
       }
     };
 
@@ -763,14 +761,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     step(r + 1, E0, Y, Y, sA, sB, pB, pA);
   }
 
-  // ---- epilogue: O = acc / lr, LSE = ln2 * (m + log2 l). With bf16 inputs O is divided by the
-  // sum of the very values P V was formed with, so the weights that multiply V sum to one: the
-  // rounding of a dominant weight to bf16 (up to 2^-9 relative) then cancels instead of scaling
-  // the whole row. fp16 rounds 8 times finer, and there O takes the unrounded sum, which saves
-  // the pair sums of the rounded values. The LSE keeps the unrounded sum. A row that saw no key
-  // (a band can leave one empty) has both sums zero: O = 0 and LSE = -inf.
+  // ---- epilogue: O = acc / lr, LSE = ln2 * (m + log2 l). O is divided by the sum of the very
+  // values P V was formed with, so the weights that multiply V sum to one: the rounding of a
+  // dominant weight to the input type (up to 2^-9 relative in bf16, 2^-11 in fp16) then cancels
+  // instead of scaling the whole row, which with |V| = 5 would cost about 2.4e-3 in fp16. The
+  // LSE keeps the unrounded sum. A row that saw no key (a band can leave one empty) has both
+  // sums zero: O = 0 and LSE = -inf.
   const float l_tot = wave_half_sum(l_run);
-  const float lr_tot = RSUM ? wave_half_sum(lr_run) : l_tot;
+  const float lr_tot = wave_half_sum(lr_run);
   if (qrow < Nq) {
     const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
     const int64_t obase = ((int64_t)(b * p.Hq + hq) * Nq + qrow) * D;
