@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention forward on one MI355X.
 
-One step = one fa_fwd launch over the whole batch of the workload (every step of
+One step = one fa_fwd call over the whole batch of the workload (every step of
 the hot path: work decomposition, K/V streaming, Q K^T, masked online softmax,
-P V, epilogue with O and LSE). Inputs are seeded synthetic data already resident
-in HBM when the timed region starts. Prints ONE JSON line.
+P V, epilogue with O and LSE), which is one attention-kernel launch. Inputs are
+seeded synthetic data already resident in HBM when the timed region starts.
+Prints ONE JSON line. The default workload is the largest configuration that
+fits one GPU: causal attention at B=4, H=48, N=16384, d=64, fp16 (6.6 TFLOP per
+launch); --workload picks another.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits S]
                   [--no-cpu-baseline] [--calibrate-copy] [--sweep]
 
 --splits S cuts each Q-tile's keys into S chunks merged by their LSEs (fa_fwd_split; the
 merge kernel is then part of the step); 0, the default, lets the library choose, which keeps
-one chunk on grids that already fill the chip; 1 never splits.
+one chunk on grids that already fill the chip (the call is then fa_fwd); 1 never splits.
 --sweep additionally prints one line per workload (for tables; not the bench line), and for
 workloads the library splits, a second line without the split.
 --bwd measures the backward pass (fa_bwd) on the workload instead and prints its own line:
@@ -41,7 +44,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MFMA peak, 1 GPU"
-DEFAULT_WORKLOAD = "gqa_causal_b4_hq32_hkv8_n8192_d128_bf16"
+DEFAULT_WORKLOAD = "causal_b4_h48_n16384_d64_f16"
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, fp16 / bf16
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_hbm_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_114_amd", "csrc", f)
@@ -130,9 +133,14 @@ def time_gpu(w, steps: int, warmup: int, splits: int = 0, mask=None):
     stream = torch.cuda.current_stream(dev)
     tm = None if mask is None else torch.from_numpy(mask).to(dev)
 
+    # a square unmasked problem the plan does not split is one fa_fwd call
+    plain = mask is None and w.window_left is None and w.nk == w.N and planned_splits(w, splits) == 1
+    causal = w.causal if plain else False
+    window = None if plain else w.band
+
     def call():
-        fa.fwd(q, k, v, scale=w.scale, window=w.band, out=out, lse=lse, splits=splits, workspace=ws,
-               mask=tm, stream=stream)
+        fa.fwd(q, k, v, scale=w.scale, causal=causal, window=window, out=out, lse=lse,
+               splits=None if plain else splits, workspace=ws, mask=tm, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -294,7 +302,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
     if w.window_left is not None or w.nk != w.N:
         return None  # the pooled oracle covers the causal and unmasked square forms; the bench line is GQA
     qkv = I.workload_qkv(w)
-    cores = max(1, min(16, available_cores()))
+    # one process per core of the host, capped at 16: the CPU share of one GPU on the GPU machines
+    host_cores = available_cores()
+    cores = max(1, min(16, host_cores))
     rows_per_unit = 1024
     chunk = 2 * cores
     flops = 0.0
@@ -324,8 +334,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
     total_units = w.B * w.Hq * ((w.N + rows_per_unit - 1) // rows_per_unit)
     sample = (f"{n_units} of {total_units} units (1024 query rows of one head each, in batch/head order): "
               f"{flops / 1e9:.1f} GFLOP (causal-halved count) in {elapsed:.1f} s on a {cores}-process pool")
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": sample}
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "host_cores": host_cores,
+            "kind": "oracle", "sample": sample + (f" (the pool is capped at 16 of the host's {host_cores} cores, "
+                                                   "the CPU share of one GPU)" if host_cores > cores else "")}
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:

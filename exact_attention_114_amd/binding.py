@@ -194,7 +194,8 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
     out_dtype defaults to float32 (or pass q.dtype); LSE is float32 [B, Hq, Nq].
     causal=True, or window=(left, right) (None for an unlimited edge), bands the
     keys as fa_fwd_ex does: query row i sees keys i + Nk - Nq - left ..
-    i + Nk - Nq + right. splits (0 = automatic, or a chunk count up to 16) cuts each
+    i + Nk - Nq + right. Without a window, split or mask, and with as many keys as
+    queries, the call is fa_fwd itself. splits (0 = automatic, or a chunk count up to 16) cuts each
     Q-tile's keys into chunks merged afterwards (fa_fwd_split); its workspace is
     allocated when not given. mask, a bool or uint8 [B or 1, Hq or 1, Nq, Nk] tensor whose
     nonzero entries hide keys (fa_fwd_mask), applies on top of the band. Runs on ``stream``
@@ -263,6 +264,11 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
         _check(fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                              workspace.data_ptr(), B, Hq, Hkv, N, Nk, d, scale, left, right, int(splits), in_code,
                              out_code, stream.cuda_stream))
+        return out, lse
+    if window is None and Nk == N:
+        # plain or causal attention over one sequence: the boundary's own entry point
+        _check(fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, Hq, Hkv, N, d, scale, causal, in_code, out_code, stream.cuda_stream))
         return out, lse
     _check(fwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, Nk, d, scale, left, right, in_code, out_code, stream.cuda_stream))

@@ -7,7 +7,10 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip")]
-DEPENDS = [os.path.join(HERE, "csrc", "fa_fwd_kernel.hpp"), os.path.join(HERE, "csrc", "fa_bwd_kernel.hpp"),
+# The forward kernel instances, one object per (input type, head dimension) slice of one source.
+SLICE_SOURCE = os.path.join(HERE, "csrc", "fa_fwd_inst.hip")
+SLICES = [(bf16, d) for bf16 in (0, 1) for d in (32, 64, 96, 128)]
+DEPENDS = [os.path.join(HERE, "csrc", "fa_fwd_kernel.hpp"), os.path.join(HERE, "csrc", "fa_fwd_launch.hpp"), os.path.join(HERE, "csrc", "fa_bwd_kernel.hpp"),
            os.path.join(HERE, "csrc", "fa_status.hpp"), os.path.join(HERE, "csrc", "fa_mask.hpp"),
            os.path.join(HERE, "csrc", "fa_mask_kernel.hpp"),
            os.path.join(os.path.dirname(HERE), "include", "fa.h")]
@@ -30,17 +33,40 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source into libfa.so (always recompiles)."""
+    """Compile every HIP source into libfa.so (always recompiles): one hipcc process per source,
+    run in parallel, then one link."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    procs = []
+    objs = []
+    units = [(src, [], os.path.basename(src)) for src in SOURCES]
+    units += [(SLICE_SOURCE, [f"-DFA_INST_BF16={bf}", f"-DFA_INST_D={d}"], f"fa_fwd_inst_{'bf16' if bf else 'f16'}_d{d}")
+              for bf, d in SLICES]
+    for src, defs, name in units:
+        obj = os.path.join(objdir, name + ".o")
+        objs.append(obj)
+        cmd = [hipcc()] + compile_flags + defs + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    failed = []
+    for (src, _, name), p in zip(units, procs):
+        _, err = p.communicate()
+        errs = "\n".join(l for l in err.splitlines() if "packed-fp32-ops" not in l and l.strip())
+        if p.returncode != 0:
+            failed.append(f"{name} ({p.returncode}):\n{errs}")
+        elif verbose and errs:
+            print(errs, file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed: " + "\n".join(failed))
     tmp = OUTPUT + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + SOURCES + ["-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
-    if verbose and errs:
-        print(errs, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
     # A kernel whose host stub was not emitted leaves an undefined symbol behind: refuse a
     # library that the dynamic loader cannot resolve.
     import ctypes

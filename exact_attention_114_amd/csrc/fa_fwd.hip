@@ -12,15 +12,50 @@
 #include <cstdint>
 
 #include "../../include/fa.h"
-#include "fa_fwd_kernel.hpp"
+#include "fa_fwd_launch.hpp"
 #include "fa_mask.hpp"
 #include "fa_status.hpp"
 
+namespace fa {
+
+fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool out_f32, int kb, hipStream_t s) {
+  switch (d) {
+#define FA_SLICE(DD)                                                                          \
+  case DD:                                                                                    \
+    return bf16 ? fwd_dispatch_slice<true, DD>(p, band, am, out_f32, kb, s)                  \
+                : fwd_dispatch_slice<false, DD>(p, band, am, out_f32, kb, s);
+    FA_SLICE(32)
+    FA_SLICE(64)
+    FA_SLICE(96)
+    FA_SLICE(128)
+#undef FA_SLICE
+  }
+  return FA_ERR_UNSUPPORTED;
+}
+
+void merge_dispatch(bool bf16, int d, bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse,
+                    int64_t rows, int nsplit, hipStream_t s) {
+  switch (d) {
+#define FA_SLICE(DD)                                                                                      \
+  case DD:                                                                                                \
+    if (bf16)                                                                                             \
+      merge_dispatch_slice<true, DD>(out_f32, mg, ow, lw, o, lse, rows, nsplit, s);                      \
+    else                                                                                                  \
+      merge_dispatch_slice<false, DD>(out_f32, mg, ow, lw, o, lse, rows, nsplit, s);                     \
+    break;
+    FA_SLICE(32)
+    FA_SLICE(64)
+    FA_SLICE(96)
+    FA_SLICE(128)
+#undef FA_SLICE
+  }
+}
+
+}  // namespace fa
+
 namespace {
 
-// Waves per work-group: 4, 32 query rows each, so a work-group takes BM = 128 rows.
-constexpr int kWaves = 4;
-constexpr int kBlockM = 32 * kWaves;
+constexpr int kBlockM = 32 * fa::kFwdWaves;  // query rows per work-group
 // MI355X has 256 CUs. At d = 128 (and 96) a step of one 32-key block needs fewer registers and
 // half the LDS of a two-block step, so three work-groups fit on a CU instead of two; that pays
 // when the grid can fill them, while a small grid does better with the longer step (fewer
@@ -62,47 +97,6 @@ void split_plan(int64_t grid, int64_t Nk, int requested, int* nsplit, int* kchun
   const int64_t chunk = ((tiles64 + s - 1) / s) * 64;
   *kchunk = (int)chunk;
   *nsplit = (int)((Nk + chunk - 1) / chunk);
-}
-
-template <bool BF16, int D, bool BAND, bool OUT_F32, int KB, bool AM>
-fa_status launch(const fa::Params& p, hipStream_t stream) {
-  // The K/V double buffer is static LDS inside the kernel (4 tiles of 32*KB rows).
-  auto kern = fa::fa_fwd_kernel<BF16, D, BAND, OUT_F32, kWaves, KB, AM>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kWaves * 64), 0, stream, p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    fa::last_hip_error = (int)e;
-    return FA_ERR_HIP;
-  }
-  return FA_OK;
-}
-
-template <bool BF16, int D, bool BAND, bool OUT_F32, bool AM>
-fa_status dispatch_kb(const fa::Params& p, int kb, hipStream_t s) {
-  if constexpr (D == 128 || D == 96) {
-    if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1, AM>(p, s);
-  }
-  return launch<BF16, D, BAND, OUT_F32, 2, AM>(p, s);
-}
-template <bool BF16, int D, bool BAND, bool AM>
-fa_status dispatch_out(const fa::Params& p, bool out_f32, int kb, hipStream_t s) {
-  return out_f32 ? dispatch_kb<BF16, D, BAND, true, AM>(p, kb, s) : dispatch_kb<BF16, D, BAND, false, AM>(p, kb, s);
-}
-// A mask runs on the banded kernel (with unlimited edges when there is no band).
-template <bool BF16, int D>
-fa_status dispatch_band(const fa::Params& p, bool band, bool am, bool out_f32, int kb, hipStream_t s) {
-  if (am) return dispatch_out<BF16, D, true, true>(p, out_f32, kb, s);
-  return band ? dispatch_out<BF16, D, true, false>(p, out_f32, kb, s)
-              : dispatch_out<BF16, D, false, false>(p, out_f32, kb, s);
-}
-template <bool BF16>
-fa_status dispatch_d(const fa::Params& p, int d, bool band, bool am, bool out_f32, int kb, hipStream_t s) {
-  switch (d) {
-    case 32: return dispatch_band<BF16, 32>(p, band, am, out_f32, kb, s);
-    case 64: return dispatch_band<BF16, 64>(p, band, am, out_f32, kb, s);
-    case 96: return dispatch_band<BF16, 96>(p, band, am, out_f32, kb, s);
-    default: return dispatch_band<BF16, 128>(p, band, am, out_f32, kb, s);
-  }
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -217,26 +211,13 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
       return FA_ERR_HIP;
     }
   }
-  st = bf16 ? dispatch_d<true>(p, (int)d, band, am, out_f32, kb, s)
-            : dispatch_d<false>(p, (int)d, band, am, out_f32, kb, s);
+  st = fa::fwd_dispatch(p, bf16, (int)d, band, am, out_f32, kb, s);
   if (st != FA_OK || ns == 1) return st;
   const int rows_per_wg = 256 / (int)(d / 4);  // the merge kernel's rows per work-group
   const dim3 mg((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
   const float* ow = workspace;
   const float* lw = workspace + ns * rows * d;
-  const bool f32 = out_dtype == FA_F32;
-#define FA_MERGE(BF, DD, F32) hipLaunchKernelGGL((fa::fa_merge_kernel<BF, DD, F32>), mg, dim3(256), 0, s, ow, lw, o, lse, rows, ns)
-#define FA_MERGE_D(DD)                                                                  \
-  if (f32) { if (bf16) FA_MERGE(true, DD, true); else FA_MERGE(false, DD, true); }      \
-  else { if (bf16) FA_MERGE(true, DD, false); else FA_MERGE(false, DD, false); }
-  switch (d) {
-    case 32: FA_MERGE_D(32); break;
-    case 64: FA_MERGE_D(64); break;
-    case 96: FA_MERGE_D(96); break;
-    default: FA_MERGE_D(128); break;
-  }
-#undef FA_MERGE_D
-#undef FA_MERGE
+  fa::merge_dispatch(bf16, (int)d, out_dtype == FA_F32, mg, ow, lw, o, lse, rows, ns, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     fa::last_hip_error = (int)e;

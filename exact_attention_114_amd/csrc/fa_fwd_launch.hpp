@@ -1,0 +1,75 @@
+// fa_fwd_launch.hpp — launches of the forward kernels, one (input type, head dimension) slice at
+// a time. Each slice's kernel instances live in their own object, built from fa_fwd_inst.hip with
+// FA_INST_BF16 and FA_INST_D defined, so the slices compile in parallel; the host code in
+// fa_fwd.hip reaches them through fwd_dispatch and merge_dispatch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/fa.h"
+#include "fa_fwd_kernel.hpp"
+#include "fa_status.hpp"
+
+namespace fa {
+
+// Waves per work-group: 4, 32 query rows each, so a work-group takes BM = 128 rows.
+constexpr int kFwdWaves = 4;
+
+// The attention kernel for one problem (p filled by the host), after its argument checks.
+fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool out_f32, int kb, hipStream_t s);
+// The merge of split-key partials (fa_merge_kernel) on grid mg.
+void merge_dispatch(bool bf16, int d, bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse,
+                    int64_t rows, int nsplit, hipStream_t s);
+
+// One slice: defined in the slice's object only.
+template <bool BF16, int D>
+fa_status fwd_dispatch_slice(const Params& p, bool band, bool am, bool out_f32, int kb, hipStream_t s);
+template <bool BF16, int D>
+void merge_dispatch_slice(bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse, int64_t rows,
+                          int nsplit, hipStream_t s);
+
+#define FA_FWD_SLICE_DECL(BF, D)                                                                              \
+  template <>                                                                                                 \
+  fa_status fwd_dispatch_slice<BF, D>(const Params& p, bool band, bool am, bool out_f32, int kb, hipStream_t s); \
+  template <>                                                                                                 \
+  void merge_dispatch_slice<BF, D>(bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse,  \
+                                   int64_t rows, int nsplit, hipStream_t s);
+FA_FWD_SLICE_DECL(false, 32)
+FA_FWD_SLICE_DECL(false, 64)
+FA_FWD_SLICE_DECL(false, 96)
+FA_FWD_SLICE_DECL(false, 128)
+FA_FWD_SLICE_DECL(true, 32)
+FA_FWD_SLICE_DECL(true, 64)
+FA_FWD_SLICE_DECL(true, 96)
+FA_FWD_SLICE_DECL(true, 128)
+#undef FA_FWD_SLICE_DECL
+
+#ifdef FA_INST_D
+// ---- kernel launches, compiled in the slice objects only
+template <bool BF16, int D, bool BAND, bool OUT_F32, int KB, bool AM>
+fa_status launch(const Params& p, hipStream_t stream) {
+  // The K/V double buffer is static LDS inside the kernel (4 tiles of 32*KB rows).
+  auto kern = fa_fwd_kernel<BF16, D, BAND, OUT_F32, kFwdWaves, KB, AM>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kFwdWaves * 64), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+template <bool BF16, int D, bool BAND, bool OUT_F32, bool AM>
+fa_status dispatch_kb(const Params& p, int kb, hipStream_t s) {
+  if constexpr (D == 128 || D == 96) {
+    if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1, AM>(p, s);
+  }
+  return launch<BF16, D, BAND, OUT_F32, 2, AM>(p, s);
+}
+template <bool BF16, int D, bool BAND, bool AM>
+fa_status dispatch_out(const Params& p, bool out_f32, int kb, hipStream_t s) {
+  return out_f32 ? dispatch_kb<BF16, D, BAND, true, AM>(p, kb, s) : dispatch_kb<BF16, D, BAND, false, AM>(p, kb, s);
+}
+#endif
+
+}  // namespace fa

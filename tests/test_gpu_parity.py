@@ -77,6 +77,33 @@ def check_full(w, out_dtype=torch.float32):
     return assert_close(O, L, O_ref, L_ref, w.dtype, w.name, stored_dt=stored)
 
 
+# ---------------------------------------------------------------- the boundary's entry point
+
+@pytest.mark.parametrize("case", ["single_head_n256_d64_f16", "gqa_causal_small"])
+def test_fa_fwd_through_ctypes(case):
+    """fa_fwd itself, called through ctypes with raw device addresses and torch's stream: the
+    single-head workload (fp32 O) and a causal grouped-query case with O in the input type."""
+    if case == "single_head_n256_d64_f16":
+        w, out_code = I.WORKLOADS[case], bnd.FA_F32
+    else:
+        w, out_code = I.small_case(2, 8, 2, 777, 128, I.BF16, True, seed=660, k_mult=2.0), bnd.FA_BF16
+    qkv = I.workload_qkv(w)
+    q, k, v = (to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v))
+    in_code = bnd.FA_F16 if w.dtype == I.F16 else bnd.FA_BF16
+    o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32 if out_code == bnd.FA_F32 else tdtype(w.dtype),
+                    device=DEV)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=DEV)
+    print(f"[gpu] fa_fwd via ctypes {w.name}", flush=True)
+    st = bnd.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N,
+                     w.d, I.scale_f32(w.scale), w.causal, in_code, out_code,
+                     torch.cuda.current_stream().cuda_stream)
+    assert st == bnd.FA_OK, bnd.status_str(st)
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_fp64(*qkv.f64(), I.scale_f32(w.scale), w.causal)
+    assert_close(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), O_ref, L_ref,
+                 w.dtype, f"fa_fwd {w.name}", stored_dt=None if out_code == bnd.FA_F32 else w.dtype)
+
+
 # ---------------------------------------------------------------- small and ragged shapes
 
 RAGGED_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 257]
@@ -172,10 +199,13 @@ def test_workload_sampled(name):
         assert_close(O[b, hq][rows], L[b, hq][rows], O_ref, L_ref, w.dtype, f"{name} b={b} h={hq}")
 
 
-@pytest.mark.parametrize("name", ["gqa_causal_b4_hq32_hkv8_n8192_d128_bf16", "causal_b4_h48_n8192_d64_f16"])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["gqa_causal_b4_hq32_hkv8_n8192_d128_bf16", "causal_b4_h48_n4096_d64_f16",
+                                  "causal_b4_h48_n8192_d64_f16", "causal_b4_h48_n16384_d64_f16"])
 def test_workload_every_output(name):
     """Every O and LSE element of a full-size workload (the launch the benchmark times) against
-    the fp64 oracle, computed per batch element on a process pool of the host's cores."""
+    the fp64 oracle, computed per batch element on a process pool of the host's cores (at most
+    16 processes, the CPU share of one GPU)."""
     w = I.WORKLOADS[name]
     qkv = I.workload_qkv(w)
     O, L = run_gpu(w, qkv)
@@ -191,6 +221,7 @@ def test_workload_every_output(name):
             rows = np.asarray(rows)
             eo, el = assert_close(O[b, h][rows], L[b, h][rows], o_ref, l_ref, w.dtype, f"{name} b={b} h={h}")
             worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        print(f"{name}: batch element {b} done, max|dO| so far {worst_o:.3e}", flush=True)
     print(f"{name}: every output, max|dO| {worst_o:.3e}, max LSE rel {worst_l:.3e}", flush=True)
 
 
@@ -233,6 +264,49 @@ def test_rescale_paths(kind, d, dt, Hq, Hkv, causal):
         seen = slice(w.N - 5, None) if causal else slice(None)
         assert (L_ref[:, :, seen] > 60).all()  # the spike dominates: exp overflows fp32 by far
     assert_close(O, L, O_ref, L_ref, dt, f"{w.name} {kind}")
+
+
+C_LOG2E = 1.4426950408889634
+
+
+@pytest.mark.parametrize("dt", [I.F16, I.BF16])
+def test_dominant_key_stale_reference(dt):
+    """A key that dominates its row arrives in a later tile than the key that set the row's
+    reference, 7 to 7.95 (log2 units) above it: the lane-sum check accepts the tile, so the
+    dominant weight is an exponential 2^x with an arbitrary mantissa, rounded to the input type
+    before it multiplies V = +-5. Normalised by the unrounded sum that rounding would reach O as
+    about u |V| (2.4e-3 in fp16, above the bar; tests/test_normaliser_model.py); with the sum of
+    the rounded weights it cancels. The rows sweep the alignment: the precondition below checks
+    on the CPU that some row would break the bar with the unrounded sum."""
+    N, d = 256, 64
+    w = I.small_case(1, 1, 1, N, d, dt, False, seed=650)
+    g = np.random.Generator(np.random.PCG64(651))
+    q = np.zeros((1, 1, N, d), np.float32)
+    k = np.zeros((1, 1, N, d), np.float32)
+    v = (0.1 * g.standard_normal((1, 1, N, d))).astype(np.float32)
+    q[0, 0, :, 0] = np.linspace(38.9, 44.0, N)
+    q[0, 0, :, 1] = g.uniform(-1.0, 1.0, N)
+    k[0, 0, :, 0] = -8.0                      # every other key: weight below 2^-60
+    k[0, 0, 0, 0] = 1.0                       # the reference key, in the first tile
+    k[0, 0, 100, :2] = (2.0, 1.0 / 64.0)      # the dominant key, in a later tile
+    v[0, 0, 100] = np.where(np.arange(d) % 2 == 0, 5.0, -5.0)
+    v[0, 0, 0] = -v[0, 0, 100]
+    qkv = I.QKV(I.to_bits(q, dt), I.to_bits(k, dt), I.to_bits(v, dt), dt)
+    qf, kf, vf = qkv.f64()
+    # precondition (CPU model of the kernel's arithmetic): the unrounded sum would break the bar
+    c = np.float32(np.float32(w.scale) * np.float32(C_LOG2E))
+    s_ref = (qf[0, 0] @ kf[0, 0, 0]).astype(np.float32)
+    s_dom = (qf[0, 0] @ kf[0, 0, 100]).astype(np.float32)
+    x = (s_dom.astype(np.float64) * np.float64(c) - (s_ref * c).astype(np.float64)).astype(np.float32)
+    p = np.exp2(x.astype(np.float64)).astype(np.float32).astype(np.float64)
+    assert (p < 256).all() and (p > 128).all()
+    p16 = I.bits_to_f64(I.to_bits(p.astype(np.float32), dt), dt)
+    model_err = np.abs((p16 - p) / (p + 1.0))[:, None] * np.abs(vf[0, 0, 100] - vf[0, 0, 0])[None, :]
+    assert model_err.max() > TOL_O[dt]
+    O, L = run_gpu(w, qkv)
+    O_ref, L_ref = attention_fp64(qf, kf, vf, I.scale_f32(w.scale), False)
+    err_o, _ = assert_close(O, L, O_ref, L_ref, dt, f"dominant key {dt}")
+    print(f"dominant key {dt}: max|dO| {err_o:.3e} (the unrounded-sum model reaches {model_err.max():.3e})")
 
 
 # ---------------------------------------------------------------- invariants
