@@ -16,7 +16,8 @@ from typing import Optional, Tuple
 LIB_NAME = "libfa.so"
 
 FA_F16, FA_BF16, FA_F32 = 0, 1, 2
-FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_HIP = range(6)
+FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_SCRATCH = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FA_NOALLOC_SCRATCH_BYTES
 
 # Every function include/fa.h declares, with its ctypes signature.
 SIGNATURES = {
@@ -38,6 +39,8 @@ SIGNATURES = {
     "fa_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                      + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
+    "fa_fwd_split_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
+                             + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 2),
     "fa_bwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 7),
     "fa_bwd_mask": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 9 + [ctypes.c_float]
@@ -111,6 +114,15 @@ def fwd_split_raw(q: int, k: int, v: int, o: int, lse: int, ws: int, B: int, Hq:
     """Call fa_fwd_split with raw device addresses; returns the fa_status code."""
     return load_library().fa_fwd_split(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right,
                                        n_splits, in_dtype, out_dtype, stream)
+
+
+def fwd_split_noalloc_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int,
+                          d: int, scale: float, left: int, right: int, n_splits: int, in_dtype: int, out_dtype: int,
+                          stream: int = 0) -> int:
+    """Call fa_fwd_split_noalloc (split partials in the library's static scratch) with raw device
+    addresses; returns the fa_status code."""
+    return load_library().fa_fwd_split_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right,
+                                               n_splits, in_dtype, out_dtype, stream)
 
 
 def fwd_mask_raw(q: int, k: int, v: int, o: int, lse: int, mask: int, m_sb: int, m_sh: int, m_ld: int, ws: int,

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_fwd_launch.hpp"
@@ -52,6 +53,10 @@ void merge_dispatch(bool bf16, int d, bool out_f32, dim3 mg, const float* ow, co
 }
 
 }  // namespace fa
+
+// The scratch array of fa_fwd_split_noalloc (FA_NOALLOC_SCRATCH_BYTES per device). Host code
+// never uses this name as an address: it holds the per-device pointer from hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -226,6 +231,43 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   return FA_OK;
 }
 
+// Device addresses of `scratch`, one per device, looked up on the first call on that device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch array; the stream must belong to that device.
+fa_status device_scratch(void* stream, float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fa::last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) {
+      fa::last_hip_error = (int)e;
+      return FA_ERR_HIP;
+    }
+    if ((int)sdev != dev) return FA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fa::last_hip_error = (int)e;
+      return FA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = reinterpret_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,6 +317,23 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                  MaskArg{}, in_dtype, out_dtype, stream);
 }
 
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                               int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                               int64_t window_left, int64_t window_right, int n_splits, fa_dtype in_dtype,
+                               fa_dtype out_dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+  // 0 for a problem that does not split (or invalid arguments, which fwd_run reports)
+  const size_t need = fa_fwd_split_workspace_bytes(B, Hq, Nq, Nk, d, n_splits);
+  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  float* ws = nullptr;
+  if (need > 0) {
+    const fa_status st = device_scratch(stream, &ws);
+    if (st != FA_OK) return st;
+  }
+  return fwd_run(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, n_splits, MaskArg{},
+                 in_dtype, out_dtype, stream);
+}
+
 fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, float* lse, const void* mask,
                       int64_t mask_b_stride, int64_t mask_h_stride, int64_t mask_row_stride, float* workspace,
                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
@@ -311,6 +370,9 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 32, 64, 96 or 128, inputs fp16/bf16, output fp32 or the input type";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error (see fa_last_hip_error)";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the split partials exceed the 64 MiB static scratch of fa_fwd_split_noalloc "
+             "(use fa_fwd_split with a workspace)";
   }
   return "unknown fa_status";
 }

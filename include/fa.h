@@ -68,7 +68,9 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 3, /* d not 32, 64, 96 or 128; in_dtype not F16/BF16; out_dtype
                              not F32 or in_dtype */
   FA_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned */
-  FA_ERR_HIP = 5          /* the HIP runtime reported an error; see fa_last_hip_error() */
+  FA_ERR_HIP = 5,         /* the HIP runtime reported an error; see fa_last_hip_error() */
+  FA_ERR_SCRATCH = 6      /* fa_fwd_split_noalloc: the problem needs more scratch than the
+                             library's static array holds (FA_NOALLOC_SCRATCH_BYTES) */
 } fa_status;
 
 /*
@@ -146,6 +148,32 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int64_t Nk, int64_t d, float scale, int64_t window_left,
                        int64_t window_right, int n_splits, fa_dtype in_dtype,
                        fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_fwd_split_noalloc — fa_fwd_split for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The split partials go to a static scratch array inside the
+ * library, FA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the library runs on,
+ * held until the process ends; the call allocates nothing and takes no
+ * workspace. The caller still passes the inputs and outputs.
+ *   The array used is the current device's; stream must belong to that device
+ *   (or be NULL), else FA_ERR_UNSUPPORTED. The first call on a device looks up
+ *   its array's address (hipGetSymbolAddress); make one call before capturing.
+ *   A problem whose partials (fa_fwd_split_workspace_bytes) exceed the array
+ *   returns FA_ERR_SCRATCH with nothing launched; a problem that does not split
+ *   needs no scratch and runs as fa_fwd_ex.
+ *   Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   partials (each call writes every partial it reads, so nothing needs to
+ *   start at zero): calls that overlap on one GPU (several streams or threads)
+ *   race, and the caller must serialise them.
+ * Other arguments, errors and execution as fa_fwd_split.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                               int64_t d, float scale, int64_t window_left,
+                               int64_t window_right, int n_splits, fa_dtype in_dtype,
+                               fa_dtype out_dtype, void* stream);
 
 /*
  * fa_fwd_mask — fa_fwd_split with a mask input: the Ascend operator's optional

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         msg = bnd.status_str(s)
         assert msg.startswith("FA_"), msg
     assert "unknown" in bnd.status_str(99)
@@ -358,3 +358,20 @@ def test_bwd_mask_validation():
     assert call(d=80) == bnd.FA_ERR_UNSUPPORTED
     for kw in (dict(ld=82, Nk=81), dict(sb=2), dict()):
         assert call(**kw) == bnd.FA_ERR_ALIGN
+
+
+def test_split_noalloc_validation():
+    """fa_fwd_split_noalloc checks its arguments on the host: NULL pointers, a problem whose split
+    partials exceed the static scratch (FA_ERR_SCRATCH, before any HIP call), and, for a problem
+    that does not split, the checks of fa_fwd_ex (misaligned pointers)."""
+    def call(q=BAD, Nq=64, Nk=64, n_splits=0, B=1, Hq=2, d=64):
+        return bnd.fwd_split_noalloc_raw(q, BAD, BAD, BAD, BAD, B, Hq, 1, Nq, Nk, d, 0.125, -1, 0, n_splits,
+                                         bnd.FA_F16, bnd.FA_F32, 0)
+    assert call(q=0) == bnd.FA_ERR_NULLPTR
+    need = bnd.split_workspace_bytes(1, 32, 512, 32768, 128, 16)
+    assert need > bnd.NOALLOC_SCRATCH_BYTES
+    assert call(Nq=512, Nk=32768, n_splits=16, Hq=32, d=128) == bnd.FA_ERR_SCRATCH
+    assert "scratch" in bnd.status_str(bnd.FA_ERR_SCRATCH)
+    assert bnd.split_workspace_bytes(1, 2, 64, 64, 64, 0) == 0  # no split: no scratch, fa_fwd_ex's checks
+    assert call() == bnd.FA_ERR_ALIGN
+    assert call(Nq=0) == bnd.FA_ERR_SHAPE
