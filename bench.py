@@ -48,7 +48,7 @@ DEFAULT_WORKLOAD = "causal_b4_h48_n16384_d64_f16"
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, fp16 / bf16
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_hbm_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_114_amd", "csrc", f)
-                  for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip", "fa_status.hpp")]
+                  for f in ("fa_fwd_kernel.hpp", "fa_fwd_launch.hpp", "fa_fwd_inst.hip", "fa_fwd.hip", "fa_status.hpp")]
 
 
 def kernel_source_hash(sources=None) -> str:

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip")]
 # The forward kernel instances, one object per (input type, head dimension) slice of one source.
 SLICE_SOURCE = os.path.join(HERE, "csrc", "fa_fwd_inst.hip")
-SLICES = [(bf16, d) for bf16 in (0, 1) for d in (32, 64, 96, 128)]
+SLICES = [(bf16, d) for bf16 in (0, 1) for d in (32, 48, 64, 80, 96, 112, 128)]
 DEPENDS = [os.path.join(HERE, "csrc", "fa_fwd_kernel.hpp"), os.path.join(HERE, "csrc", "fa_fwd_launch.hpp"), os.path.join(HERE, "csrc", "fa_bwd_kernel.hpp"),
            os.path.join(HERE, "csrc", "fa_status.hpp"), os.path.join(HERE, "csrc", "fa_mask.hpp"),
            os.path.join(HERE, "csrc", "fa_mask_kernel.hpp"),

@@ -74,7 +74,7 @@ fa_status check_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, 
                     int64_t* tq, int64_t* tk) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d % 16 != 0 || d < 32 || d > 128) return FA_ERR_UNSUPPORTED;
   if (Nq * d > kMaxPlaneElems || Nk * d > kMaxPlaneElems) return FA_ERR_SHAPE;
   const int64_t lim = (int64_t)1 << 31;
   const int64_t t = (Nq + kTile - 1) / kTile, u = (Nk + kTile - 1) / kTile;
@@ -183,8 +183,11 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
     return bf16 ? dispatch_band<true, DD>(p, band, am, o_f32, prep_rows, grid_kv, grid_q, s)    \
                 : dispatch_band<false, DD>(p, band, am, o_f32, prep_rows, grid_kv, grid_q, s);
     FA_BWD_D(32)
+    FA_BWD_D(48)
     FA_BWD_D(64)
+    FA_BWD_D(80)
     FA_BWD_D(96)
+    FA_BWD_D(112)
     FA_BWD_D(128)
 #undef FA_BWD_D
   }

@@ -225,9 +225,9 @@ __device__ inline u32x4 tr_operand(const lds_char* tile, int rowb, int t2, int o
   return a;
 }
 
-// At d = 128 the dK/dV kernel keeps V's rows in LDS rather than registers, which brings it
-// under the 256 VGPRs two waves per SIMD allow.
-constexpr bool bwd_v_in_lds(int d) { return d == 128; }
+// At d = 112 and 128 the dK/dV kernel keeps V's rows in LDS rather than registers, which brings
+// it under the 256 VGPRs two waves per SIMD allow.
+constexpr bool bwd_v_in_lds(int d) { return d > 96; }
 constexpr int bwd_waves_per_simd(int d) { return 2; }
 
 // 4 * (lane id), formed from scratch where it is used: as an opaque instruction sequence it
@@ -245,9 +245,9 @@ template <bool BF16, int D, bool BAND, int NW, bool AM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
-  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
+  static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 16 from 32 to 128");
   constexpr int ROWBL = lds_pitch(D) * 2, TB = 32 * ROWBL;  // LDS row pitch and tile bytes
-  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int NKS = D / 16, NDB = (D + 31) / 32;  // a half-filled last d-block reads LDS padding
   __shared__ __attribute__((aligned(1024))) char sQ0[TB];
   __shared__ __attribute__((aligned(1024))) char sQ1[TB];
   __shared__ __attribute__((aligned(1024))) char sG0[TB];
@@ -476,6 +476,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     if (key < Nk) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
+        if (D % 32 != 0 && db == NDB - 1 && l32 >= 16) continue;  // padding columns of a half block
         dkp[(int64_t)key * D + 32 * db + l32] = dk[db][i] * sc;
         dvp[(int64_t)key * D + 32 * db + l32] = dv[db][i];
       }
@@ -488,9 +489,9 @@ template <bool BF16, int D, bool BAND, int NW, bool AM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p) {
   using E = Elt<BF16>;
-  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
+  static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 16 from 32 to 128");
   constexpr int ROWBL = lds_pitch(D) * 2, TB = 32 * ROWBL, BM = 32 * NW;  // LDS row pitch, tile bytes
-  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int NKS = D / 16, NDB = (D + 31) / 32;  // a half-filled last d-block reads LDS padding
   __shared__ __attribute__((aligned(1024))) char sK0[TB];
   __shared__ __attribute__((aligned(1024))) char sK1[TB];
   __shared__ __attribute__((aligned(1024))) char sV0[TB];
@@ -642,7 +643,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
     const int q = q0w + 8 * (i >> 2) + 4 * h + (i & 3);
     if (q < Nq) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) dqp[(int64_t)q * D + 32 * db + l32] = acc[db][i] * sc;
+      for (int db = 0; db < NDB; ++db) {
+        if (D % 32 != 0 && db == NDB - 1 && l32 >= 16) continue;  // padding columns of a half block
+        dqp[(int64_t)q * D + 32 * db + l32] = acc[db][i] * sc;
+      }
     }
   }
 }

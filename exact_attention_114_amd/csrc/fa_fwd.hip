@@ -26,8 +26,11 @@ fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bo
     return bf16 ? fwd_dispatch_slice<true, DD>(p, band, am, out_f32, kb, s)                  \
                 : fwd_dispatch_slice<false, DD>(p, band, am, out_f32, kb, s);
     FA_SLICE(32)
+    FA_SLICE(48)
     FA_SLICE(64)
+    FA_SLICE(80)
     FA_SLICE(96)
+    FA_SLICE(112)
     FA_SLICE(128)
 #undef FA_SLICE
   }
@@ -45,8 +48,11 @@ void merge_dispatch(bool bf16, int d, bool out_f32, dim3 mg, const float* ow, co
       merge_dispatch_slice<false, DD>(out_f32, mg, ow, lw, o, lse, rows, nsplit, s);                     \
     break;
     FA_SLICE(32)
+    FA_SLICE(48)
     FA_SLICE(64)
+    FA_SLICE(80)
     FA_SLICE(96)
+    FA_SLICE(112)
     FA_SLICE(128)
 #undef FA_SLICE
   }
@@ -61,7 +67,7 @@ static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof
 namespace {
 
 constexpr int kBlockM = 32 * fa::kFwdWaves;  // query rows per work-group
-// MI355X has 256 CUs. At d = 128 (and 96) a step of one 32-key block needs fewer registers and
+// MI355X has 256 CUs. At d > 64 a step of one 32-key block needs fewer registers and
 // half the LDS of a two-block step, so three work-groups fit on a CU instead of two; that pays
 // when the grid can fill them, while a small grid does better with the longer step (fewer
 // barriers). At d = 96 the one-block step measured 4-6% faster on grids above 512.
@@ -71,7 +77,7 @@ constexpr int64_t kOneBlockMinGrid = 2 * 256;
 // prefetches may reach beyond it stays below 2^31 bytes.
 constexpr int64_t kMaxPlaneElems = ((int64_t)1 << 30) - ((int64_t)1 << 16);
 
-int key_blocks(int64_t d, int64_t grid) { return (d == 128 || d == 96) && grid > kOneBlockMinGrid ? 1 : 2; }
+int key_blocks(int64_t d, int64_t grid) { return d > 64 && grid > kOneBlockMinGrid ? 1 : 2; }
 
 // A band edge of this size or more is unlimited: every in-range index difference is smaller.
 constexpr int kUnlimited = 1 << 30;
@@ -111,7 +117,7 @@ fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t 
                         int64_t* n_qtiles, int64_t* grid) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d % 16 != 0 || d < 32 || d > 128) return FA_ERR_UNSUPPORTED;
   if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
   // The kernel sizes its tile loads in 32-bit byte offsets from the start of a K/V head
@@ -367,7 +373,7 @@ const char* fa_status_str(fa_status s) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: a pointer argument is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes, head grouping, scale or causal flag";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 32, 64, 96 or 128, inputs fp16/bf16, output fp32 or the input type";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be a multiple of 16 from 32 to 128, inputs fp16/bf16, output fp32 or the input type";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error (see fa_last_hip_error)";
     case FA_ERR_SCRATCH:

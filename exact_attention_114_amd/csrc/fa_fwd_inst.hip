@@ -1,5 +1,6 @@
 // fa_fwd_inst.hip — the forward kernel instances of one (input type, head dimension) slice.
-// Built once per slice with FA_INST_BF16 (0 or 1) and FA_INST_D (32, 64, 96 or 128) defined
+// Built once per slice with FA_INST_BF16 (0 or 1) and FA_INST_D (a head dimension: 32, 48, 64,
+// 80, 96, 112 or 128) defined
 // (exact_attention_114_amd/build.py); fa_fwd.hip's host code calls them through
 // fa::fwd_dispatch and fa::merge_dispatch.
 #include "fa_fwd_launch.hpp"

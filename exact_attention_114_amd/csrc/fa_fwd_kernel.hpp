@@ -104,8 +104,9 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kPadOffset = 0x7FFF0000;
 
 // LDS row pitch (elements) for a head dimension: rows are stored at a power-of-two pitch so
-// the XOR swizzles below stay inside a row; a head dimension of 32 or 96 leaves padding
-// chunks at the end of each row that are loaded as zeros and never read.
+// the XOR swizzles below stay inside a row; a head dimension below the pitch (32, 48, 80, 96,
+// 112) leaves padding chunks at the end of each row that are loaded as zeros; only the P V
+// operand of a half-filled last d-block reads them.
 constexpr int lds_pitch(int d) { return d <= 64 ? 64 : 128; }
 
 struct Params {
@@ -273,7 +274,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Waves that share a SIMD for a tile shape: registers bound it (a d = 128 step with two key
 // blocks holds 189 VGPRs, with one 168; d = 64 about 150) and so does LDS (4 tiles of
 // 32*KB rows at the LDS pitch per work-group).
-constexpr int waves_per_simd(int d, int kb) { return d >= 96 && kb == 1 ? 3 : 2; }
+constexpr int waves_per_simd(int d, int kb) { return d > 64 && kb == 1 ? 3 : 2; }
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
 // pipeline step takes KB blocks of 32 keys.
@@ -281,7 +282,7 @@ template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB, bool AM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
-  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 32 up to 128");
+  static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 16 from 32 to 128");
   constexpr int BM = 32 * NW;
   constexpr int BN = 32 * KB;
   constexpr int DP = lds_pitch(D);        // LDS row pitch (elements)
@@ -291,7 +292,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   constexpr int ROWBL = DP * 2;           // bytes per row in LDS
   constexpr int TILE_BYTES = BN * ROWBL;  // one K or one V tile in LDS
   constexpr int NKS = D / 16;             // MFMA k-steps of Q K^T
-  constexpr int NDB = D / 32;             // MFMA d-blocks of P V
+  // MFMA d-blocks of P V. A head dimension that is an odd multiple of 16 leaves the last block half
+  // filled: its upper 16 columns read the LDS row padding (zeros) and are never stored.
+  constexpr int NDB = (D + 31) / 32;
   constexpr int NLD = TILE_BYTES / (NW * 1024);  // 1 KiB tile-load instructions per wave per matrix
   constexpr int RPI = NW * 1024 / ROWBL;  // tile rows between a wave's consecutive load instructions
   static_assert(NLD >= 1 && TILE_BYTES % (NW * 1024) == 0, "each wave issues the same number of tile loads");
@@ -776,6 +779,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
+        if (32 * db + 8 * g4 >= D) continue;  // the padding columns of a half-filled last block
         const int dcol = 32 * db + 8 * g4 + 4 * h;
         const float o0 = acc_o[db][4 * g4 + 0] * inv, o1 = acc_o[db][4 * g4 + 1] * inv;
         const float o2 = acc_o[db][4 * g4 + 2] * inv, o3 = acc_o[db][4 * g4 + 3] * inv;

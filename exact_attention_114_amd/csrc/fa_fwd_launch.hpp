@@ -34,14 +34,15 @@ void merge_dispatch_slice(bool out_f32, dim3 mg, const float* ow, const float* l
   template <>                                                                                                 \
   void merge_dispatch_slice<BF, D>(bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse,  \
                                    int64_t rows, int nsplit, hipStream_t s);
-FA_FWD_SLICE_DECL(false, 32)
-FA_FWD_SLICE_DECL(false, 64)
-FA_FWD_SLICE_DECL(false, 96)
-FA_FWD_SLICE_DECL(false, 128)
-FA_FWD_SLICE_DECL(true, 32)
-FA_FWD_SLICE_DECL(true, 64)
-FA_FWD_SLICE_DECL(true, 96)
-FA_FWD_SLICE_DECL(true, 128)
+#define FA_FWD_SLICE_DECL_D(D) FA_FWD_SLICE_DECL(false, D) FA_FWD_SLICE_DECL(true, D)
+FA_FWD_SLICE_DECL_D(32)
+FA_FWD_SLICE_DECL_D(48)
+FA_FWD_SLICE_DECL_D(64)
+FA_FWD_SLICE_DECL_D(80)
+FA_FWD_SLICE_DECL_D(96)
+FA_FWD_SLICE_DECL_D(112)
+FA_FWD_SLICE_DECL_D(128)
+#undef FA_FWD_SLICE_DECL_D
 #undef FA_FWD_SLICE_DECL
 
 #ifdef FA_INST_D
@@ -61,7 +62,7 @@ fa_status launch(const Params& p, hipStream_t stream) {
 
 template <bool BF16, int D, bool BAND, bool OUT_F32, bool AM>
 fa_status dispatch_kb(const Params& p, int kb, hipStream_t s) {
-  if constexpr (D == 128 || D == 96) {
+  if constexpr (D > 64) {
     if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1, AM>(p, s);
   }
   return launch<BF16, D, BAND, OUT_F32, 2, AM>(p, s);

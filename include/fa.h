@@ -65,8 +65,8 @@ typedef enum {
   FA_ERR_NULLPTR = 1,     /* a pointer argument is NULL */
   FA_ERR_SHAPE = 2,       /* B, Hq, Hkv, N or d < 1; Hq not a multiple of Hkv; non-finite
                              or non-positive scale; sizes beyond the 32-bit index range */
-  FA_ERR_UNSUPPORTED = 3, /* d not 32, 64, 96 or 128; in_dtype not F16/BF16; out_dtype
-                             not F32 or in_dtype */
+  FA_ERR_UNSUPPORTED = 3, /* d not a multiple of 16 from 32 to 128; in_dtype not
+                             F16/BF16; out_dtype not F32 or in_dtype */
   FA_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned */
   FA_ERR_HIP = 5,         /* the HIP runtime reported an error; see fa_last_hip_error() */
   FA_ERR_SCRATCH = 6      /* fa_fwd_split_noalloc: the problem needs more scratch than the
@@ -79,9 +79,10 @@ typedef enum {
  *   q, k, v   device pointers, layouts above, element type in_dtype
  *   o         device pointer, [B][Hq][N][d] of out_dtype
  *   lse       device pointer, [B][Hq][N] float32
- *   B, Hq, Hkv, N, d   sizes; Hq % Hkv == 0; d in {32, 64, 96, 128} (the
- *             intelliparadigm page, section 1.3, asks for head dimensions that
- *             are not powers of two); N >= 1 (any N,
+ *   B, Hq, Hkv, N, d   sizes; Hq % Hkv == 0; d a multiple of 16 from 32 to
+ *             128: 32, 48, 64, 80, 96, 112 or 128 (the intelliparadigm page,
+ *             section 1.3, asks for head dimensions that are not powers of
+ *             two); N >= 1 (any N,
  *             tails are masked); B*Hq*ceil(N/128) below 2^31; N*d at most
  *             2^30 - 2^16 (a K/V head plane under 2 GiB)
  *   scale     multiplies Q.K^T (commonly 1/sqrt(d)); finite and > 0

@@ -71,7 +71,7 @@ def test_shape_errors(kw):
     assert call(**kw) == bnd.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(d=48), dict(d=80), dict(d=16), dict(d=256), dict(in_dtype=bnd.FA_F32),
+@pytest.mark.parametrize("kw", [dict(d=40), dict(d=72), dict(d=16), dict(d=144), dict(d=256), dict(in_dtype=bnd.FA_F32),
                                 dict(in_dtype=7), dict(out_dtype=bnd.FA_BF16),
                                 dict(in_dtype=bnd.FA_BF16, out_dtype=bnd.FA_F16)])
 def test_unsupported(kw):
@@ -145,7 +145,7 @@ def test_bwd_shape_errors(kw):
     assert call_bwd(**kw) == bnd.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(d=48), dict(d=16), dict(d=256), dict(in_dtype=bnd.FA_F32), dict(in_dtype=9),
+@pytest.mark.parametrize("kw", [dict(d=40), dict(d=16), dict(d=256), dict(in_dtype=bnd.FA_F32), dict(in_dtype=9),
                                 dict(o_dtype=bnd.FA_BF16), dict(in_dtype=bnd.FA_BF16, o_dtype=bnd.FA_F16)])
 def test_bwd_unsupported(kw):
     assert call_bwd(**kw) == bnd.FA_ERR_UNSUPPORTED
@@ -161,7 +161,7 @@ def test_bwd_workspace_bytes():
     assert bnd.bwd_workspace_bytes(2, 3, 1, 64) == 2 * 3 * 128 * 2 * 4
     assert bnd.bwd_workspace_bytes(1, 1, 129, 128) == 256 * 2 * 4
     assert bnd.bwd_workspace_bytes(4, 32, 8192, 128) == 4 * 32 * 8192 * 2 * 4
-    assert bnd.bwd_workspace_bytes(1, 1, 64, 80) == 0
+    assert bnd.bwd_workspace_bytes(1, 1, 64, 72) == 0
     assert bnd.bwd_workspace_bytes(1, 1, 64, 96) == 128 * 2 * 4
     assert bnd.bwd_workspace_bytes(0, 1, 64, 64) == 0
 
@@ -220,7 +220,7 @@ def test_bwd_ex_null_pointers(which):
 
 def test_bwd_ex_validation_order():
     assert call_bwd_ex(Nk=0) == bnd.FA_ERR_SHAPE
-    assert call_bwd_ex(d=80) == bnd.FA_ERR_UNSUPPORTED
+    assert call_bwd_ex(d=72) == bnd.FA_ERR_UNSUPPORTED
     assert call_bwd_ex(d=96) == bnd.FA_ERR_ALIGN
     assert call_bwd_ex(o_dtype=bnd.FA_F16) == bnd.FA_ERR_UNSUPPORTED
     assert call_bwd_ex() == bnd.FA_ERR_ALIGN
@@ -248,7 +248,7 @@ def test_split_workspace_bytes():
     # requested splits are bounded by the 64-key tiles: 256 keys -> 4 tiles -> 2 chunks
     assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 8) == 2 * 1 * 10 * 65 * 4
     assert bnd.split_workspace_bytes(1, 1, 10, 256, 64, 17) == 0
-    assert bnd.split_workspace_bytes(1, 1, 10, 256, 80, 2) == 0
+    assert bnd.split_workspace_bytes(1, 1, 10, 256, 72, 2) == 0
     assert bnd.split_workspace_bytes(1, 1, 10, 256, 96, 2) == 2 * 1 * 10 * 97 * 4
 
 
@@ -267,7 +267,7 @@ def test_split_validation():
     assert call(ws=0) == bnd.FA_ERR_NULLPTR          # a split needs its workspace
     assert call(ns=-1) == bnd.FA_ERR_SHAPE
     assert call(ns=17) == bnd.FA_ERR_SHAPE
-    assert call(d=80) == bnd.FA_ERR_UNSUPPORTED
+    assert call(d=72) == bnd.FA_ERR_UNSUPPORTED
     assert call() == bnd.FA_ERR_ALIGN
     assert call(d=96) == bnd.FA_ERR_ALIGN
     assert call(ws=0, Nk=64) == bnd.FA_ERR_ALIGN     # no split possible: the workspace is not needed
@@ -291,7 +291,7 @@ def test_fwd_mask_validation():
     assert call_fwd_mask(ld=76) == bnd.FA_ERR_SHAPE            # rows shorter than Nk
     assert call_fwd_mask(sb=-4) == bnd.FA_ERR_SHAPE
     assert call_fwd_mask(ld=(1 << 31) // 64) == bnd.FA_ERR_SHAPE  # Nq * row stride past 2^31 - 2^16
-    assert call_fwd_mask(d=80) == bnd.FA_ERR_UNSUPPORTED
+    assert call_fwd_mask(d=72) == bnd.FA_ERR_UNSUPPORTED
     assert call_fwd_mask(ns=17) == bnd.FA_ERR_SHAPE
     for kw in (dict(ld=82, Nk=81), dict(sh=6), dict()):     # row stride, plane stride, pointers
         assert call_fwd_mask(**kw) == bnd.FA_ERR_ALIGN
@@ -309,7 +309,7 @@ def test_mask_workspace_bytes():
     assert bnd.mask_workspace_bytes(1, 16, 100, 2048, 128, 3, 0, 400) == split + 256 + 16 * 100 * 64 * 4
     split = 2 * 1 * 10 * 65 * 4
     assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 8, 0, 0) == (split + 255) // 256 * 256 + 256 + 10 * 8 * 4
-    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 80, 2, 0, 0) == 0
+    assert bnd.mask_workspace_bytes(1, 1, 10, 256, 72, 2, 0, 0) == 0
     assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 17, 0, 0) == 0
     assert bnd.mask_workspace_bytes(1, 1, 10, 256, 64, 1, -4, 0) == 0
 
@@ -326,7 +326,7 @@ def test_bwd_mask_workspace_bytes():
     cols = 4 * 8192 * 256 * 4
     assert bnd.bwd_mask_workspace_bytes(4, 32, 8192, 8192, 128, 1, 0) == base + hull + bits + 4 * 64 * 64 + cols
     assert bnd.bwd_mask_workspace_bytes(1, 2, 64, 80, 64, -4, 0) == 0
-    assert bnd.bwd_mask_workspace_bytes(1, 2, 64, 80, 80, 0, 0) == 0
+    assert bnd.bwd_mask_workspace_bytes(1, 2, 64, 80, 72, 0, 0) == 0
 
 
 def test_mask_strides_of_tensors():
@@ -355,7 +355,7 @@ def test_bwd_mask_validation():
     assert call(ld=76) == bnd.FA_ERR_SHAPE
     assert call(sh=-4) == bnd.FA_ERR_SHAPE
     assert call(ld=(1 << 31) // 64) == bnd.FA_ERR_SHAPE
-    assert call(d=80) == bnd.FA_ERR_UNSUPPORTED
+    assert call(d=72) == bnd.FA_ERR_UNSUPPORTED
     for kw in (dict(ld=82, Nk=81), dict(sb=2), dict()):
         assert call(**kw) == bnd.FA_ERR_ALIGN
 

@@ -71,13 +71,14 @@ def test_bwd_ragged_shapes(N, d, dt, causal):
 
 
 @pytest.mark.parametrize("N", [1, 65, 129, 257])
-@pytest.mark.parametrize("d,dt", [(32, I.F16), (32, I.BF16), (96, I.F16), (96, I.BF16)])
+@pytest.mark.parametrize("d,dt", [(32, I.F16), (32, I.BF16), (48, I.F16), (48, I.BF16), (80, I.F16), (80, I.BF16),
+                                  (96, I.F16), (96, I.BF16), (112, I.F16), (112, I.BF16)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_head_dims_32_and_96(N, d, dt, causal):
+def test_bwd_head_dims_not_64_or_128(N, d, dt, causal):
     run_case(I.small_case(1, 2, 1, N, d, dt, causal, seed=770 + N + d))
 
 
-@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("d", [32, 48, 80, 96, 112])
 def test_bwd_head_dims_gqa(d):
     run_case(I.small_case(2, 8, 2, 400, d, I.BF16, True, seed=780 + d, k_mult=2.0))
     run_case(I.small_case(1, 4, 4, 300, d, I.F16, False, seed=790 + d), o_in_dtype=True)

@@ -117,14 +117,16 @@ def test_ragged_shapes(N, d, dt, causal):
 
 
 @pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 257])
-@pytest.mark.parametrize("d,dt", [(32, I.F16), (32, I.BF16), (96, I.F16), (96, I.BF16)])
+@pytest.mark.parametrize("d,dt", [(32, I.F16), (32, I.BF16), (48, I.F16), (48, I.BF16), (80, I.F16), (80, I.BF16),
+                                  (96, I.F16), (96, I.BF16), (112, I.F16), (112, I.BF16)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_head_dims_32_and_96(N, d, dt, causal):
-    """Head dimensions that are not 64 or 128: rows sit at a padded LDS pitch."""
+def test_head_dims_not_64_or_128(N, d, dt, causal):
+    """Head dimensions that are not 64 or 128: rows sit at a padded LDS pitch, and for 48, 80 and
+    112 the last 32-column block of P V is half filled."""
     check_full(I.small_case(1, 2, 1, N, d, dt, causal, seed=700 + N + d))
 
 
-@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("d", [32, 48, 80, 96, 112])
 def test_head_dims_gqa_many_tiles(d):
     check_full(I.small_case(2, 8, 2, 700, d, I.BF16, True, seed=750 + d, k_mult=2.0))
     check_full(I.small_case(1, 4, 4, 1000, d, I.F16, False, seed=760 + d), out_dtype=torch.float16)
@@ -140,9 +142,9 @@ def test_gqa_groups(Hq, Hkv, causal):
 @pytest.mark.parametrize("N", [1, 33, 65, 300])
 @pytest.mark.parametrize("dt", [I.F16, I.BF16])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [128, 96])
+@pytest.mark.parametrize("d", [128, 112, 96, 80])
 def test_d128_large_grid_shapes(N, dt, causal, d):
-    """d = 128 and 96 grids above two work-groups per CU run the kernel with 32-key steps."""
+    """Grids above two work-groups per CU with d > 64 run the kernel with 32-key steps."""
     T = (N + 127) // 128
     Hq = 4 * (-(-520 // (2 * T * 4)))  # B = 2: at least 520 work-groups, heads a multiple of 4
     w = I.small_case(2, Hq, Hq // 4, N, d, dt, causal, seed=600 + N + d, k_mult=2.0)
@@ -371,6 +373,6 @@ def test_outputs_written_in_place_and_errors_raise():
     torch.cuda.synchronize()
     assert o.data_ptr() == out.data_ptr() and torch.isfinite(out).all() and torch.isfinite(lse).all()
     with pytest.raises(bnd.FaError):
-        fa.fwd(q[..., :48].contiguous(), k[..., :48].contiguous(), v[..., :48].contiguous())  # d = 48
+        fa.fwd(q[..., :40].contiguous(), k[..., :40].contiguous(), v[..., :40].contiguous())  # d = 40
     with pytest.raises(bnd.FaError):
         fa.fwd(q[:, :1].expand(1, 3, 100, 64).contiguous(), k, v)  # 3 query heads over 2 K/V heads
