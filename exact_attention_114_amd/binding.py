@@ -201,8 +201,9 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
         out=None, lse=None, splits: Optional[int] = None, workspace=None, mask=None, stream=None):
     """Exact attention forward on the GPU: returns (O, LSE).
 
-    q: [B, Hq, Nq, d], k and v: [B, Hkv, Nk, d], contiguous fp16 or bf16 CUDA
-    tensors (on ROCm, HIP device tensors). scale defaults to 1/sqrt(d);
+    q: [B, Hq, Nq, d], k and v: [B, Hkv, Nk, d], contiguous fp16, bf16 or fp32 CUDA
+    tensors (on ROCm, HIP device tensors); fp32 inputs take fp32 O and neither split keys
+    nor a mask. scale defaults to 1/sqrt(d);
     out_dtype defaults to float32 (or pass q.dtype); LSE is float32 [B, Hq, Nq].
     causal=True, or window=(left, right) (None for an unlimited edge), bands the
     keys as fa_fwd_ex does: query row i sees keys i + Nk - Nq - left ..
@@ -215,8 +216,8 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
     """
     import torch
 
-    if q.dtype not in (torch.float16, torch.bfloat16):
-        raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must be float16 or bfloat16")
+    if q.dtype not in (torch.float16, torch.bfloat16, torch.float32):
+        raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must be float16, bfloat16 or float32")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must share one dtype")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -234,7 +235,7 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
         scale = 1.0 / math.sqrt(d)
     if out_dtype is None:
         out_dtype = torch.float32
-    in_code = FA_F16 if q.dtype == torch.float16 else FA_BF16
+    in_code = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float32: FA_F32}[q.dtype]
     if out_dtype == torch.float32:
         out_code = FA_F32
     elif out_dtype == q.dtype:

@@ -118,7 +118,7 @@ fa_status check_problem(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t 
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d % 16 != 0 || d < 32 || d > 128) return FA_ERR_UNSUPPORTED;
-  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16 && in_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
   // The kernel sizes its tile loads in 32-bit byte offsets from the start of a K/V head
   // plane, which can reach a few tiles past its end: N*d*2 bytes plus that margin stay below 2^31.
@@ -149,10 +149,14 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   int64_t nq = 0, grid = 0;
   fa_status st = check_problem(B, Hq, Hkv, Nq, Nk, d, in_dtype, &nq, &grid);
   if (st != FA_OK) return st;
-  int ns = 1, kc = (int)(((Nk + 63) / 64) * 64);
-  split_plan(grid, Nk, n_splits, &ns, &kc);
-  if (ns == 1) kc = (int)(((Nk + 63) / 64) * 64);
   const bool am = mask.data != nullptr;
+  const bool f32_in = in_dtype == FA_F32;
+  // fp32 inputs run their own kernel: no split keys (an automatic plan keeps one chunk), no mask
+  // input, fp32 O
+  if (f32_in && (n_splits > 1 || am || out_dtype != FA_F32)) return FA_ERR_UNSUPPORTED;
+  int ns = 1, kc = (int)(((Nk + 63) / 64) * 64);
+  if (!f32_in) split_plan(grid, Nk, n_splits, &ns, &kc);
+  if (ns == 1) kc = (int)(((Nk + 63) / 64) * 64);
   if ((ns > 1 || am) && !workspace) return FA_ERR_NULLPTR;
   if (!(std::isfinite(scale) && scale > 0.0f)) return FA_ERR_SHAPE;
   if (out_dtype != FA_F32 && out_dtype != in_dtype) return FA_ERR_UNSUPPORTED;
@@ -222,6 +226,7 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
       return FA_ERR_HIP;
     }
   }
+  if (f32_in) return fa::fwd_dispatch_f32(p, (int)d, band, s);
   st = fa::fwd_dispatch(p, bf16, (int)d, band, am, out_f32, kb, s);
   if (st != FA_OK || ns == 1) return st;
   const int rows_per_wg = 256 / (int)(d / 4);  // the merge kernel's rows per work-group
@@ -363,7 +368,7 @@ fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, 
   const fa_status st = check_problem(B, Hq, Hkv, N, N, d, in_dtype, &nq, &g);
   if (st != FA_OK) return st;
   *block_m = kBlockM;
-  *block_n = 32 * key_blocks(d, g);
+  *block_n = in_dtype == FA_F32 ? 32 : 32 * key_blocks(d, g);
   *grid = g;
   return FA_OK;
 }
@@ -373,7 +378,7 @@ const char* fa_status_str(fa_status s) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: a pointer argument is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes, head grouping, scale or causal flag";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be a multiple of 16 from 32 to 128, inputs fp16/bf16, output fp32 or the input type";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be a multiple of 16 from 32 to 128, inputs fp16/bf16 (or fp32 without split keys or mask, fp32 output), output fp32 or the input type";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error (see fa_last_hip_error)";
     case FA_ERR_SCRATCH:

@@ -194,6 +194,19 @@ def draw_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
     return QKV(to_bits(q, dtype), to_bits(k, dtype), to_bits(v, dtype), dtype)
 
 
+def draw_qkv_f32(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int, k_mult: float = 1.0,
+                 Nk: Optional[int] = None):
+    """The same draws as draw_qkv kept in float32 (the fp32-input path): (q, k, v) arrays."""
+    Nk = N if Nk is None else Nk
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = g.standard_normal((B, Hq, N, d), dtype=np.float32)
+    k = g.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = g.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    if k_mult != 1.0:
+        k = k * np.float32(k_mult)
+    return q, k, v
+
+
 def draw_dout(B: int, Hq: int, N: int, d: int, dtype: str, seed: int) -> np.ndarray:
     """The gradient arriving at O for the backward pass: [B,Hq,N,d] standard normal from its
     own PCG64 stream (seed), rounded to the storage type; returns the bit pattern."""

@@ -71,7 +71,7 @@ def test_shape_errors(kw):
     assert call(**kw) == bnd.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(d=40), dict(d=72), dict(d=16), dict(d=144), dict(d=256), dict(in_dtype=bnd.FA_F32),
+@pytest.mark.parametrize("kw", [dict(d=40), dict(d=72), dict(d=16), dict(d=144), dict(d=256), dict(in_dtype=bnd.FA_F32, out_dtype=bnd.FA_F16),
                                 dict(in_dtype=7), dict(out_dtype=bnd.FA_BF16),
                                 dict(in_dtype=bnd.FA_BF16, out_dtype=bnd.FA_F16)])
 def test_unsupported(kw):

@@ -1,0 +1,105 @@
+"""GPU parity of the fp32-input forward (fa_fwd / fa_fwd_ex with in_dtype FA_F32) against the fp64
+oracle, within the fp32 bar of oracle/precision.py: per element of O,
+    (d + 8) e32 sum_j w_ij a_ij |V_jc - O_ic| + 2 (n_i + 2) e32 sum_j w_ij |V_jc|
+and per row of LSE (d + 8) e32 sum_j w_ij a_ij + (n_i + 4) e32 + 2 e32 |LSE_i|, with w the
+softmax weights over the row's n_i visible keys and a_ij = s sum_c |Q_ic K_jc| + 1 (the bar's
+derivation is in that module). Inputs are seeded float32 N(0,1) draws; both sides see the same
+values. Each case prints its worst error-to-bar ratio."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_114_amd as fa
+from exact_attention_114_amd import binding as bnd
+from exact_attention_114_amd import inputs as I
+from oracle.attention import head_attention_band_fp64, kv_head_of
+from oracle.precision import head_attention_f32_bar_fp64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run(B, Hq, Hkv, Nq, Nk, d, seed, causal=False, window=None, k_mult=1.0, rows=None, heads=None):
+    q, k, v = I.draw_qkv_f32(B, Hq, Hkv, Nq, d, seed, k_mult, Nk)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[gpu] fa_fwd fp32 B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} window={window}",
+          flush=True)
+    o, lse = fa.fwd(*(torch.from_numpy(x).to(DEV) for x in (q, k, v)), scale=scale, causal=causal, window=window)
+    torch.cuda.synchronize()
+    O = o.cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    left, right = (None, 0) if causal else (window if window is not None else (None, None))
+    sc = I.scale_f32(scale)
+    worst = [0.0, 0.0]
+    for b, h in (heads or [(b, h) for b in range(B) for h in range(Hq)]):
+        hk = kv_head_of(h, Hq, Hkv)
+        qq = q[b, h].astype(np.float64) if rows is None else q[b, h][rows].astype(np.float64)
+        kk, vv = k[b, hk].astype(np.float64), v[b, hk].astype(np.float64)
+        if rows is None:
+            O_ref, L_ref = head_attention_band_fp64(qq, kk, vv, sc, left, right, Nk - Nq)
+            bo, bl = head_attention_f32_bar_fp64(qq, kk, vv, sc, left, right, Nk - Nq)
+            Og, Lg = O[b, h], L[b, h]
+        else:  # sampled rows: the band's offset moves with each row
+            O_ref = np.empty((len(rows), d)); L_ref = np.empty(len(rows))
+            bo = np.empty((len(rows), d)); bl = np.empty(len(rows))
+            for n, r in enumerate(rows):
+                a, c = head_attention_band_fp64(qq[n:n + 1], kk, vv, sc, left, right, r + Nk - Nq)
+                x, y = head_attention_f32_bar_fp64(qq[n:n + 1], kk, vv, sc, left, right, r + Nk - Nq)
+                O_ref[n], L_ref[n], bo[n], bl[n] = a[0], c[0], x[0], y[0]
+            Og, Lg = O[b, h][rows], L[b, h][rows]
+        assert np.isfinite(Og).all()
+        seen = np.isfinite(L_ref)
+        assert (Og[~seen] == 0).all() and (Lg[~seen] == -np.inf).all()
+        ro = (np.abs(Og - O_ref) / np.maximum(bo, 1e-300))[seen].max() if seen.any() else 0.0
+        rl = (np.abs(Lg - L_ref)[seen] / np.maximum(bl[seen], 1e-300)).max() if seen.any() else 0.0
+        worst = [max(worst[0], ro), max(worst[1], rl)]
+        assert ro <= 1.0, f"b={b} h={h}: O error reaches {ro:.3f} of the fp32 bar"
+        assert rl <= 1.0, f"b={b} h={h}: LSE error reaches {rl:.3f} of the fp32 bar"
+    print(f"[f32 bar] worst error/bar O {worst[0]:.4f} LSE {worst[1]:.4f}", flush=True)
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 257])
+@pytest.mark.parametrize("d", [32, 48, 64, 80, 96, 112, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_ragged(N, d, causal):
+    run(1, 2, 1, N, N, d, 3000 + N + d, causal=causal)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 1)])
+def test_f32_gqa_sharp_rows(Hq, Hkv):
+    run(2, Hq, Hkv, 333, 333, 128, 3100 + Hq + Hkv, causal=True, k_mult=2.0)
+
+
+@pytest.mark.parametrize("Nq,Nk,window", [(300, 300, (64, 0)), (200, 450, (None, 0)), (450, 200, (None, 0)),
+                                          (160, 96, (20, 70)), (1, 500, (None, 0))])
+def test_f32_bands(Nq, Nk, window):
+    run(1, 4, 2, Nq, Nk, 64, 3200 + Nq + Nk, window=window)
+
+
+def test_f32_long_head_shape_sampled_rows():
+    """The long-head shape (B=1, H=16, N=2048, d=128) in fp32, on sampled rows of four heads."""
+    rows = np.array([0, 1, 2, 127, 128, 1000, 2046, 2047])
+    run(1, 16, 16, 2048, 2048, 128, 3300, rows=rows, heads=[(0, 0), (0, 5), (0, 10), (0, 15)])
+
+
+def test_f32_causal_long_sampled_rows():
+    """A causal N = 8192, d = 128 grouped-query case in fp32 on sampled rows."""
+    rows = np.array([0, 1, 31, 32, 4095, 4096, 8190, 8191])
+    run(1, 8, 2, 8192, 8192, 128, 3400, causal=True, rows=rows, heads=[(0, 0), (0, 3), (0, 7)])
+
+
+def test_f32_unsupported_combinations_raise():
+    q, k, v = (torch.from_numpy(x).to(DEV) for x in I.draw_qkv_f32(1, 2, 2, 64, 64, 3500))
+    with pytest.raises(bnd.FaError):
+        fa.fwd(q, k, v, out_dtype=torch.float16)  # fp32 inputs give fp32 O
+    with pytest.raises(bnd.FaError):
+        fa.fwd(q, k, v, splits=2)
+    with pytest.raises(bnd.FaError):
+        fa.fwd(q, k, v, mask=torch.zeros((1, 1, 64, 64), dtype=torch.uint8, device=DEV))
+    o, lse = fa.fwd(q, k, v)
+    do = torch.zeros_like(q)
+    with pytest.raises(bnd.FaError):
+        fa.bwd(q, k, v, o, lse, do)  # the backward takes 16-bit inputs

@@ -1,0 +1,120 @@
+"""Pins for the fp32-input parity bar (oracle/precision.py), on the CPU.
+
+  * brute force: pure-Python loops form the same sums (weights from math.exp of the definition),
+    so a dropped or misplaced term of the bar fails;
+  * validity: a numpy float32 emulation of the tiled algorithm (32-key tiles, running maximum
+    moved every tile, base-2 exponentials, fp32 sums) stays inside the bar on ragged, causal,
+    windowed and long-row cases; its worst error-to-bar ratio is printed;
+  * planted slips: the same emulation with Q and K rounded to fp16, with V rounded to bf16, or
+    with the probabilities rounded to bf16 before P V, exceeds the bar.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from exact_attention_114_amd import inputs as I
+from oracle.attention import band_visible, head_attention_band_fp64
+from oracle.precision import E32, head_attention_f32_bar_fp64
+
+
+def draw(n, N, d, seed, k_mult=1.0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = g.standard_normal((n, d), dtype=np.float32)
+    k = g.standard_normal((N, d), dtype=np.float32) * np.float32(k_mult)
+    v = g.standard_normal((N, d), dtype=np.float32)
+    return q, k, v
+
+
+def test_bar_equals_brute_force():
+    q, k, v = draw(5, 7, 3, 41)
+    scale, left, right, off = 0.6, 3, 1, 2
+    bo, bl = head_attention_f32_bar_fp64(q, k, v, scale, left, right, off)
+    O, L = head_attention_band_fp64(q, k, v, scale, left, right, off)
+    vis = band_visible(np.arange(5), np.arange(7), left, right, off)
+    d = 3
+    for i in range(5):
+        js = [j for j in range(7) if vis[i, j]]
+        w = {j: math.exp(scale * sum(float(q[i, c]) * float(k[j, c]) for c in range(d)) - L[i]) for j in js}
+        a = {j: scale * sum(abs(float(q[i, c]) * float(k[j, c])) for c in range(d)) + 1.0 for j in js}
+        for c in range(d):
+            want = (d + 8) * E32 * sum(w[j] * a[j] * abs(float(v[j, c]) - O[i, c]) for j in js) \
+                + 2 * (len(js) + 2) * E32 * sum(w[j] * abs(float(v[j, c])) for j in js)
+            assert abs(bo[i, c] - want) <= 1e-12 * want
+        want_l = (d + 8) * E32 * sum(w[j] * a[j] for j in js) + (len(js) + 4) * E32 + 2 * E32 * abs(L[i])
+        assert abs(bl[i] - want_l) <= 1e-12 * want_l
+
+
+def round16(x, dt):
+    return I.bits_to_f64(I.to_bits(np.asarray(x, np.float32), dt), dt).astype(np.float32)
+
+
+def emulate(q, k, v, scale, left, right, off, slip=None):
+    """One head in float32, tile by tile as the kernel: 32-key tiles, the running max moved to
+    each tile's row max, exponentials in base 2 with scale*log2(e) folded into one fma."""
+    f = np.float32
+    q, k, v = (np.asarray(x, f) for x in (q, k, v))
+    if slip == "qk_f16":
+        q, k = round16(q, I.F16), round16(k, I.F16)
+    if slip == "v_bf16":
+        v = round16(v, I.BF16)
+    n, N = q.shape[0], k.shape[0]
+    c = f(np.float64(f(scale)) * 1.4426950408889634)
+    m = np.full(n, -np.inf, f)
+    l = np.zeros(n, f)
+    acc = np.zeros((n, v.shape[1]), f)
+    for j0 in range(0, N, 32):
+        j1 = min(N, j0 + 32)
+        S = (q @ k[j0:j1].T).astype(f)
+        vis = band_visible(np.arange(n), np.arange(j0, j1), left, right, off)
+        S = np.where(vis, S, f(-np.inf))
+        m_new = np.maximum(np.maximum(m, S.max(axis=1) * c), f(-1e30)).astype(f)
+        alpha = np.exp2(m - m_new).astype(f)
+        m = m_new
+        l = (l * alpha).astype(f)
+        acc = (acc * alpha[:, None]).astype(f)
+        P = np.exp2((S.astype(np.float64) * np.float64(c) - m[:, None].astype(np.float64)).astype(f)).astype(f)
+        if slip == "p_bf16":
+            P = round16(P, I.BF16)
+        l = (l + P.sum(axis=1, dtype=f)).astype(f)
+        acc = (acc + P @ v[j0:j1]).astype(f)
+    seen = l > 0
+    O = np.where(seen[:, None], acc / np.where(seen, l, f(1))[:, None], f(0))
+    L = np.where(seen, (m.astype(np.float64) + np.log2(np.where(seen, l, 1.0))) * math.log(2.0), -np.inf)
+    return O.astype(np.float64), L
+
+
+def ratios(q, k, v, scale, left, right, off, slip=None):
+    O_ref, L_ref = head_attention_band_fp64(q, k, v, scale, left, right, off)
+    bo, bl = head_attention_f32_bar_fp64(q, k, v, scale, left, right, off)
+    O, L = emulate(q, k, v, scale, left, right, off, slip)
+    seen = np.isfinite(L_ref)
+    ro = (np.abs(O - O_ref) / np.maximum(bo, 1e-300))[seen].max()
+    rl = (np.abs(L - L_ref)[seen] / np.maximum(bl[seen], 1e-300)).max()
+    return ro, rl
+
+
+CASES = [
+    (1, 1, 64, None, None, 0, 1.0),
+    (37, 37, 32, None, 0, 0, 1.0),
+    (200, 200, 128, None, None, 0, 2.0),
+    (150, 300, 64, 40, 10, 150, 1.0),
+    (64, 1500, 96, None, 0, 1436, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_emulated_fp32_within_bar(case):
+    n, N, d, left, right, off, km = case
+    q, k, v = draw(n, N, d, 900 + n + d, km)
+    ro, rl = ratios(q, k, v, d ** -0.5, left, right, off)
+    print(f"fp32 emulation, worst error / bar: O {ro:.3f}, LSE {rl:.3f}")
+    assert ro <= 1.0 and rl <= 1.0
+
+
+@pytest.mark.parametrize("slip", ["qk_f16", "v_bf16", "p_bf16"])
+def test_sixteen_bit_slips_exceed_bar(slip):
+    q, k, v = draw(256, 256, 64, 950, 1.0)
+    ro, rl = ratios(q, k, v, 0.125, None, 0, 0, slip)
+    print(f"{slip}: worst error / bar O {ro:.1f}, LSE {rl:.1f}")
+    assert max(ro, rl) > 1.0
