@@ -39,6 +39,8 @@ SIGNATURES = {
     "fa_fwd_split": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                      + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
+    "fa_fwd_fp8": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_float] * 3 + [ctypes.c_int64] * 6
+                   + [ctypes.c_float] + [ctypes.c_int64] * 2 + [ctypes.c_void_p]),
     "fa_fwd_split_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                              + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 2),
@@ -123,6 +125,52 @@ def fwd_split_noalloc_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: 
     addresses; returns the fa_status code."""
     return load_library().fa_fwd_split_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right,
                                                n_splits, in_dtype, out_dtype, stream)
+
+
+def fwd_fp8_raw(q: int, k: int, v: int, o: int, lse: int, descale_q: float, descale_k: float, descale_v: float,
+                B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, scale: float, left: int, right: int,
+                stream: int = 0) -> int:
+    """Call fa_fwd_fp8 with raw device addresses; returns the fa_status code."""
+    return load_library().fa_fwd_fp8(q, k, v, o, lse, float(descale_q), float(descale_k), float(descale_v), B, Hq,
+                                     Hkv, Nq, Nk, d, float(scale), left, right, stream)
+
+
+def fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, *, scale: Optional[float] = None,
+            causal: bool = False, window=None, out=None, lse=None, stream=None):
+    """fp8 (OCP e4m3) attention forward: returns (O float32, LSE float32).
+
+    q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d]: contiguous uint8 (or torch.float8_e4m3fn) CUDA
+    tensors of e4m3 bytes; each tensor's real values are its bytes' values times its descale.
+    scale defaults to 1/sqrt(d); causal and window as for ``fwd``.
+    """
+    import torch
+
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    for t in (q, k, v):
+        if t.dtype not in (torch.uint8,) + ((fp8,) if fp8 is not None else ()):
+            raise FaError(FA_ERR_UNSUPPORTED, "q, k, v must hold e4m3 bytes (uint8 or float8_e4m3fn)")
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise FaError(FA_ERR_SHAPE, "q, k, v must be contiguous 4-D GPU tensors")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise FaError(FA_ERR_SHAPE, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    left, right = _edges(causal, window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if out.shape != (B, Hq, N, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise FaError(FA_ERR_SHAPE, "out must be a contiguous float32 [B, Hq, N, d] tensor")
+    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise FaError(FA_ERR_SHAPE, "lse must be a contiguous float32 [B, Hq, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fwd_fp8_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), descale_q,
+                       descale_k, descale_v, B, Hq, Hkv, N, Nk, d, scale, left, right, stream.cuda_stream))
+    return out, lse
 
 
 def fwd_mask_raw(q: int, k: int, v: int, o: int, lse: int, mask: int, m_sb: int, m_sh: int, m_ld: int, ws: int,

@@ -7,12 +7,12 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip"),
-           os.path.join(HERE, "csrc", "fa_fwd_f32.hip")]
+           os.path.join(HERE, "csrc", "fa_fwd_f32.hip"), os.path.join(HERE, "csrc", "fa_fwd_fp8.hip")]
 # The forward kernel instances, one object per (input type, head dimension) slice of one source.
 SLICE_SOURCE = os.path.join(HERE, "csrc", "fa_fwd_inst.hip")
 SLICES = [(bf16, d) for bf16 in (0, 1) for d in (32, 48, 64, 80, 96, 112, 128)]
 DEPENDS = [os.path.join(HERE, "csrc", "fa_fwd_kernel.hpp"), os.path.join(HERE, "csrc", "fa_fwd_launch.hpp"),
-           os.path.join(HERE, "csrc", "fa_fwd_f32_kernel.hpp"), os.path.join(HERE, "csrc", "fa_bwd_kernel.hpp"),
+           os.path.join(HERE, "csrc", "fa_fwd_f32_kernel.hpp"), os.path.join(HERE, "csrc", "fa_fwd_fp8_kernel.hpp"), os.path.join(HERE, "csrc", "fa_bwd_kernel.hpp"),
            os.path.join(HERE, "csrc", "fa_status.hpp"), os.path.join(HERE, "csrc", "fa_mask.hpp"),
            os.path.join(HERE, "csrc", "fa_mask_kernel.hpp"),
            os.path.join(os.path.dirname(HERE), "include", "fa.h")]

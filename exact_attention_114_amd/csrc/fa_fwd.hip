@@ -200,6 +200,7 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   p.total_wg = (int)(grid * ns);
   p.ilv = fa::interleave_groups(p.left, p.right, kUnlimited, am, B * Hkv, Nk, d);
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  p.vscale = 1.0f;
   char* const wsb = reinterpret_cast<char*>(workspace);
   int2* const hull = am ? reinterpret_cast<int2*>(wsb + ml.hull_off) : nullptr;
   unsigned* const bits = am ? reinterpret_cast<unsigned*>(wsb + ml.bits_off) : nullptr;
@@ -358,6 +359,45 @@ fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, floa
   m.row_stride = mask_row_stride;
   return fwd_run(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, n_splits, m,
                  in_dtype, out_dtype, stream);
+}
+
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float* o, float* lse, float descale_q,
+                     float descale_k, float descale_v, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                     int64_t d, float scale, int64_t window_left, int64_t window_right, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+  int64_t nq = 0, grid = 0;
+  const fa_status st = check_problem(B, Hq, Hkv, Nq, Nk, d, FA_F16, &nq, &grid);
+  if (st != FA_OK) return st;
+  const double c = (double)scale * descale_q * descale_k * 1.4426950408889634074;
+  if (!(std::isfinite(scale) && scale > 0.0f) || !(std::isfinite(descale_q) && descale_q > 0.0f) ||
+      !(std::isfinite(descale_k) && descale_k > 0.0f) || !(std::isfinite(descale_v) && descale_v > 0.0f) ||
+      !(std::isfinite(c) && c > 0.0 && c < 3.0e38))
+    return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::Params p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.off = (int)(Nk - Nq);
+  p.left = window_left < 0 || window_left >= kUnlimited ? kUnlimited : (int)window_left;
+  p.right = window_right < 0 || window_right >= kUnlimited ? kUnlimited : (int)window_right;
+  p.group = (int)(Hq / Hkv);
+  p.n_qtiles = (int)nq;
+  p.nsplit = 1;
+  p.kchunk = (int)(((Nk + 63) / 64) * 64);
+  p.total_wg = (int)grid;
+  p.ilv = 1;
+  p.c = (float)c;
+  p.vscale = descale_v;
+  const bool band = p.left != kUnlimited || p.right != kUnlimited;
+  return fa::fwd_dispatch_fp8(p, (int)d, band, reinterpret_cast<hipStream_t>(stream));
 }
 
 fa_status fa_fwd_tile(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal, fa_dtype in_dtype,

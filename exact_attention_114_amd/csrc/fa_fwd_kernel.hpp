@@ -125,7 +125,8 @@ struct Params {
   int kchunk;    // keys per chunk, a multiple of 64 (every key-tile size)
   int total_wg;  // B * Hq * n_qtiles * nsplit
   int ilv;       // (b, hkv) groups whose Q-tiles are interleaved longest first (1, 2 or 4)
-  float c;       // scale * log2(e)
+  float c;       // scale * log2(e) (fp8 inputs: times the query and key descales)
+  float vscale;  // fp8 inputs: the value descale, applied to O (1 otherwise)
   // optional mask (kernels built with AM), as fa_mask_prep_kernel leaves it: one bit per
   // (query, key), set where the key is hidden, in rows of am_nw 32-bit words; the (b, hq)
   // plane starts at am_bits + b*bits_sb + hq*bits_sh (strides 0 along an axis the mask shares)

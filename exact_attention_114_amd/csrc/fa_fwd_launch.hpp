@@ -19,6 +19,9 @@ constexpr int kFwdWaves = 4;
 fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool out_f32, int kb, hipStream_t s);
 // The fp32-input kernel (fa_fwd_f32.hip): no split keys, no mask input, fp32 O.
 fa_status fwd_dispatch_f32(const Params& p, int d, bool band, hipStream_t s);
+// The fp8-input kernel (fa_fwd_fp8.hip): e4m3 Q, K, V with descales folded into p.c and
+// p.vscale; no split keys, no mask input, fp32 O.
+fa_status fwd_dispatch_fp8(const Params& p, int d, bool band, hipStream_t s);
 // The merge of split-key partials (fa_merge_kernel) on grid mg.
 void merge_dispatch(bool bf16, int d, bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse,
                     int64_t rows, int nsplit, hipStream_t s);

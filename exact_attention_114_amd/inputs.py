@@ -207,6 +207,51 @@ def draw_qkv_f32(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int, k_mult: f
     return q, k, v
 
 
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP fp8 e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+    no infinities, largest finite 448), nearest even; values beyond 448 saturate to +-448; uint8
+    bits. Normal numbers have exponents -6..8; below 2^-6 the grid is the subnormal one, 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.isfinite(x).all():
+        raise ValueError("e4m3 rounding expects finite values")
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.minimum(np.abs(x), 448.0)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)                         # below 2^-6: the subnormal spacing 2^-9
+    q = np.ldexp(1.0, (e - 3).astype(np.int64))   # grid spacing in this binade
+    r = np.round(a / q) * q                       # numpy rounds halves to even
+    r = np.minimum(r, 448.0)
+    e2 = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    normal = r >= 2.0 ** -6
+    exp_f = np.where(normal, e2 + 7, 0).astype(np.int64)
+    man = np.where(normal, np.round((r / np.ldexp(1.0, e2.astype(np.int64)) - 1.0) * 8), np.round(r / 2.0 ** -9))
+    return (sign | (exp_f.astype(np.uint8) << 3) | man.astype(np.uint8)).astype(np.uint8)
+
+
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of OCP e4m3 bit patterns (the NaN patterns 0x7F and 0xFF are not produced)."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    e = (b >> 3) & 15
+    m = b & 7
+    v = np.where(e == 0, np.ldexp(m.astype(np.float64), -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where(b >> 7 != 0, -v, v)
+
+
+def draw_qkv_fp8(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int, k_mult: float = 1.0,
+                 Nk: Optional[int] = None):
+    """fp8 inputs: the draws of draw_qkv_f32, each tensor stored as e4m3 bytes of x / descale with
+    descale = max|x| / 448 (float32), the per-tensor scaling that uses e4m3's whole range. Returns
+    (q, k, v) uint8 arrays and (descale_q, descale_k, descale_v) floats; the represented values are
+    e4m3(bytes) * descale."""
+    xs = draw_qkv_f32(B, Hq, Hkv, N, d, seed, k_mult, Nk)
+    out, ds = [], []
+    for x in xs:
+        dsc = float(np.float32(np.abs(x).max() / 448.0))
+        out.append(f32_to_e4m3_bits(x.astype(np.float64) / dsc))
+        ds.append(dsc)
+    return tuple(out), tuple(ds)
+
+
 def draw_dout(B: int, Hq: int, N: int, d: int, dtype: str, seed: int) -> np.ndarray:
     """The gradient arriving at O for the backward pass: [B,Hq,N,d] standard normal from its
     own PCG64 stream (seed), rounded to the storage type; returns the bit pattern."""

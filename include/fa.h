@@ -177,6 +177,29 @@ fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void
                                fa_dtype out_dtype, void* stream);
 
 /*
+ * fa_fwd_fp8 — fa_fwd_ex for fp8 inputs. The zyxy lecture (section 5) lists fp8
+ * among the input types of the FA2 generation of kernels. q, k and v hold OCP
+ * e4m3 bytes (sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F and 0xFF
+ * are NaN), laid out as fa_fwd's q, k and v with one byte per element; the value
+ * of an element is its e4m3 value times the tensor's descale. Scores are
+ * scale * (descale_q q) . (descale_k k); both products run on gfx950's fp8
+ * matrix cores with fp32 accumulation; the probabilities are rounded to e4m3
+ * for the P V product (relative 2^-4, or 2^-10 of the row's running maximum in
+ * e4m3's subnormal range), and O is divided by the sum of those rounded values.
+ *
+ *   o          device pointer, [B][Hq][Nq][d] float32
+ *   lse        device pointer, [B][Hq][Nq] float32, natural log of the sum of exp(score)
+ *   descale_q, descale_k, descale_v   finite and > 0 (FA_ERR_SHAPE otherwise)
+ *   window_left, window_right         the band of fa_fwd_ex (causal: -1, 0)
+ * Sizes, alignment (16 bytes), errors and execution as fa_fwd_ex. No split keys
+ * and no mask input.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float* o, float* lse,
+                     float descale_q, float descale_k, float descale_v, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                     int64_t window_left, int64_t window_right, void* stream);
+
+/*
  * fa_fwd_mask — fa_fwd_split with a mask input: the Ascend operator's optional
  * boolean attn_mask (the intelliparadigm page, section 2.2), which is the Mask
  * step of FlashAttention-1's Algorithm 2 that the cnblogs page points to. Key

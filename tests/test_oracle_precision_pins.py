@@ -118,3 +118,142 @@ def test_sixteen_bit_slips_exceed_bar(slip):
     ro, rl = ratios(q, k, v, 0.125, None, 0, 0, slip)
     print(f"{slip}: worst error / bar O {ro:.1f}, LSE {rl:.1f}")
     assert max(ro, rl) > 1.0
+
+
+# ---------------------------------------------------------------- fp8 (OCP e4m3) inputs
+
+from oracle.precision import FP8_DOT_REL, fp8_exponent_error, head_attention_fp8_bar_fp64  # noqa: E402
+
+
+def test_e4m3_rounding_matches_torch():
+    """The input generator's e4m3 rounding (nearest even, saturating at 448) against torch's
+    float8_e4m3fn conversion, a library routine, on in-range values; every finite bit pattern
+    decodes to torch's value."""
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(5))
+    x = np.concatenate([g.standard_normal(100000).astype(np.float32) * np.float32(60),
+                        g.standard_normal(10000).astype(np.float32) * np.float32(0.01),
+                        np.array([0, 1, -1, 448, -448, 2 ** -9, 2 ** -10, 1.5 * 2 ** -10, 2 ** -6, 0.3, 17,
+                                  1.0625, 1.1875, 240, 2.5 * 2 ** -9], np.float32)])
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (I.f32_to_e4m3_bits(x) == ref).all()
+    pats = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    tv = torch.from_numpy(pats).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(I.e4m3_bits_to_f64(pats), tv)
+    assert (I.f32_to_e4m3_bits(np.array([500.0, -1e4], np.float32)) == np.array([0x7E, 0xFE], np.uint8)).all()
+
+
+def test_fp8_bar_brute_force():
+    q, k, v = draw(4, 6, 3, 61)
+    scale, left, right, off = 0.7, None, 0, 2
+    bo, bl = head_attention_fp8_bar_fp64(q, k, v, scale, left, right, off)
+    # the exponent error by brute force: 2^-10 of the largest product of each 64-long range plus 8 e32 a
+    E = fp8_exponent_error(q, k, scale)
+    for i in range(4):
+        for j in range(6):
+            prods = [abs(float(q[i, c]) * float(k[j, c])) for c in range(3)]
+            want = scale * FP8_DOT_REL * max(prods) + 8 * E32 * (scale * sum(prods) + 1.0)
+            assert abs(E[i, j] - want) <= 1e-12 * want
+    b32o, b32l = head_attention_f32_bar_fp64(q, k, v, scale, left, right, off, exponent_error=fp8_exponent_error)
+    O, L = head_attention_band_fp64(q, k, v, scale, left, right, off)
+    vis = band_visible(np.arange(4), np.arange(6), left, right, off)
+    for i in range(4):
+        js = [j for j in range(6) if vis[i, j]]
+        w = {j: math.exp(scale * sum(float(q[i, c]) * float(k[j, c]) for c in range(3)) - L[i]) for j in js}
+        wm = max(w.values())
+        sub = {j: min(w[j], 2.0 ** -10 * wm) for j in js}
+        den = 1 - 2.0 ** -4 - sum(sub.values())
+        for c in range(3):
+            num = sum((2.0 ** -4 * w[j] + sub[j]) * abs(float(v[j, c]) - O[i, c]) for j in js)
+            assert abs(bo[i, c] - (num / den + b32o[i, c])) <= 1e-12 * bo[i, c]
+        assert bl[i] == b32l[i]
+
+
+def e4m3(x):
+    return I.e4m3_bits_to_f64(I.f32_to_e4m3_bits(np.asarray(x, np.float64))).astype(np.float32)
+
+
+def e3m2_like(x):
+    """Rounding with one mantissa bit fewer than e4m3 (a slip: twice e4m3's step)."""
+    x = np.asarray(x, np.float64)
+    e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    q = np.ldexp(1.0, (np.maximum(e, -6) - 2).astype(np.int64))
+    return (np.round(x / q) * q).astype(np.float32)
+
+
+def emulate_fp8(q8, k8, v8, dq, dk, dv, scale, left, right, off, slip=None):
+    """One head as the fp8 kernel computes it: e4m3 inputs (bytes), exact products summed in
+    fp32, 64-key steps with the running max moved every step, P rounded to e4m3 for P V, O
+    divided by the sum of the rounded P, then times descale_v."""
+    f = np.float32
+    q = I.e4m3_bits_to_f64(q8).astype(f)
+    k = I.e4m3_bits_to_f64(k8).astype(f)
+    v = I.e4m3_bits_to_f64(v8).astype(f)
+    n, N = q.shape[0], k.shape[0]
+    c = f(np.float64(scale) * dq * (1.0 if slip == "no_descale_k" else dk) * 1.4426950408889634)
+    m = np.full(n, -np.inf, f)
+    l = np.zeros(n, f)
+    lr = np.zeros(n, f)
+    acc = np.zeros((n, v.shape[1]), f)
+    for j0 in range(0, N, 64):
+        j1 = min(N, j0 + 64)
+        S = (q @ k[j0:j1].T).astype(f)
+        vis = band_visible(np.arange(n), np.arange(j0, j1), left, right, off)
+        S = np.where(vis, S, f(-np.inf))
+        m_new = np.maximum(np.maximum(m, S.max(axis=1) * c), f(-1e30)).astype(f)
+        alpha = np.exp2(m - m_new).astype(f)
+        m = m_new
+        l, lr = (l * alpha).astype(f), (lr * alpha).astype(f)
+        acc = (acc * alpha[:, None]).astype(f)
+        P = np.exp2((S.astype(np.float64) * np.float64(c) - m[:, None].astype(np.float64)).astype(f)).astype(f)
+        Pr = e3m2_like(P) if slip == "p_coarse" else e4m3(P)
+        l = (l + P.sum(axis=1, dtype=f)).astype(f)
+        lr = (lr + Pr.sum(axis=1, dtype=f)).astype(f)
+        acc = (acc + Pr @ v[j0:j1]).astype(f)
+    seen = l > 0
+    ov = f(dv) * (f(dv) if slip == "descale_v_twice" else f(1))
+    O = np.where(seen[:, None], acc * (ov / np.where(seen, lr, f(1)))[:, None], f(0))
+    L = np.where(seen, (m.astype(np.float64) + np.log2(np.where(seen, l, 1.0))) * math.log(2.0), -np.inf)
+    return O.astype(np.float64), L
+
+
+def fp8_ratios(n, N, d, seed, k_mult, left, right, off, slip=None):
+    (q8, k8, v8), (dq, dk, dv) = I.draw_qkv_fp8(1, 1, 1, n, d, seed, k_mult, N)
+    q8, k8, v8 = q8[0, 0], k8[0, 0], v8[0, 0]
+    q, k, v = (I.e4m3_bits_to_f64(x) * s for x, s in ((q8, dq), (k8, dk), (v8, dv)))
+    scale = float(np.float32(d ** -0.5))
+    O_ref, L_ref = head_attention_band_fp64(q, k, v, scale, left, right, off)
+    bo, bl = head_attention_fp8_bar_fp64(q, k, v, scale, left, right, off)
+    O, L = emulate_fp8(q8, k8, v8, dq, dk, dv, scale, left, right, off, slip)
+    seen = np.isfinite(L_ref)
+    ro = (np.abs(O - O_ref) / np.maximum(bo, 1e-300))[seen].max()
+    rl = (np.abs(L - L_ref)[seen] / np.maximum(bl[seen], 1e-300)).max()
+    return ro, rl
+
+
+FP8_CASES = [
+    (1, 1, 64, 1.0, None, None, 0),
+    (37, 37, 32, 1.0, None, 0, 0),
+    (200, 200, 128, 2.0, None, 0, 0),
+    (150, 300, 64, 1.0, 40, 10, 150),
+    (100, 1000, 96, 1.0, None, 0, 900),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES)
+def test_emulated_fp8_within_bar(case):
+    n, N, d, km, left, right, off = case
+    ro, rl = fp8_ratios(n, N, d, 970 + n + d, km, left, right, off)
+    print(f"fp8 emulation, worst error / bar: O {ro:.3f}, LSE {rl:.3f}")
+    assert ro <= 1.0 and rl <= 1.0
+
+
+@pytest.mark.parametrize("slip", ["p_coarse", "descale_v_twice", "no_descale_k"])
+def test_fp8_slips_exceed_bar(slip):
+    # three keys per row: the roundings of a row do not average out, so rounding P to a step
+    # twice e4m3's shows above the bar (the same rows stay at 0.71 of it with e4m3)
+    ro, rl = fp8_ratios(256, 3, 64, 990, 1.0, None, None, 0, slip)
+    print(f"{slip}: worst error / bar O {ro:.2f}, LSE {rl:.2f}")
+    assert max(ro, rl) > 1.0
