@@ -41,6 +41,9 @@ SIGNATURES = {
     "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int]),
     "fa_fwd_fp8": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_float] * 3 + [ctypes.c_int64] * 6
                    + [ctypes.c_float] + [ctypes.c_int64] * 2 + [ctypes.c_void_p]),
+    "fa_fwd_dropout": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
+                       + [ctypes.c_int64] * 2 + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                              + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 2),
@@ -125,6 +128,15 @@ def fwd_split_noalloc_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: 
     addresses; returns the fa_status code."""
     return load_library().fa_fwd_split_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right,
                                                n_splits, in_dtype, out_dtype, stream)
+
+
+def fwd_dropout_raw(q: int, k: int, v: int, o: int, lse: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                    scale: float, left: int, right: int, keep_prob: float, seed: int, offset: int, in_dtype: int,
+                    out_dtype: int, stream: int = 0) -> int:
+    """Call fa_fwd_dropout with raw device addresses; returns the fa_status code."""
+    return load_library().fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right,
+                                         float(keep_prob), int(seed) & (2 ** 64 - 1), int(offset) & 0xFFFFFFFF,
+                                         in_dtype, out_dtype, stream)
 
 
 def fwd_fp8_raw(q: int, k: int, v: int, o: int, lse: int, descale_q: float, descale_k: float, descale_v: float,
@@ -246,7 +258,7 @@ def tile(B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool, in_dtype: int)
 
 
 def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=None, out_dtype=None,
-        out=None, lse=None, splits: Optional[int] = None, workspace=None, mask=None, stream=None):
+        out=None, lse=None, splits: Optional[int] = None, workspace=None, mask=None, dropout=None, stream=None):
     """Exact attention forward on the GPU: returns (O, LSE).
 
     q: [B, Hq, Nq, d], k and v: [B, Hkv, Nk, d], contiguous fp16, bf16 or fp32 CUDA
@@ -259,8 +271,9 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
     queries, the call is fa_fwd itself. splits (0 = automatic, or a chunk count up to 16) cuts each
     Q-tile's keys into chunks merged afterwards (fa_fwd_split); its workspace is
     allocated when not given. mask, a bool or uint8 [B or 1, Hq or 1, Nq, Nk] tensor whose
-    nonzero entries hide keys (fa_fwd_mask), applies on top of the band. Runs on ``stream``
-    (a torch stream) or torch's current stream.
+    nonzero entries hide keys (fa_fwd_mask), applies on top of the band. dropout=(keep_prob,
+    seed, offset) drops probabilities with the Philox keep mask of fa_fwd_dropout (16-bit
+    inputs, no split or mask). Runs on ``stream`` (a torch stream) or torch's current stream.
     """
     import torch
 
@@ -302,6 +315,14 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
         raise FaError(FA_ERR_SHAPE, "all tensors must be on one device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if dropout is not None:
+        if mask is not None or splits is not None:
+            raise FaError(FA_ERR_UNSUPPORTED, "dropout takes neither a mask nor split keys")
+        keep_prob, seed, offset = dropout
+        _check(fwd_dropout_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                               N, Nk, d, scale, left, right, keep_prob, seed, offset, in_code, out_code,
+                               stream.cuda_stream))
+        return out, lse
     if mask is not None:
         if mask.device != q.device:
             raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")

@@ -19,12 +19,13 @@
 
 namespace fa {
 
-fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool out_f32, int kb, hipStream_t s) {
+fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool drop, bool out_f32, int kb,
+                       hipStream_t s) {
   switch (d) {
 #define FA_SLICE(DD)                                                                          \
   case DD:                                                                                    \
-    return bf16 ? fwd_dispatch_slice<true, DD>(p, band, am, out_f32, kb, s)                  \
-                : fwd_dispatch_slice<false, DD>(p, band, am, out_f32, kb, s);
+    return bf16 ? fwd_dispatch_slice<true, DD>(p, band, am, drop, out_f32, kb, s)            \
+                : fwd_dispatch_slice<false, DD>(p, band, am, drop, out_f32, kb, s);
     FA_SLICE(32)
     FA_SLICE(48)
     FA_SLICE(64)
@@ -137,13 +138,20 @@ struct MaskArg {
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
 };
 
+// Dropout on the probabilities (fa_fwd_dropout; keep_t == 0: none).
+struct DropArg {
+  int keep_t = 0;
+  uint64_t seed = 0;
+  uint32_t offset = 0;
+};
+
 // Every forward entry point: validation, the split plan (n_splits = 1: never split; workspace
 // is then unused unless there is a mask), the mask hull, the attention kernel and, with split
 // keys, the merge.
 fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
                   int64_t window_right, int n_splits, const MaskArg& mask, fa_dtype in_dtype, fa_dtype out_dtype,
-                  void* stream) {
+                  void* stream, const DropArg& drop = DropArg{}) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
   if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
   int64_t nq = 0, grid = 0;
@@ -154,6 +162,8 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   // fp32 inputs run their own kernel: no split keys (an automatic plan keeps one chunk), no mask
   // input, fp32 O
   if (f32_in && (n_splits > 1 || am || out_dtype != FA_F32)) return FA_ERR_UNSUPPORTED;
+  const bool dropping = drop.keep_t > 0;
+  if (dropping && (f32_in || am || n_splits != 1)) return FA_ERR_UNSUPPORTED;
   int ns = 1, kc = (int)(((Nk + 63) / 64) * 64);
   if (!f32_in) split_plan(grid, Nk, n_splits, &ns, &kc);
   if (ns == 1) kc = (int)(((Nk + 63) / 64) * 64);
@@ -201,6 +211,11 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   p.ilv = fa::interleave_groups(p.left, p.right, kUnlimited, am, B * Hkv, Nk, d);
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   p.vscale = 1.0f;
+  p.seed_lo = (unsigned)(drop.seed & 0xFFFFFFFFu);
+  p.seed_hi = (unsigned)(drop.seed >> 32);
+  p.drop_offset = drop.offset;
+  p.keep_t = dropping ? drop.keep_t : 256;
+  p.drop_scale = dropping ? 256.0f / (float)drop.keep_t : 1.0f;
   char* const wsb = reinterpret_cast<char*>(workspace);
   int2* const hull = am ? reinterpret_cast<int2*>(wsb + ml.hull_off) : nullptr;
   unsigned* const bits = am ? reinterpret_cast<unsigned*>(wsb + ml.bits_off) : nullptr;
@@ -228,7 +243,7 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
     }
   }
   if (f32_in) return fa::fwd_dispatch_f32(p, (int)d, band, s);
-  st = fa::fwd_dispatch(p, bf16, (int)d, band, am, out_f32, kb, s);
+  st = fa::fwd_dispatch(p, bf16, (int)d, band, am, dropping, out_f32, kb, s);
   if (st != FA_OK || ns == 1) return st;
   const int rows_per_wg = 256 / (int)(d / 4);  // the merge kernel's rows per work-group
   const dim3 mg((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
@@ -327,6 +342,19 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        fa_dtype out_dtype, void* stream) {
   return fwd_run(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, n_splits,
                  MaskArg{}, in_dtype, out_dtype, stream);
+}
+
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                         int64_t window_right, float keep_prob, uint64_t seed, uint32_t offset, fa_dtype in_dtype,
+                         fa_dtype out_dtype, void* stream) {
+  if (!(keep_prob > 0.0f && keep_prob <= 1.0f)) return FA_ERR_SHAPE;
+  DropArg dr;
+  dr.keep_t = std::min(256, std::max(1, (int)std::lround(256.0 * (double)keep_prob)));
+  dr.seed = seed;
+  dr.offset = offset;
+  return fwd_run(q, k, v, o, lse, nullptr, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, 1, MaskArg{},
+                 in_dtype, out_dtype, stream, dr);
 }
 
 fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

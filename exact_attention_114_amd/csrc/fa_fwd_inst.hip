@@ -13,10 +13,14 @@ namespace fa {
 
 // A mask runs on the banded kernel (with unlimited edges when there is no band).
 template <>
-fa_status fwd_dispatch_slice<(bool)FA_INST_BF16, FA_INST_D>(const Params& p, bool band, bool am, bool out_f32, int kb,
-                                                            hipStream_t s) {
+fa_status fwd_dispatch_slice<(bool)FA_INST_BF16, FA_INST_D>(const Params& p, bool band, bool am, bool drop,
+                                                            bool out_f32, int kb, hipStream_t s) {
   constexpr bool BF = (bool)FA_INST_BF16;
   constexpr int D = FA_INST_D;
+  // dropout has its own instances (no mask input with it)
+  if (drop)
+    return band ? dispatch_out<BF, D, true, false, true>(p, out_f32, kb, s)
+                : dispatch_out<BF, D, false, false, true>(p, out_f32, kb, s);
   if (am) return dispatch_out<BF, D, true, true>(p, out_f32, kb, s);
   return band ? dispatch_out<BF, D, true, false>(p, out_f32, kb, s) : dispatch_out<BF, D, false, false>(p, out_f32, kb, s);
 }

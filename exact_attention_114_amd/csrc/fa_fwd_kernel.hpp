@@ -127,6 +127,11 @@ struct Params {
   int ilv;       // (b, hkv) groups whose Q-tiles are interleaved longest first (1, 2 or 4)
   float c;       // scale * log2(e) (fp8 inputs: times the query and key descales)
   float vscale;  // fp8 inputs: the value descale, applied to O (1 otherwise)
+  // dropout (kernels built with DROP): a pair is kept iff its Philox byte is below keep_t, and kept
+  // probabilities are scaled by drop_scale = 256 / keep_t
+  unsigned seed_lo, seed_hi, drop_offset;
+  int keep_t;
+  float drop_scale;
   // optional mask (kernels built with AM), as fa_mask_prep_kernel leaves it: one bit per
   // (query, key), set where the key is hidden, in rows of am_nw 32-bit words; the (b, hq)
   // plane starts at am_bits + b*bits_sb + hq*bits_sh (strides 0 along an axis the mask shares)
@@ -272,16 +277,52 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC 2011): ten rounds over the counter (c0..c3) with the key (k0, k1) bumped by the Weyl
+// constants between rounds; each round multiplies two counter words by the round constants and
+// mixes the 32-bit halves of the products with the other words and the key.
+__device__ inline void philox4x32_10(unsigned c0, unsigned c1, unsigned c2, unsigned c3, unsigned k0, unsigned k1,
+                                     unsigned (&out)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const unsigned hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const unsigned hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+// Keep mask of a packed pair of 16-bit probabilities: word holds the random bytes of four
+// consecutive keys; the pair is keys (0, 1) or, with `upper`, (2, 3). A half is kept (0xFFFF)
+// iff its byte is below t: the two bytes go to 16-bit lanes and byte - t is negative.
+__device__ inline unsigned keep_pair_mask(unsigned word, bool upper, int t) {
+  const unsigned x = __builtin_amdgcn_perm(0u, word, upper ? 0x0C030C02u : 0x0C010C00u);
+  const s16x2 d = __builtin_bit_cast(s16x2, x) - (s16x2){(short)t, (short)t};
+  return __builtin_bit_cast(unsigned, d >> (s16x2){15, 15});
+}
+
 // Waves that share a SIMD for a tile shape: registers bound it (a d = 128 step with two key
 // blocks holds 189 VGPRs, with one 168; d = 64 about 150) and so does LDS (4 tiles of
-// 32*KB rows at the LDS pitch per work-group).
-constexpr int waves_per_simd(int d, int kb) { return d > 64 && kb == 1 ? 3 : 2; }
+// 32*KB rows at the LDS pitch per work-group). Dropout's random words need about 20 more
+// registers, which at three waves would spill.
+constexpr int waves_per_simd(int d, int kb, bool drop) { return d > 64 && kb == 1 && !drop ? 3 : 2; }
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
 // pipeline step takes KB blocks of 32 keys.
-template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB, bool AM>
+template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB, bool AM, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(const Params p) {
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
   static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 16 from 32 to 128");
   constexpr int BM = 32 * NW;
@@ -307,6 +348,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sK1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[TILE_BYTES];
+  // dropout: the four Philox words of each lane's call, exchanged within its quad (16 words a quad)
+  __shared__ __attribute__((aligned(16))) unsigned sDrop[DROP ? NW * 256 : 4];
   lds_char* const K0 = (lds_char*)sK0;
   lds_char* const V0 = (lds_char*)sV0;
   lds_char* const K1 = (lds_char*)sK1;
@@ -522,6 +565,34 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
       }
     }
   };
+  // Dropout: Philox call (key tile, row tile, plane, offset) covers 4 rows x 4 keys, byte
+  // 4 (row & 3) + (key & 3). The 4 lanes of a quad (rows 4a .. 4a+3, one half) need the calls of
+  // their 4 key groups g (keys 32 kb + 8 g + 4 h .. + 3 of a block): lane s of the quad computes
+  // group s, writes word r (row 4a + r) to slot [r][s] of the quad's LDS area, and reads back
+  // slot [s][0..3], word g of which holds its own row's 4 bytes for group g. LDS operations of a
+  // wave complete in order, so no barrier is needed.
+  unsigned drop_w[DROP ? KB : 1][4];
+  auto drop_words = [&](int jt) {
+    if constexpr (DROP) {
+      const int s = lane & 3;
+      __attribute__((address_space(3))) unsigned* slot =
+          (__attribute__((address_space(3))) unsigned*)sDrop + wave * 256 + (lane >> 2) * 16;
+      const unsigned rtile = (unsigned)(q0w + l32) >> 2;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        unsigned w[4];
+        philox4x32_10((unsigned)(jt * BN + 32 * kb + 8 * s + 4 * h) >> 2, rtile, (unsigned)(b * p.Hq + hq),
+                      p.drop_offset, p.seed_lo, p.seed_hi, w);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) slot[4 * r + s] = w[r];
+        asm volatile("" ::: "memory");
+        const u32x4 x = *(__attribute__((address_space(3))) u32x4*)(slot + 4 * s);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) drop_w[kb][g4] = x[g4];
+      }
+    }
+  };
   if constexpr (AM) {
     const unsigned* plane = p.am_bits + b * p.bits_sb + hq * p.bits_sh;
     am_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.am_nw * 4, kBufferWord3);
@@ -598,6 +669,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
       apply_am(scur, am_w);
       load_am(j + 1, am_w);  // the next step's words; its closing wait covers them
     }
+    drop_words(j);  // dropout: this tile's random bytes (no work without DROP)
 
     // ---- the MFMA stream: P V first (its operands are ready), then S_{j+1}
     u32x4 opnd[NM > 0 ? NM : 1];
@@ -653,7 +725,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
           // Keep the packing in this slot: the value is only used after the step's closing
           // branch, and the compiler would otherwise sink it out of the interleaved block.
           pin(w);
-          pcur[q >> 2][q & 3] = w;
+          // dropout hides the pair's dropped halves from P V; the sums keep every probability
+          if constexpr (DROP)
+            pcur[q >> 2][q & 3] = w & keep_pair_mask(drop_w[kb][i >> 2], (i & 2) != 0, p.keep_t);
+          else
+            pcur[q >> 2][q & 3] = w;
           const float s2 = ex[e - 1] + ex[e];
           part[q & 1] = q < 2 ? s2 : part[q & 1] + s2;
           tile_rsum = E::sum2(w, q == 0 ? 0.f : tile_rsum);
@@ -732,7 +808,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
           const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i], c, -m_run));
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i + 1], c, -m_run));
           const unsigned w = E::pack2(e0, e1);
-          pcur[q >> 2][q & 3] = w;
+          if constexpr (DROP)
+            pcur[q >> 2][q & 3] = w & keep_pair_mask(drop_w[kb][(q & 7) >> 1], (q & 1) != 0, p.keep_t);
+          else
+            pcur[q >> 2][q & 3] = w;
           prt += e0 + e1;
           rs = E::sum2(w, rs);
         }
@@ -774,7 +853,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB)))) void fa_fwd_kernel(c
   const float l_tot = wave_half_sum(l_run);
   const float lr_tot = wave_half_sum(lr_run);
   if (qrow < Nq) {
-    const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+    const float inv = lr_tot > 0.f ? (DROP ? p.drop_scale : 1.0f) / lr_tot : 0.f;
     const int64_t obase = ((int64_t)(b * p.Hq + hq) * Nq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -200,6 +200,38 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float* o, floa
                      int64_t window_left, int64_t window_right, void* stream);
 
 /*
+ * fa_fwd_dropout — fa_fwd_ex with dropout on the probabilities: the Ascend
+ * operator's keep_prob attribute (the intelliparadigm page, section 2.2, and its
+ * call in section 4.1), the Dropout step of FlashAttention-1's Algorithm 2 that
+ * the cnblogs page points to. Each (query, key) pair is kept independently and
+ * kept probabilities are scaled by the inverse of the keep probability:
+ *
+ *   O_i = sum_j (Z_ij / keep) P_ij V_j,   lse as without dropout (the undropped
+ *   softmax's statistic, which a backward recomputes P from).
+ *
+ * Z comes from Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy
+ * as 1, 2, 3", SC 2011) so that it can be drawn again: for head plane
+ * h = b * Hq + hq, query row i and key j, the call with counter
+ * (j / 4, i / 4, h, offset) and key (seed & 0xffffffff, seed >> 32) gives four
+ * 32-bit words; byte j % 4 (bits 8 (j % 4) ..) of word i % 4 is the pair's random
+ * byte, and the pair is kept iff that byte is below T = round(256 keep_prob),
+ * clamped to [1, 256]. keep is therefore T / 256 and the scale applied 256 / T.
+ *
+ *   keep_prob  in (0, 1] (FA_ERR_SHAPE otherwise); 1 keeps every pair
+ *   seed       64-bit Philox key; offset: counter word 3, so that calls with one
+ *              seed can draw independent masks (e.g. one offset per layer)
+ * The probabilities are normalised by the sum of their rounded 16-bit values as
+ * in fa_fwd, with every pair in the sum (dropped or not). Inputs FA_F16 or
+ * FA_BF16; no split keys and no mask input. Other arguments, errors and
+ * execution as fa_fwd_ex.
+ */
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                         float scale, int64_t window_left, int64_t window_right,
+                         float keep_prob, uint64_t seed, uint32_t offset, fa_dtype in_dtype,
+                         fa_dtype out_dtype, void* stream);
+
+/*
  * fa_fwd_mask — fa_fwd_split with a mask input: the Ascend operator's optional
  * boolean attn_mask (the intelliparadigm page, section 2.2), which is the Mask
  * step of FlashAttention-1's Algorithm 2 that the cnblogs page points to. Key

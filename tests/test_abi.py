@@ -375,3 +375,32 @@ def test_split_noalloc_validation():
     assert bnd.split_workspace_bytes(1, 2, 64, 64, 64, 0) == 0  # no split: no scratch, fa_fwd_ex's checks
     assert call() == bnd.FA_ERR_ALIGN
     assert call(Nq=0) == bnd.FA_ERR_SHAPE
+
+
+def test_fwd_dropout_validation():
+    """fa_fwd_dropout checks keep_prob, then the checks of fa_fwd_ex; fp32 inputs are refused."""
+    def call(q=BAD, keep=0.9, in_dtype=bnd.FA_F16, out_dtype=bnd.FA_F32, d=64, Nq=64):
+        return bnd.fwd_dropout_raw(q, BAD, BAD, BAD, BAD, 1, 2, 1, Nq, 80, d, 0.125, -1, 0, keep, 2 ** 63 + 5, 7,
+                                   in_dtype, out_dtype, 0)
+    for keep in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert call(keep=keep) == bnd.FA_ERR_SHAPE, keep
+    assert call(q=0) == bnd.FA_ERR_NULLPTR
+    assert call(Nq=0) == bnd.FA_ERR_SHAPE
+    assert call(d=40) == bnd.FA_ERR_UNSUPPORTED
+    assert call(in_dtype=bnd.FA_F32) == bnd.FA_ERR_UNSUPPORTED
+    for keep in (1.0, 0.5, 1e-6):  # 1e-6 keeps T = 1 of 256
+        assert call(keep=keep) == bnd.FA_ERR_ALIGN
+    assert call(in_dtype=bnd.FA_BF16, out_dtype=bnd.FA_BF16) == bnd.FA_ERR_ALIGN
+
+
+def test_fwd_fp8_validation():
+    """fa_fwd_fp8 checks pointers, sizes, then scale and descales (finite, > 0), then alignment."""
+    def call(q=BAD, dq=1.0, dk=0.5, dv=2.0, scale=0.125, d=64, Nq=64):
+        return bnd.fwd_fp8_raw(q, BAD, BAD, BAD, BAD, dq, dk, dv, 1, 2, 1, Nq, 80, d, scale, -1, 0, 0)
+    assert call(q=0) == bnd.FA_ERR_NULLPTR
+    assert call(Nq=0) == bnd.FA_ERR_SHAPE
+    assert call(d=40) == bnd.FA_ERR_UNSUPPORTED
+    for kw in (dict(dq=0.0), dict(dk=-1.0), dict(dv=float("nan")), dict(scale=float("inf")),
+               dict(dq=1e30, dk=1e30)):
+        assert call(**kw) == bnd.FA_ERR_SHAPE, kw
+    assert call() == bnd.FA_ERR_ALIGN
