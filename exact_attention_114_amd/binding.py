@@ -44,6 +44,9 @@ SIGNATURES = {
     "fa_fwd_dropout": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                        + [ctypes.c_int64] * 2 + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_void_p]),
+    "fa_bwd_dropout": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [ctypes.c_float]
+                       + [ctypes.c_int64] * 2 + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                              + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 2),
@@ -378,8 +381,17 @@ def bwd_ex_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk:
                                     left, right, in_dtype, o_dtype, stream)
 
 
+def bwd_dropout_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, ws: int,
+                    B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, scale: float, left: int, right: int,
+                    keep_prob: float, seed: int, offset: int, in_dtype: int, o_dtype: int, stream: int = 0) -> int:
+    """Call fa_bwd_dropout with raw device addresses; returns the fa_status code."""
+    return load_library().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                         left, right, float(keep_prob), int(seed) & (2 ** 64 - 1),
+                                         int(offset) & 0xFFFFFFFF, in_dtype, o_dtype, stream)
+
+
 def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False, window=None,
-        workspace=None, grads=None, mask=None, stream=None):
+        workspace=None, grads=None, mask=None, dropout=None, stream=None):
     """Gradients (dQ, dK, dV) of exact attention on the GPU, all float32.
 
     q, k, v as for ``fwd``; o and lse as ``fwd`` returned them (o float32 or
@@ -388,7 +400,8 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
     sequence length). The workspace (a uint8 CUDA tensor of at least
     ``bwd_workspace_bytes`` bytes, or ``bwd_mask_workspace_bytes`` with a mask) and the outputs (``grads``: contiguous
     float32 dq [B, Hq, N, d], dk and dv [B, Hkv, N, d]) are allocated when not
-    given. mask, as for ``fwd`` (and the same one the forward used), goes to fa_bwd_mask.
+    given. mask, as for ``fwd`` (and the same one the forward used), goes to fa_bwd_mask;
+    dropout=(keep_prob, seed, offset), the forward's, to fa_bwd_dropout.
     Runs on ``stream`` or torch's current stream.
     """
     import torch
@@ -438,6 +451,15 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
             raise FaError(FA_ERR_SHAPE, "grads must be contiguous float32 dq [B,Hq,Nq,d], dk and dv [B,Hkv,Nk,d]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    if dropout is not None:
+        if mask is not None:
+            raise FaError(FA_ERR_UNSUPPORTED, "dropout takes no mask")
+        keep_prob, seed, offset = dropout
+        _check(bwd_dropout_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B,
+                               Hq, Hkv, N, Nk, d, scale, left, right, keep_prob, seed, offset, in_code, o_code,
+                               stream.cuda_stream))
+        return dq, dk, dv
     if mask is not None:
         _check(bwd_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), mask.data_ptr(), sb, sh,

@@ -6,6 +6,7 @@
 // attention matrix from the forward's LSE: intelliparadigm page, section 1.2.3).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -30,7 +31,7 @@ fa_status launched() {
   return FA_OK;
 }
 
-template <bool BF16, int D, bool BAND, bool AM>
+template <bool BF16, int D, bool BAND, bool AM, bool DROP>
 fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t grid_kv, int64_t grid_q,
                      hipStream_t s) {
   constexpr int RPB = 256 / fa::prep_lanes(D);  // the prep kernel's rows per work-group
@@ -43,28 +44,41 @@ fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t gri
   if (st != FA_OK) return st;
   p.n_tiles = (int)((p.Nk + kTile - 1) / kTile);
   p.total_wg = (int)grid_kv;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves, AM>), dim3((unsigned)grid_kv), dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves, AM, DROP>), dim3((unsigned)grid_kv),
+                     dim3(kWaves * 64), 0, s, p);
   st = launched();
   if (st != FA_OK) return st;
   p.n_tiles = (int)((p.Nq + kTile - 1) / kTile);
   p.total_wg = (int)grid_q;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves, AM>), dim3((unsigned)grid_q), dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves, AM, DROP>), dim3((unsigned)grid_q),
+                     dim3(kWaves * 64), 0, s, p);
   return launched();
 }
 
-// A mask runs on the banded kernels (with unlimited edges when there is no band).
+// A mask runs on the banded kernels (with unlimited edges when there is no band); dropout has
+// its own instances (no mask input with it).
 template <bool BF16, int D>
-fa_status dispatch_band(const fa::BwdParams& p, bool band, bool am, bool o_f32, int64_t pr, int64_t gkv, int64_t gq,
-                        hipStream_t s) {
-  if (am) return launch_all<BF16, D, true, true>(p, o_f32, pr, gkv, gq, s);
-  return band ? launch_all<BF16, D, true, false>(p, o_f32, pr, gkv, gq, s)
-              : launch_all<BF16, D, false, false>(p, o_f32, pr, gkv, gq, s);
+fa_status dispatch_band(const fa::BwdParams& p, bool band, bool am, bool drop, bool o_f32, int64_t pr, int64_t gkv,
+                        int64_t gq, hipStream_t s) {
+  if (drop)
+    return band ? launch_all<BF16, D, true, false, true>(p, o_f32, pr, gkv, gq, s)
+                : launch_all<BF16, D, false, false, true>(p, o_f32, pr, gkv, gq, s);
+  if (am) return launch_all<BF16, D, true, true, false>(p, o_f32, pr, gkv, gq, s);
+  return band ? launch_all<BF16, D, true, false, false>(p, o_f32, pr, gkv, gq, s)
+              : launch_all<BF16, D, false, false, false>(p, o_f32, pr, gkv, gq, s);
 }
 
 // The optional mask of fa_bwd_mask (data == nullptr: none).
 struct MaskArg {
   const void* data = nullptr;
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
+};
+
+// The dropout of fa_bwd_dropout (keep_t == 0: none).
+struct DropArg {
+  int keep_t = 0;
+  uint64_t seed = 0;
+  uint32_t offset = 0;
 };
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -89,7 +103,8 @@ fa_status check_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, 
 fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   float* dq, float* dk, float* dv, float* workspace, const MaskArg& mask, int64_t B, int64_t Hq,
                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
-                  int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
+                  int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream,
+                  const DropArg& drop = DropArg{}) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
   int64_t ws_blk = 0, tq = 0, tk = 0;
   const fa_status st = check_bwd(B, Hq, Hkv, Nq, Nk, d, &ws_blk, &tq, &tk);
@@ -162,6 +177,12 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   p.cbits_nqb = (int)ml.nqb;
   p.cbits_sh = ml.planes_h > 1 ? Nk * ml.nqb : 0;
   p.cbits_sb = ml.planes_b > 1 ? ml.planes_h * Nk * ml.nqb : 0;
+  const bool dropping = drop.keep_t > 0;
+  p.seed_lo = (unsigned)(drop.seed & 0xFFFFFFFFu);
+  p.seed_hi = (unsigned)(drop.seed >> 32);
+  p.drop_offset = drop.offset;
+  p.keep_t = dropping ? drop.keep_t : 256;
+  p.drop_scale = dropping ? 256.0f / (float)drop.keep_t : 1.0f;
 
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const int64_t prep_rows = B * Hq * ws_blk * 32;
@@ -180,8 +201,8 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   switch (d) {
 #define FA_BWD_D(DD)                                                                            \
   case DD:                                                                                      \
-    return bf16 ? dispatch_band<true, DD>(p, band, am, o_f32, prep_rows, grid_kv, grid_q, s)    \
-                : dispatch_band<false, DD>(p, band, am, o_f32, prep_rows, grid_kv, grid_q, s);
+    return bf16 ? dispatch_band<true, DD>(p, band, am, dropping, o_f32, prep_rows, grid_kv, grid_q, s)    \
+                : dispatch_band<false, DD>(p, band, am, dropping, o_f32, prep_rows, grid_kv, grid_q, s);
     FA_BWD_D(32)
     FA_BWD_D(48)
     FA_BWD_D(64)
@@ -218,6 +239,20 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream) {
   return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, workspace, MaskArg{}, B, Hq, Hkv, Nq, Nk, d, scale, window_left,
                  window_right, in_dtype, o_dtype, stream);
+}
+
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, float* dq, float* dk, float* dv, float* workspace, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
+                         int64_t window_right, float keep_prob, uint64_t seed, uint32_t offset, fa_dtype in_dtype,
+                         fa_dtype o_dtype, void* stream) {
+  if (!(keep_prob > 0.0f && keep_prob <= 1.0f)) return FA_ERR_SHAPE;
+  DropArg dr;
+  dr.keep_t = std::min(256, std::max(1, (int)std::lround(256.0 * (double)keep_prob)));
+  dr.seed = seed;
+  dr.offset = offset;
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, workspace, MaskArg{}, B, Hq, Hkv, Nq, Nk, d, scale, window_left,
+                 window_right, in_dtype, o_dtype, stream, dr);
 }
 
 fa_status fa_bwd_mask(const void* q, const void* k, const void* v, const void* o, const float* lse,

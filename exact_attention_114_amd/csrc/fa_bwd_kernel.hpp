@@ -77,7 +77,28 @@ struct BwdParams {
   const unsigned* am_cbits;
   long long cbits_sb, cbits_sh;
   int cbits_nqb;                  // 32-row query blocks per key
+  // dropout (kernels built with DROP), as in the forward's Params: pair (i, j) of head plane
+  // b * Hq + hq is kept iff its Philox byte is below keep_t; kept terms are scaled by drop_scale
+  unsigned seed_lo, seed_hi, drop_offset;
+  int keep_t;
+  float drop_scale;
 };
+
+// 4x4 byte transpose: out[t] byte r = byte t of w[r].
+__device__ inline void byte_transpose4(const unsigned (&w)[4], unsigned (&out)[4]) {
+  // (w0.b0, w1.b0, w0.b1, w1.b1) and (w0.b2, w1.b2, w0.b3, w1.b3); the same for w2, w3
+  const unsigned a_lo = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+  const unsigned a_hi = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+  const unsigned b_lo = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+  const unsigned b_hi = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
+}
+
+// Keep test of one pair: byte `sel` of word (bits 8 sel ..) below t.
+__device__ inline bool kept(unsigned word, int sel, int t) { return (int)((word >> (8 * sel)) & 0xFFu) < t; }
 
 // One LDS swizzle for tiles that are read both as rows (ds_read_b128: 16 consecutive rows at one
 // logical 16-byte chunk must hit 16 different bank slots) and transposed (ds_read_b64_tr_b16: an
@@ -241,7 +262,7 @@ __device__ inline int lane_bytes4() {
 // (lane_id_here, the lane id formed the same opaque way, is in fa_fwd_kernel.hpp.)
 
 // ---- 2. dK/dV ---------------------------------------------------------------------------------
-template <bool BF16, int D, bool BAND, int NW, bool AM>
+template <bool BF16, int D, bool BAND, int NW, bool AM, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -256,7 +277,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   __shared__ __attribute__((aligned(256))) float sW1[64];
   constexpr bool VL = bwd_v_in_lds(D);
   __shared__ __attribute__((aligned(1024))) char sV[VL ? NW * TB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned sDrop[DROP ? NW * 256 : 4];
   static_assert(!AM || BAND, "the masked kernels are built on the banded ones");
+  static_assert(!(AM && DROP), "dropout kernels take no mask input");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -397,6 +420,30 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     const int qb = qb0 + (it % nqb);
     const int q0 = qb * 32;
     const bool mfree = mask_free(it);
+    // Dropout: the lane's key meets queries q0 + 8 g4 + 4h + r; Philox call (key / 4, query / 4)
+    // covers a 4 x 4 block, byte 4 (query & 3) + (key & 3). The quad of lanes with keys 4a .. 4a+3
+    // (one half) needs the calls of its 4 query groups g4: lane s computes group s, transposes
+    // the block's bytes so that word t holds key t's 4 query bytes, writes word t to slot [t][s]
+    // and reads back slot [s][0..3]: zw[g4] byte r is the lane's byte for query 8 g4 + 4h + r.
+    // A wave's LDS operations complete in order, so no barrier is needed.
+    unsigned zw[DROP ? 4 : 1];
+    if constexpr (DROP) {
+      const int sq = lane & 3;
+      __attribute__((address_space(3))) unsigned* slot =
+          (__attribute__((address_space(3))) unsigned*)sDrop + wave * 256 + (lane >> 2) * 16;
+      const int g = it / nqb;
+      unsigned w[4], tw4[4];
+      philox4x32_10((unsigned)(k0w + (l32 & ~3)) >> 2, (unsigned)(q0 >> 2) + 2 * sq + h,
+                    (unsigned)(b * p.Hq + hkv * G + g), p.drop_offset, p.seed_lo, p.seed_hi, w);
+      byte_transpose4(w, tw4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) slot[4 * r + sq] = tw4[r];
+      asm volatile("" ::: "memory");
+      const u32x4 x = *(__attribute__((address_space(3))) u32x4*)(slot + 4 * sq);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) zw[g4] = x[g4];
+    }
 
     // S = Q K^T, dP = dO V^T: lane holds key l32 (column), queries 8(i/4) + 4h + i%4 (rows)
     f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -443,11 +490,19 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
         }
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a[2 * r2]));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -a[2 * r2 + 1]));
-        const float d0 = p0 * (dp[i] - d4[2 * r2]);
-        const float d1 = p1 * (dp[i + 1] - d4[2 * r2 + 1]);
         const int q2 = i >> 1;
-        pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1);
-        sw[q2 >> 2][q2 & 3] = E::pack2(d0, d1);
+        if constexpr (DROP) {
+          // dV takes the kept P (scaled at the end); dS = P o (Z dP / keep - D)
+          const float g0 = kept(zw[g4], 2 * r2, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
+          const float g1 = kept(zw[g4], 2 * r2 + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
+          pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1) & keep_pair_mask(zw[g4], r2 != 0, p.keep_t);
+          sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 - d4[2 * r2]), p1 * (g1 - d4[2 * r2 + 1]));
+        } else {
+          const float d0 = p0 * (dp[i] - d4[2 * r2]);
+          const float d1 = p1 * (dp[i + 1] - d4[2 * r2 + 1]);
+          pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1);
+          sw[q2 >> 2][q2 & 3] = E::pack2(d0, d1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -469,7 +524,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   // element i of block db: key k0w + 8(i/4) + 4h + i%4, column 32db + l32
   float* dkp = p.dk + (int64_t)bk * Nk * D;
   float* dvp = p.dv + (int64_t)bk * Nk * D;
-  const float sc = p.scale;
+  const float sc = p.scale, vsc = DROP ? p.drop_scale : 1.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int key = k0w + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -478,14 +533,14 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
       for (int db = 0; db < NDB; ++db) {
         if (D % 32 != 0 && db == NDB - 1 && l32 >= 16) continue;  // padding columns of a half block
         dkp[(int64_t)key * D + 32 * db + l32] = dk[db][i] * sc;
-        dvp[(int64_t)key * D + 32 * db + l32] = dv[db][i];
+        dvp[(int64_t)key * D + 32 * db + l32] = DROP ? dv[db][i] * vsc : dv[db][i];
       }
     }
   }
 }
 
 // ---- 3. dQ ------------------------------------------------------------------------------------
-template <bool BF16, int D, bool BAND, int NW, bool AM>
+template <bool BF16, int D, bool BAND, int NW, bool AM, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -496,6 +551,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   __shared__ __attribute__((aligned(1024))) char sK1[TB];
   __shared__ __attribute__((aligned(1024))) char sV0[TB];
   __shared__ __attribute__((aligned(1024))) char sV1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned sDrop[DROP ? NW * 256 : 4];
+  static_assert(!(AM && DROP), "dropout kernels take no mask input");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -617,13 +674,40 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
         s[i] = ((x >> (8 * (i & 3) + 2 * (i >> 2))) & 1u) != 0u ? -__builtin_inff() : s[i];
       if (r + 1 < nt) load_am(j + 1);  // the next iteration's opening wait covers it
     }
+    // Dropout, as in the forward: the quad of lanes with queries 4a .. 4a+3 (one half) needs the
+    // Philox calls of its 4 key groups (keys 32j + 8g + 4h .. +3); lane s computes group s,
+    // writes word r (query 4a + r) to slot [r][s] and reads back slot [s][0..3]: zw[g] holds the
+    // lane's query's bytes for key group g, byte key & 3.
+    unsigned zw[DROP ? 4 : 1];
+    if constexpr (DROP) {
+      const int sq = lane & 3;
+      __attribute__((address_space(3))) unsigned* slot =
+          (__attribute__((address_space(3))) unsigned*)sDrop + wave * 256 + (lane >> 2) * 16;
+      unsigned wd[4];
+      philox4x32_10((unsigned)(kbase + 8 * sq + 4 * h) >> 2, (unsigned)(q0w + l32) >> 2, (unsigned)head,
+                    p.drop_offset, p.seed_lo, p.seed_hi, wd);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) slot[4 * r + sq] = wd[r];
+      asm volatile("" ::: "memory");
+      const u32x4 x = *(__attribute__((address_space(3))) u32x4*)(slot + 4 * sq);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) zw[g4] = x[g4];
+    }
     u32x4 sw[2];
 #pragma unroll
     for (int q2 = 0; q2 < 8; ++q2) {
       const int i = 2 * q2;
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -lse2));
-      sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
+      if constexpr (DROP) {
+        // dS = P o (Z dP / keep - D); key 32j + 8(i/4) + 4h + i%4 is byte i%4 of zw[i/4]
+        const float g0 = kept(zw[q2 >> 1], i & 3, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
+        const float g1 = kept(zw[q2 >> 1], (i & 3) + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
+        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 - dlt), p1 * (g1 - dlt));
+      } else {
+        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
+      }
     }
     // dQ += dS K: B operand is K read transposed
     int x1[NDB];

@@ -357,6 +357,24 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
 
 /*
+ * fa_bwd_dropout — fa_bwd_ex for a forward run with fa_fwd_dropout: the same
+ * keep_prob, seed and offset draw the same keep mask Z (the Philox bytes of
+ * fa_fwd_dropout), which is held fixed, and the chain rule through the scaled,
+ * masked probabilities gives
+ *   dV = (Z o P / keep)^T dO,  dP = (dO V^T) o Z / keep,  D_i = dO_i . O_i,
+ *   dS = P o (dP - D),  dQ = s dS K,  dK = s dS^T Q
+ * with P the undropped softmax (recomputed from the forward's LSE) and O the
+ * forward's (dropped) output. keep_prob in (0, 1] (FA_ERR_SHAPE otherwise).
+ * Other arguments, workspace, errors and execution as fa_bwd_ex.
+ */
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                         float* workspace, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                         int64_t Nk, int64_t d, float scale, int64_t window_left,
+                         int64_t window_right, float keep_prob, uint64_t seed, uint32_t offset,
+                         fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
+
+/*
  * fa_bwd_mask — fa_bwd_ex for a forward run with fa_fwd_mask: the same mask
  * (arguments and layout as fa_fwd_mask) hides the same scores, so P and dS
  * are zero there. The LSE must come from the masked forward.

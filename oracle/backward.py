@@ -34,6 +34,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 from .attention import band_visible, head_attention_band_fp64, head_attention_fp64, kv_head_of, mask_of_head
+from .dropout import head_attention_dropout_fp64, keep_threshold
 
 ROW_BLOCK = 1024  # query rows per block (bounds memory only)
 
@@ -97,7 +98,7 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
 
 def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                                       scale: float, causal: bool, band: Optional[Tuple] = None,
-                                      hidden: Optional[np.ndarray] = None
+                                      hidden: Optional[np.ndarray] = None, drop: Optional[Tuple] = None
                                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Magnitude sums (Mq [n,d], Mk [N,d], Mv [N,d]) of one head's gradients: each gradient
     element written out as a sum of products of the inputs (Q, K, V, dO), the probabilities P
@@ -113,13 +114,22 @@ def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarra
     not part of the result. ``band`` = (left, right, off) replaces ``causal`` by the band of
     ``attention.band_visible``, and ``hidden`` [n, N] (with a band) hides further keys where
     nonzero; hidden keys and rows that see no key have P = 0.
+    ``drop`` = (Z, keep_prob), with a band, is the dropout of dropout.py with the keep mask Z
+    [n, N] held fixed: the terms that pass through dV or dP carry Z_ij / keep (dV_jc =
+    sum_i (Z_ij / keep) P_ij dO_ic, dP_ij = (Z_ij / keep) sum_c dO_ic V_jc), so Mv and A take that
+    factor, and E uses the dropped output O.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     n, N = q.shape[0], k.shape[0]
-    if band is None:
+    if drop is not None:
+        if band is None or hidden is not None:
+            raise ValueError("dropout magnitudes take a band and no hidden keys")
+        O, lse = head_attention_dropout_fp64(q, k, v, scale, band[0], band[1], band[2], drop[0], drop[1])
+        zk = np.asarray(drop[0], dtype=np.float64) * (256.0 / keep_threshold(drop[1]))
+    elif band is None:
         O, lse = head_attention_fp64(q, k, v, scale, causal)
     else:
         O, lse = head_attention_band_fp64(q, k, v, scale, *band, hidden=hidden)
@@ -143,8 +153,9 @@ def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarra
                 S = np.where(np.arange(kend)[None, :] > np.arange(r0, r1)[:, None], -np.inf, S)
             P = np.exp(S - lse[r0:r1, None])
         A = np.abs(do[r0:r1]) @ np.abs(v[:kend]).T
-        W = P * (A + E[r0:r1, None])
-        mv[:kend] += P.T @ np.abs(do[r0:r1])
+        PZ = P if drop is None else P * zk[r0:r1, :kend]
+        W = PZ * A + P * E[r0:r1, None]
+        mv[:kend] += PZ.T @ np.abs(do[r0:r1])
         mq[r0:r1] = scale * (W @ np.abs(k[:kend]))
         mk[:kend] += scale * (W.T @ np.abs(q[r0:r1]))
     return mq, mk, mv

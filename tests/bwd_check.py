@@ -17,6 +17,7 @@ import numpy as np
 from exact_attention_114_amd import inputs as I
 from oracle.attention import kv_head_of
 from oracle.backward import bwd_parity_bar, head_attention_bwd_magnitude_fp64  # noqa: F401
+from oracle.dropout import keep_mask
 
 UNIT = {I.F16: 2.0 ** -11, I.BF16: 2.0 ** -8}
 
@@ -27,9 +28,12 @@ def mask_plane(mask, b, h):
     return mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]
 
 
-def magnitudes(q, k, v, do, scale, causal=False, band=None, mask=None, heads=None):
+def magnitudes(q, k, v, do, scale, causal=False, band=None, mask=None, heads=None, drop=None):
     """(Mq, Mk, Mv) over [B, Hq, Nq, d] / [B, Hkv, Nk, d] arrays; ``band`` = (left, right) with
-    off = Nk - Nq. ``heads``: an optional list of (b, hq) to fill (others stay 0)."""
+    off = Nk - Nq. ``heads``: an optional list of (b, hq) to fill (others stay 0). ``drop`` =
+    (keep_prob, seed, offset): dropout with the keep mask of head plane b * Hq + hq."""
+    if drop is not None and band is None:
+        band = (None, 0) if causal else (None, None)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     mq = np.zeros(q.shape)
@@ -39,9 +43,12 @@ def magnitudes(q, k, v, do, scale, causal=False, band=None, mask=None, heads=Non
     for b, h in todo:
         hk = kv_head_of(h, Hq, Hkv)
         bd = None if band is None else (band[0], band[1], Nk - Nq)
+        dr = None
+        if drop is not None:
+            dr = (keep_mask(drop[1], drop[2], b * Hq + h, np.arange(Nq), np.arange(Nk), drop[0]), drop[0])
         x, y, z = head_attention_bwd_magnitude_fp64(q[b, h], k[b, hk], v[b, hk], do[b, h], scale,
                                                     causal if band is None else False, band=bd,
-                                                    hidden=mask_plane(mask, b, h))
+                                                    hidden=mask_plane(mask, b, h), drop=dr)
         mq[b, h] = x
         mk[b, hk] += y
         mv[b, hk] += z

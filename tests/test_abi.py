@@ -404,3 +404,18 @@ def test_fwd_fp8_validation():
                dict(dq=1e30, dk=1e30)):
         assert call(**kw) == bnd.FA_ERR_SHAPE, kw
     assert call() == bnd.FA_ERR_ALIGN
+
+
+def test_bwd_dropout_validation():
+    """fa_bwd_dropout checks keep_prob, then the checks of fa_bwd_ex."""
+    def call(q=BAD, keep=0.9, in_dtype=bnd.FA_BF16, d=64, Nq=64):
+        return bnd.bwd_dropout_raw(q, BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, 1, 2, 1, Nq, 80, d, 0.125, -1, 0,
+                                   keep, 12345, 0, in_dtype, bnd.FA_F32, 0)
+    for keep in (0.0, 1.01, float("nan")):
+        assert call(keep=keep) == bnd.FA_ERR_SHAPE, keep
+    assert call(q=0) == bnd.FA_ERR_NULLPTR
+    assert call(Nq=0) == bnd.FA_ERR_SHAPE
+    assert call(d=40) == bnd.FA_ERR_UNSUPPORTED
+    assert call(in_dtype=bnd.FA_F32) == bnd.FA_ERR_UNSUPPORTED
+    assert call() == bnd.FA_ERR_ALIGN
+    assert call(keep=1.0) == bnd.FA_ERR_ALIGN

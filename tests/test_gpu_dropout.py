@@ -169,3 +169,101 @@ def test_dropout_masks_differ_by_seed_offset_and_head():
     h, _ = fa.fwd(q2, kd, vd, dropout=(0.5, 11, 0))
     torch.cuda.synchronize()
     assert not torch.equal(h[0, 0], h[0, 1])
+
+
+# ------------------------------------------------------------------ backward (fa_bwd_dropout)
+#
+# Bar: the backward's (bwd_check.py), with the magnitude sums of the dropout chain rule
+# (oracle.backward.head_attention_bwd_magnitude_fp64 with ``drop``): the terms through dV and dP
+# carry Z / keep and D uses the dropped output.
+
+import bwd_check  # noqa: E402
+from oracle.dropout import head_attention_bwd_dropout_fp64  # noqa: E402
+
+BWD_CASES = [  # (B, Hq, Hkv, Nq, Nk, d, dt, left, right, keep)
+    (1, 2, 1, 257, 257, 64, I.F16, None, 0, 0.9),
+    (2, 4, 2, 200, 200, 128, I.BF16, None, None, 0.5),
+    (1, 2, 2, 129, 300, 96, I.F16, None, 0, 0.3),
+    (1, 4, 1, 300, 190, 48, I.BF16, 50, 10, 0.8),
+    (1, 2, 1, 65, 65, 32, I.F16, None, None, 0.1),
+    (1, 2, 1, 300, 300, 112, I.BF16, 64, 0, 0.7),
+    (1, 2, 2, 200, 200, 80, I.F16, None, 0, 1.0),
+]
+
+
+def bwd_reference(q, k, v, do, s, left, right, Z_of, keep):
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            a, c, e = head_attention_bwd_dropout_fp64(q[b, h], k[b, h // G], v[b, h // G], do[b, h], s, left, right,
+                                                      Nk - Nq, Z_of(b, h), keep)
+            dq[b, h] = a
+            dk[b, h // G] += c
+            dv[b, h // G] += e
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dt,left,right,keep", BWD_CASES)
+def test_bwd_dropout_parity(B, Hq, Hkv, Nq, Nk, d, dt, left, right, keep):
+    seed, offset = 0xD0D0 + 3 * Nq + d, 11
+    label = f"fa_bwd_dropout B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dt} band=({left},{right}) keep={keep}"
+    print(f"[gpu] {label}", flush=True)
+    g = np.random.Generator(np.random.PCG64(seed))
+    qb, kb, vb = (I.to_bits(g.standard_normal(sh, dtype=np.float32), dt)
+                  for sh in ((B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)))
+    dob = I.to_bits(g.standard_normal((B, Hq, Nq, d), dtype=np.float32), dt)
+    q, k, v, do = (I.bits_to_f64(x, dt) for x in (qb, kb, vb, dob))
+    scale = 1.0 / math.sqrt(d)
+    s = I.scale_f32(scale)
+    G = Hq // Hkv
+
+    def Z_of(b, h):
+        return keep_mask(seed, offset, b * Hq + h, np.arange(Nq), np.arange(Nk), keep)
+
+    # the forward's O and LSE from the oracle, as the backward tests do
+    O = np.zeros(q.shape)
+    L = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            O[b, h], L[b, h] = head_attention_dropout_fp64(q[b, h], k[b, h // G], v[b, h // G], s, left, right,
+                                                           Nk - Nq, Z_of(b, h), keep)
+    dq, dk, dv = fa.bwd(to_dev(qb, dt), to_dev(kb, dt), to_dev(vb, dt), torch.from_numpy(O.astype(np.float32)).to(DEV),
+                        torch.from_numpy(L.astype(np.float32)).to(DEV), to_dev(dob, dt), scale=scale,
+                        window=(left, right), dropout=(keep, seed, offset))
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    ref = bwd_reference(q, k, v, do, s, left, right, Z_of, keep)
+    mags = bwd_check.magnitudes(q, k, v, do, s, band=(left, right), drop=(keep, seed, offset))
+    bwd_check.check(label, got, ref, mags, dt, d, Nk, G * Nq)
+
+
+@pytest.mark.parametrize("dt,causal", [(I.F16, True), (I.BF16, False)])
+def test_dropout_forward_then_backward(dt, causal):
+    """End to end: the GPU forward's O and LSE feed the GPU backward, against the oracle."""
+    B, Hq, Hkv, N, d, keep, seed, offset = 1, 4, 2, 384, 64, 0.8, 2024, 3
+    label = f"fa_fwd_dropout + fa_bwd_dropout N={N} d={d} {dt} causal={causal}"
+    print(f"[gpu] {label}", flush=True)
+    g = np.random.Generator(np.random.PCG64(seed))
+    qb, kb, vb = (I.to_bits(g.standard_normal(sh, dtype=np.float32), dt)
+                  for sh in ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)))
+    dob = I.to_bits(g.standard_normal((B, Hq, N, d), dtype=np.float32), dt)
+    qd, kd, vd, dod = (to_dev(x, dt) for x in (qb, kb, vb, dob))
+    O, L = fa.fwd(qd, kd, vd, causal=causal, dropout=(keep, seed, offset))
+    dq, dk, dv = fa.bwd(qd, kd, vd, O, L, dod, causal=causal, dropout=(keep, seed, offset))
+    torch.cuda.synchronize()
+    q, k, v, do = (I.bits_to_f64(x, dt) for x in (qb, kb, vb, dob))
+    s = I.scale_f32(1.0 / math.sqrt(d))
+    right = 0 if causal else None
+
+    def Z_of(b, h):
+        return keep_mask(seed, offset, b * Hq + h, np.arange(N), np.arange(N), keep)
+
+    got = [t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    ref = bwd_reference(q, k, v, do, s, None, right, Z_of, keep)
+    mags = bwd_check.magnitudes(q, k, v, do, s, band=(None, right), drop=(keep, seed, offset))
+    bwd_check.check(label, got, ref, mags, dt, d, N, (Hq // Hkv) * N)
