@@ -22,6 +22,11 @@ Contents
                their terms and the parity bar stated from them.
   attention.py and backward.py also hold the banded forms: a sliding window
                (left and right edges) with separate query and key lengths.
+  precision.py the parity bars for fp32 and fp8 inputs (how far an evaluation
+               in that precision may move each output, from the problem alone).
+  dropout.py   dropout on the probabilities with a Philox4x32-10 keep mask,
+               forward and backward with the mask fixed.
+  additive.py  an additive (float) attention mask, forward and backward.
   pool.py      a process pool over (batch, head) units for big shapes.
 
 Every function cites the passage of the pages it follows. Where the pages
@@ -37,3 +42,5 @@ from .brute import attention_brute  # noqa: F401
 from .backward import (attention_bwd_fp64, head_attention_bwd_fp64,  # noqa: F401
                        attention_bwd_band_fp64, head_attention_bwd_band_fp64,
                        head_attention_bwd_magnitude_fp64, bwd_parity_bar)
+from .additive import head_attention_additive_fp64, head_attention_bwd_additive_fp64  # noqa: F401
+from .dropout import head_attention_dropout_fp64, head_attention_bwd_dropout_fp64, keep_mask  # noqa: F401

@@ -34,6 +34,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 from .attention import band_visible, head_attention_band_fp64, head_attention_fp64, kv_head_of, mask_of_head
+from .additive import head_attention_additive_fp64
 from .dropout import head_attention_dropout_fp64, keep_threshold
 
 ROW_BLOCK = 1024  # query rows per block (bounds memory only)
@@ -98,7 +99,8 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
 
 def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                                       scale: float, causal: bool, band: Optional[Tuple] = None,
-                                      hidden: Optional[np.ndarray] = None, drop: Optional[Tuple] = None
+                                      hidden: Optional[np.ndarray] = None, drop: Optional[Tuple] = None,
+                                      add: Optional[np.ndarray] = None
                                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Magnitude sums (Mq [n,d], Mk [N,d], Mv [N,d]) of one head's gradients: each gradient
     element written out as a sum of products of the inputs (Q, K, V, dO), the probabilities P
@@ -117,14 +119,19 @@ def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarra
     ``drop`` = (Z, keep_prob), with a band, is the dropout of dropout.py with the keep mask Z
     [n, N] held fixed: the terms that pass through dV or dP carry Z_ij / keep (dV_jc =
     sum_i (Z_ij / keep) P_ij dO_ic, dP_ij = (Z_ij / keep) sum_c dO_ic V_jc), so Mv and A take that
-    factor, and E uses the dropped output O.
+    factor, and E uses the dropped output O. ``add`` [n, N], with a band, is the additive mask
+    of additive.py: P and O come from the masked scores (the terms are otherwise the same).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     n, N = q.shape[0], k.shape[0]
-    if drop is not None:
+    if add is not None:
+        if band is None or hidden is not None or drop is not None:
+            raise ValueError("additive-mask magnitudes take a band and nothing else")
+        O, lse = head_attention_additive_fp64(q, k, v, scale, band[0], band[1], band[2], add)
+    elif drop is not None:
         if band is None or hidden is not None:
             raise ValueError("dropout magnitudes take a band and no hidden keys")
         O, lse = head_attention_dropout_fp64(q, k, v, scale, band[0], band[1], band[2], drop[0], drop[1])
@@ -145,6 +152,10 @@ def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarra
             vis = band_visible(np.arange(r0, r1), np.arange(kend), band[0], band[1], band[2])
             if hidden is not None:
                 vis &= ~np.asarray(hidden[r0:r1, :kend], dtype=bool)
+            if add is not None:
+                Ma = np.asarray(add[r0:r1, :kend], dtype=np.float64)
+                vis &= np.isfinite(Ma)
+                S = S + np.where(vis, Ma, 0.0)
             seen = np.isfinite(lse[r0:r1])
             P = np.where(vis & seen[:, None],
                          np.exp(np.where(vis, S, 0.0) - np.where(seen, lse[r0:r1], 0.0)[:, None]), 0.0)
