@@ -47,6 +47,10 @@ SIGNATURES = {
     "fa_bwd_dropout": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                        + [ctypes.c_int64] * 2 + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_void_p]),
+    "fa_fwd_float_mask": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] + [ctypes.c_int64] * 9
+                          + [ctypes.c_float] + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "fa_bwd_float_mask": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_int] + [ctypes.c_int64] * 9
+                          + [ctypes.c_float] + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_split_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [ctypes.c_float]
                              + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 2),
@@ -204,6 +208,50 @@ def bwd_mask_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, d
                                       Nq, Nk, d, float(scale), left, right, in_dtype, o_dtype, stream)
 
 
+def fwd_float_mask_raw(q: int, k: int, v: int, o: int, lse: int, mask: int, mask_dtype: int, m_sb: int, m_sh: int,
+                       m_ld: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, scale: float, left: int,
+                       right: int, in_dtype: int, out_dtype: int, stream: int = 0) -> int:
+    """Call fa_fwd_float_mask with raw device addresses; returns the fa_status code."""
+    return load_library().fa_fwd_float_mask(q, k, v, o, lse, mask, mask_dtype, m_sb, m_sh, m_ld, B, Hq, Hkv, Nq, Nk,
+                                            d, float(scale), left, right, in_dtype, out_dtype, stream)
+
+
+def bwd_float_mask_raw(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, ws: int,
+                       mask: int, mask_dtype: int, m_sb: int, m_sh: int, m_ld: int, B: int, Hq: int, Hkv: int,
+                       Nq: int, Nk: int, d: int, scale: float, left: int, right: int, in_dtype: int, o_dtype: int,
+                       stream: int = 0) -> int:
+    """Call fa_bwd_float_mask with raw device addresses; returns the fa_status code."""
+    return load_library().fa_bwd_float_mask(q, k, v, o, lse, dout, dq, dk, dv, ws, mask, mask_dtype, m_sb, m_sh,
+                                            m_ld, B, Hq, Hkv, Nq, Nk, d, float(scale), left, right, in_dtype,
+                                            o_dtype, stream)
+
+
+def float_mask_args(mask, B: int, Hq: int, Nq: int, Nk: int) -> Tuple[int, int, int, int]:
+    """(dtype code, batch, head, row strides in elements) of a [B or 1, Hq or 1, Nq, Nk] float16 or
+    float32 additive mask tensor, a size-1 batch or head axis shared (stride 0). Rows must be
+    contiguous with a row stride that is a multiple of 4 elements (pad the key axis)."""
+    import torch
+
+    code = {torch.float16: FA_F16, torch.float32: FA_F32}.get(mask.dtype)
+    if code is None:
+        raise FaError(FA_ERR_UNSUPPORTED, "a float mask must be float16 or float32")
+    if mask.dim() != 4 or mask.shape[2] != Nq or mask.shape[3] != Nk or mask.shape[0] not in (1, B) \
+            or mask.shape[1] not in (1, Hq):
+        raise FaError(FA_ERR_SHAPE, f"mask shape {tuple(mask.shape)} is not [B or 1, Hq or 1, {Nq}, {Nk}]")
+    if mask.stride(3) != 1 or mask.stride(2) % 4 != 0:
+        raise FaError(FA_ERR_ALIGN, "mask rows must be contiguous with a row stride that is a multiple of 4 "
+                                    "elements (pad the key axis)")
+    sb = mask.stride(0) if mask.shape[0] > 1 else 0
+    sh = mask.stride(1) if mask.shape[1] > 1 else 0
+    return code, sb, sh, mask.stride(2)
+
+
+def is_float_mask(mask) -> bool:
+    import torch
+
+    return mask is not None and mask.dtype in (torch.float16, torch.float32)
+
+
 def mask_strides(mask, B: int, Hq: int, Nq: int, Nk: int) -> Tuple[int, int, int]:
     """(batch, head, row) byte strides of a [B or 1, Hq or 1, Nq, Nk] bool or uint8 mask tensor,
     a size-1 batch or head axis shared (stride 0). Rows must be contiguous and 4-byte aligned."""
@@ -274,7 +322,9 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
     queries, the call is fa_fwd itself. splits (0 = automatic, or a chunk count up to 16) cuts each
     Q-tile's keys into chunks merged afterwards (fa_fwd_split); its workspace is
     allocated when not given. mask, a bool or uint8 [B or 1, Hq or 1, Nq, Nk] tensor whose
-    nonzero entries hide keys (fa_fwd_mask), applies on top of the band. dropout=(keep_prob,
+    nonzero entries hide keys (fa_fwd_mask), applies on top of the band; a float16 or
+    float32 mask of that shape is added to the scaled scores instead (fa_fwd_float_mask,
+    -inf hiding a key; no split keys). dropout=(keep_prob,
     seed, offset) drops probabilities with the Philox keep mask of fa_fwd_dropout (16-bit
     inputs, no split or mask). Runs on ``stream`` (a torch stream) or torch's current stream.
     """
@@ -325,6 +375,16 @@ def fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, window=
         _check(fwd_dropout_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
                                N, Nk, d, scale, left, right, keep_prob, seed, offset, in_code, out_code,
                                stream.cuda_stream))
+        return out, lse
+    if is_float_mask(mask):
+        if mask.device != q.device:
+            raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
+        if splits is not None:
+            raise FaError(FA_ERR_UNSUPPORTED, "a float mask takes no split keys")
+        mcode, sb, sh, ld = float_mask_args(mask, B, Hq, N, Nk)
+        _check(fwd_float_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  mask.data_ptr(), mcode, sb, sh, ld, B, Hq, Hkv, N, Nk, d, scale, left, right,
+                                  in_code, out_code, stream.cuda_stream))
         return out, lse
     if mask is not None:
         if mask.device != q.device:
@@ -400,8 +460,9 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
     sequence length). The workspace (a uint8 CUDA tensor of at least
     ``bwd_workspace_bytes`` bytes, or ``bwd_mask_workspace_bytes`` with a mask) and the outputs (``grads``: contiguous
     float32 dq [B, Hq, N, d], dk and dv [B, Hkv, N, d]) are allocated when not
-    given. mask, as for ``fwd`` (and the same one the forward used), goes to fa_bwd_mask;
-    dropout=(keep_prob, seed, offset), the forward's, to fa_bwd_dropout.
+    given. mask, as for ``fwd`` (and the same one the forward used), goes to fa_bwd_mask
+    (float16 or float32: fa_bwd_float_mask); dropout=(keep_prob, seed, offset), the
+    forward's, to fa_bwd_dropout.
     Runs on ``stream`` or torch's current stream.
     """
     import torch
@@ -430,9 +491,13 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
         scale = 1.0 / math.sqrt(d)
     in_code = FA_F16 if q.dtype == torch.float16 else FA_BF16
     o_code = FA_F32 if o.dtype == torch.float32 else in_code
-    if mask is not None:
-        if mask.device != q.device:
-            raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
+    fmask = is_float_mask(mask)
+    if mask is not None and mask.device != q.device:
+        raise FaError(FA_ERR_SHAPE, "mask must be on the inputs' device")
+    if fmask:
+        mcode, sb, sh, ld = float_mask_args(mask, B, Hq, N, Nk)
+        need = bwd_workspace_bytes(B, Hq, N, d)
+    elif mask is not None:
         sb, sh, ld = mask_strides(mask, B, Hq, N, Nk)
         need = bwd_mask_workspace_bytes(B, Hq, N, Nk, d, sb, sh)
     else:
@@ -459,6 +524,12 @@ def bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = 
                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B,
                                Hq, Hkv, N, Nk, d, scale, left, right, keep_prob, seed, offset, in_code, o_code,
                                stream.cuda_stream))
+        return dq, dk, dv
+    if fmask:
+        _check(bwd_float_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                  mask.data_ptr(), mcode, sb, sh, ld, B, Hq, Hkv, N, Nk, d, scale, left, right,
+                                  in_code, o_code, stream.cuda_stream))
         return dq, dk, dv
     if mask is not None:
         _check(bwd_mask_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),

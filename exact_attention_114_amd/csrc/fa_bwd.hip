@@ -31,7 +31,7 @@ fa_status launched() {
   return FA_OK;
 }
 
-template <bool BF16, int D, bool BAND, bool AM, bool DROP>
+template <bool BF16, int D, bool BAND, bool AM, bool DROP, int FM = 0>
 fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t grid_kv, int64_t grid_q,
                      hipStream_t s) {
   constexpr int RPB = 256 / fa::prep_lanes(D);  // the prep kernel's rows per work-group
@@ -44,13 +44,13 @@ fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t gri
   if (st != FA_OK) return st;
   p.n_tiles = (int)((p.Nk + kTile - 1) / kTile);
   p.total_wg = (int)grid_kv;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves, AM, DROP>), dim3((unsigned)grid_kv),
+  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves, AM, DROP, FM>), dim3((unsigned)grid_kv),
                      dim3(kWaves * 64), 0, s, p);
   st = launched();
   if (st != FA_OK) return st;
   p.n_tiles = (int)((p.Nq + kTile - 1) / kTile);
   p.total_wg = (int)grid_q;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves, AM, DROP>), dim3((unsigned)grid_q),
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves, AM, DROP, FM>), dim3((unsigned)grid_q),
                      dim3(kWaves * 64), 0, s, p);
   return launched();
 }
@@ -58,8 +58,11 @@ fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t gri
 // A mask runs on the banded kernels (with unlimited edges when there is no band); dropout has
 // its own instances (no mask input with it).
 template <bool BF16, int D>
-fa_status dispatch_band(const fa::BwdParams& p, bool band, bool am, bool drop, bool o_f32, int64_t pr, int64_t gkv,
-                        int64_t gq, hipStream_t s) {
+fa_status dispatch_band(const fa::BwdParams& p, bool band, bool am, bool drop, int fm, bool o_f32, int64_t pr,
+                        int64_t gkv, int64_t gq, hipStream_t s) {
+  // the additive mask runs on the banded kernels, alone
+  if (fm == 2) return launch_all<BF16, D, true, false, false, 2>(p, o_f32, pr, gkv, gq, s);
+  if (fm == 4) return launch_all<BF16, D, true, false, false, 4>(p, o_f32, pr, gkv, gq, s);
   if (drop)
     return band ? launch_all<BF16, D, true, false, true>(p, o_f32, pr, gkv, gq, s)
                 : launch_all<BF16, D, false, false, true>(p, o_f32, pr, gkv, gq, s);
@@ -71,6 +74,13 @@ fa_status dispatch_band(const fa::BwdParams& p, bool band, bool am, bool drop, b
 // The optional mask of fa_bwd_mask (data == nullptr: none).
 struct MaskArg {
   const void* data = nullptr;
+  int64_t b_stride = 0, h_stride = 0, row_stride = 0;
+};
+
+// The additive float mask of fa_bwd_float_mask (data == nullptr: none); strides in elements.
+struct FloatMaskArg {
+  const void* data = nullptr;
+  int bytes = 0;  // 2: fp16, 4: fp32
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
 };
 
@@ -104,7 +114,7 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
                   float* dq, float* dk, float* dv, float* workspace, const MaskArg& mask, int64_t B, int64_t Hq,
                   int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
                   int64_t window_right, fa_dtype in_dtype, fa_dtype o_dtype, void* stream,
-                  const DropArg& drop = DropArg{}) {
+                  const DropArg& drop = DropArg{}, const FloatMaskArg& fmask = FloatMaskArg{}) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
   int64_t ws_blk = 0, tq = 0, tk = 0;
   const fa_status st = check_bwd(B, Hq, Hkv, Nq, Nk, d, &ws_blk, &tq, &tk);
@@ -119,6 +129,14 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
     if (Nq * mask.row_stride > ((int64_t)1 << 31) - ((int64_t)1 << 16)) return FA_ERR_SHAPE;
     if ((reinterpret_cast<uintptr_t>(mask.data) & 3u) || (mask.row_stride & 3) || (mask.b_stride & 3) ||
         (mask.h_stride & 3))
+      return FA_ERR_ALIGN;
+  }
+  const int fm = fmask.data != nullptr ? fmask.bytes : 0;
+  if (fm != 0) {
+    // as the forward's float mask; the dK/dV kernel reads up to 32 rows past Nq (as zeros)
+    if (fmask.row_stride < Nk || fmask.b_stride < 0 || fmask.h_stride < 0) return FA_ERR_SHAPE;
+    if ((Nq + 32) * fmask.row_stride * fm > ((int64_t)1 << 31) - ((int64_t)1 << 16)) return FA_ERR_SHAPE;
+    if (!aligned16(fmask.data) || (fmask.row_stride & 3) || (fmask.b_stride & 3) || (fmask.h_stride & 3))
       return FA_ERR_ALIGN;
   }
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
@@ -183,6 +201,11 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   p.drop_offset = drop.offset;
   p.keep_t = dropping ? drop.keep_t : 256;
   p.drop_scale = dropping ? 256.0f / (float)drop.keep_t : 1.0f;
+  p.fm = fmask.data;
+  p.fm_sb = fmask.b_stride;
+  p.fm_sh = fmask.h_stride;
+  p.fm_ld = (int)fmask.row_stride;
+  p.inv_scale = 1.0f / scale;
 
   const bool band = p.left != kUnlimited || p.right != kUnlimited;
   const int64_t prep_rows = B * Hq * ws_blk * 32;
@@ -201,8 +224,8 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   switch (d) {
 #define FA_BWD_D(DD)                                                                            \
   case DD:                                                                                      \
-    return bf16 ? dispatch_band<true, DD>(p, band, am, dropping, o_f32, prep_rows, grid_kv, grid_q, s)    \
-                : dispatch_band<false, DD>(p, band, am, dropping, o_f32, prep_rows, grid_kv, grid_q, s);
+    return bf16 ? dispatch_band<true, DD>(p, band, am, dropping, fm, o_f32, prep_rows, grid_kv, grid_q, s)    \
+                : dispatch_band<false, DD>(p, band, am, dropping, fm, o_f32, prep_rows, grid_kv, grid_q, s);
     FA_BWD_D(32)
     FA_BWD_D(48)
     FA_BWD_D(64)
@@ -253,6 +276,24 @@ fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void
   dr.offset = offset;
   return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, workspace, MaskArg{}, B, Hq, Hkv, Nq, Nk, d, scale, window_left,
                  window_right, in_dtype, o_dtype, stream, dr);
+}
+
+fa_status fa_bwd_float_mask(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, float* dq, float* dk, float* dv, float* workspace, const void* mask,
+                            fa_dtype mask_dtype, int64_t mask_b_stride, int64_t mask_h_stride,
+                            int64_t mask_row_stride, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                            int64_t d, float scale, int64_t window_left, int64_t window_right, fa_dtype in_dtype,
+                            fa_dtype o_dtype, void* stream) {
+  if (!mask) return FA_ERR_NULLPTR;
+  if (mask_dtype != FA_F16 && mask_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  FloatMaskArg fmk;
+  fmk.data = mask;
+  fmk.bytes = mask_dtype == FA_F16 ? 2 : 4;
+  fmk.b_stride = mask_b_stride;
+  fmk.h_stride = mask_h_stride;
+  fmk.row_stride = mask_row_stride;
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, workspace, MaskArg{}, B, Hq, Hkv, Nq, Nk, d, scale, window_left,
+                 window_right, in_dtype, o_dtype, stream, DropArg{}, fmk);
 }
 
 fa_status fa_bwd_mask(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -82,7 +82,21 @@ struct BwdParams {
   unsigned seed_lo, seed_hi, drop_offset;
   int keep_t;
   float drop_scale;
+  // additive mask (kernels built with FM = its element bytes), as in the forward's Params
+  const void* fm;
+  long long fm_sb, fm_sh;
+  int fm_ld;
+  float inv_scale;
 };
+
+// One additive-mask value (FM = 2: fp16, 4: fp32) at byte offset vo of a plane's descriptor.
+template <int FM>
+__device__ inline float fm_load1(__amdgpu_buffer_rsrc_t r, int vo) {
+  if constexpr (FM == 4)
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vo, 0, 0));
+  else
+    return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, vo, 0, 0));
+}
 
 // 4x4 byte transpose: out[t] byte r = byte t of w[r].
 __device__ inline void byte_transpose4(const unsigned (&w)[4], unsigned (&out)[4]) {
@@ -262,7 +276,7 @@ __device__ inline int lane_bytes4() {
 // (lane_id_here, the lane id formed the same opaque way, is in fa_fwd_kernel.hpp.)
 
 // ---- 2. dK/dV ---------------------------------------------------------------------------------
-template <bool BF16, int D, bool BAND, int NW, bool AM, bool DROP = false>
+template <bool BF16, int D, bool BAND, int NW, bool AM, bool DROP = false, int FM = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -280,6 +294,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   __shared__ __attribute__((aligned(16))) unsigned sDrop[DROP ? NW * 256 : 4];
   static_assert(!AM || BAND, "the masked kernels are built on the banded ones");
   static_assert(!(AM && DROP), "dropout kernels take no mask input");
+  static_assert(FM == 0 || (BAND && !AM && !DROP), "the additive mask runs on the banded kernel, alone");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -445,6 +460,19 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
       for (int g4 = 0; g4 < 4; ++g4) zw[g4] = x[g4];
     }
 
+    // Additive mask: the lane's key meets queries q0 + 8 g4 + 4h + r; value i = 4 g4 + r, read
+    // before the products so that their latency hides the loads. Query rows past Nq lie past the
+    // plane's descriptor and read zeros; keys past Nk only reach gradients that are not stored.
+    float fmv[FM ? 16 : 1];
+    if constexpr (FM != 0) {
+      const int g = it / nqb;
+      const char* plane = (const char*)p.fm + (b * p.fm_sb + (hkv * G + g) * p.fm_sh) * FM;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.fm_ld * FM, kBufferWord3);
+      const int v0 = ((q0 + 4 * h) * p.fm_ld + k0w + l32) * FM;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) fmv[i] = fm_load1<FM>(rs, v0 + (8 * (i >> 2) + (i & 3)) * p.fm_ld * FM);
+    }
     // S = Q K^T, dP = dO V^T: lane holds key l32 (column), queries 8(i/4) + 4h + i%4 (rows)
     f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
@@ -475,6 +503,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
       for (int r2 = 0; r2 < 2; ++r2) {
         const int i = 4 * g4 + 2 * r2;
         float s0 = s[i], s1 = s[i + 1];
+        if constexpr (FM != 0) {
+          s0 = __builtin_fmaf(fmv[i], p.inv_scale, s0);
+          s1 = __builtin_fmaf(fmv[i + 1], p.inv_scale, s1);
+        }
         if (diag) {
           const int pa = 8 * g4 + 2 * r2, pb = pa + 1;
           s0 = (unsigned)(pa - vlo) > width ? -__builtin_inff() : s0;
@@ -540,7 +572,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
 }
 
 // ---- 3. dQ ------------------------------------------------------------------------------------
-template <bool BF16, int D, bool BAND, int NW, bool AM, bool DROP = false>
+template <bool BF16, int D, bool BAND, int NW, bool AM, bool DROP = false, int FM = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -635,6 +667,24 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
     am_v0 = qr * p.am_nw * 4;
     if (nt > 0) load_am(j_lo);
   }
+  // Additive mask: fmw[g] holds the values of keys 32j + 8g + 4h .. +3 of the lane's query, loaded
+  // one tile ahead; reads past the plane return zeros and the key-end select replaces the scores
+  // of keys past Nk.
+  using FV = FmVec<FM == 4 ? 4 : 2>;
+  typename FV::T fmw[FM ? 4 : 1];
+  __amdgpu_buffer_rsrc_t fm_rs;
+  auto load_fm = [&](int jt) {
+    if constexpr (FM != 0) {
+      const int vo = (qr * p.fm_ld + 32 * jt + 4 * h) * FM;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) fmw[g4] = FV::load(fm_rs, vo + 8 * g4 * FM);
+    }
+  };
+  if constexpr (FM != 0) {
+    const char* plane = (const char*)p.fm + (b * p.fm_sb + hq * p.fm_sh) * FM;
+    fm_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.fm_ld * FM, kBufferWord3);
+    if (nt > 0) load_fm(j_lo);
+  }
   if (nt > 0) {
     dma_rows<D, NW>(Kp, Nk, j_lo * 32, (lds_char*)sK0, wave, ld_off);
     dma_rows<D, NW>(Vp, Nk, j_lo * 32, (lds_char*)sV0, wave, ld_off);
@@ -658,6 +708,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
       dp = E::mfma(*(const lds_u32x4*)(tv + aoff[ks]), greg[ks], dp);
     }
     const int kbase = 32 * j;
+    if constexpr (FM != 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = __builtin_fmaf(FV::at(fmw[i >> 2], i & 3), p.inv_scale, s[i]);
+      if (r + 1 < nt) load_fm(j + 1);
+    }
     if ((BAND && (kbase + 31 > min(q0w, Nq - 1) + p.off + p.right || kbase < min(q0w + 31, Nq - 1) + p.off - p.left)) ||
         kbase + 32 > Nk) {
       const int hi = khi - kbase - 4 * h, lo = klo - kbase - 4 * h;  // hide if part > hi or part < lo

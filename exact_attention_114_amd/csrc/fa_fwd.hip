@@ -19,13 +19,13 @@
 
 namespace fa {
 
-fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool drop, bool out_f32, int kb,
+fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool drop, int fm, bool out_f32, int kb,
                        hipStream_t s) {
   switch (d) {
 #define FA_SLICE(DD)                                                                          \
   case DD:                                                                                    \
-    return bf16 ? fwd_dispatch_slice<true, DD>(p, band, am, drop, out_f32, kb, s)            \
-                : fwd_dispatch_slice<false, DD>(p, band, am, drop, out_f32, kb, s);
+    return bf16 ? fwd_dispatch_slice<true, DD>(p, band, am, drop, fm, out_f32, kb, s)        \
+                : fwd_dispatch_slice<false, DD>(p, band, am, drop, fm, out_f32, kb, s);
     FA_SLICE(32)
     FA_SLICE(48)
     FA_SLICE(64)
@@ -138,6 +138,13 @@ struct MaskArg {
   int64_t b_stride = 0, h_stride = 0, row_stride = 0;
 };
 
+// The additive float mask of fa_fwd_float_mask (data == nullptr: none); strides in elements.
+struct FloatMaskArg {
+  const void* data = nullptr;
+  int bytes = 0;  // 2: fp16, 4: fp32
+  int64_t b_stride = 0, h_stride = 0, row_stride = 0;
+};
+
 // Dropout on the probabilities (fa_fwd_dropout; keep_t == 0: none).
 struct DropArg {
   int keep_t = 0;
@@ -151,7 +158,7 @@ struct DropArg {
 fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int64_t window_left,
                   int64_t window_right, int n_splits, const MaskArg& mask, fa_dtype in_dtype, fa_dtype out_dtype,
-                  void* stream, const DropArg& drop = DropArg{}) {
+                  void* stream, const DropArg& drop = DropArg{}, const FloatMaskArg& fmask = FloatMaskArg{}) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
   if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
   int64_t nq = 0, grid = 0;
@@ -164,6 +171,8 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   if (f32_in && (n_splits > 1 || am || out_dtype != FA_F32)) return FA_ERR_UNSUPPORTED;
   const bool dropping = drop.keep_t > 0;
   if (dropping && (f32_in || am || n_splits != 1)) return FA_ERR_UNSUPPORTED;
+  const int fm = fmask.data != nullptr ? fmask.bytes : 0;
+  if (fm != 0 && (f32_in || am || dropping || n_splits != 1)) return FA_ERR_UNSUPPORTED;
   int ns = 1, kc = (int)(((Nk + 63) / 64) * 64);
   if (!f32_in) split_plan(grid, Nk, n_splits, &ns, &kc);
   if (ns == 1) kc = (int)(((Nk + 63) / 64) * 64);
@@ -178,6 +187,14 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
     if (Nq * mask.row_stride > ((int64_t)1 << 31) - ((int64_t)1 << 16)) return FA_ERR_SHAPE;
     if ((reinterpret_cast<uintptr_t>(mask.data) & 3u) || (mask.row_stride & 3) || (mask.b_stride & 3) ||
         (mask.h_stride & 3))
+      return FA_ERR_ALIGN;
+  }
+  if (fm != 0) {
+    // 8- or 16-byte reads of 4 keys: rows and planes whole groups of 4 elements, the pointer
+    // 16-byte aligned; a head's plane addressed with 32-bit byte offsets
+    if (fmask.row_stride < Nk || fmask.b_stride < 0 || fmask.h_stride < 0) return FA_ERR_SHAPE;
+    if ((Nq + 32) * fmask.row_stride * fm > ((int64_t)1 << 31) - ((int64_t)1 << 16)) return FA_ERR_SHAPE;
+    if (!aligned16(fmask.data) || (fmask.row_stride & 3) || (fmask.b_stride & 3) || (fmask.h_stride & 3))
       return FA_ERR_ALIGN;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
@@ -216,6 +233,11 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
   p.drop_offset = drop.offset;
   p.keep_t = dropping ? drop.keep_t : 256;
   p.drop_scale = dropping ? 256.0f / (float)drop.keep_t : 1.0f;
+  p.fm = fmask.data;
+  p.fm_sb = fmask.b_stride;
+  p.fm_sh = fmask.h_stride;
+  p.fm_ld = (int)fmask.row_stride;
+  p.inv_scale = 1.0f / scale;
   char* const wsb = reinterpret_cast<char*>(workspace);
   int2* const hull = am ? reinterpret_cast<int2*>(wsb + ml.hull_off) : nullptr;
   unsigned* const bits = am ? reinterpret_cast<unsigned*>(wsb + ml.bits_off) : nullptr;
@@ -243,7 +265,7 @@ fa_status fwd_run(const void* q, const void* k, const void* v, void* o, float* l
     }
   }
   if (f32_in) return fa::fwd_dispatch_f32(p, (int)d, band, s);
-  st = fa::fwd_dispatch(p, bf16, (int)d, band, am, dropping, out_f32, kb, s);
+  st = fa::fwd_dispatch(p, bf16, (int)d, band, am, dropping, fm, out_f32, kb, s);
   if (st != FA_OK || ns == 1) return st;
   const int rows_per_wg = 256 / (int)(d / 4);  // the merge kernel's rows per work-group
   const dim3 mg((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
@@ -355,6 +377,23 @@ fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, f
   dr.offset = offset;
   return fwd_run(q, k, v, o, lse, nullptr, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, 1, MaskArg{},
                  in_dtype, out_dtype, stream, dr);
+}
+
+fa_status fa_fwd_float_mask(const void* q, const void* k, const void* v, void* o, float* lse, const void* mask,
+                            fa_dtype mask_dtype, int64_t mask_b_stride, int64_t mask_h_stride,
+                            int64_t mask_row_stride, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                            int64_t d, float scale, int64_t window_left, int64_t window_right, fa_dtype in_dtype,
+                            fa_dtype out_dtype, void* stream) {
+  if (!mask) return FA_ERR_NULLPTR;
+  if (mask_dtype != FA_F16 && mask_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  FloatMaskArg fmk;
+  fmk.data = mask;
+  fmk.bytes = mask_dtype == FA_F16 ? 2 : 4;
+  fmk.b_stride = mask_b_stride;
+  fmk.h_stride = mask_h_stride;
+  fmk.row_stride = mask_row_stride;
+  return fwd_run(q, k, v, o, lse, nullptr, B, Hq, Hkv, Nq, Nk, d, scale, window_left, window_right, 1, MaskArg{},
+                 in_dtype, out_dtype, stream, DropArg{}, fmk);
 }
 
 fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

@@ -13,10 +13,13 @@ namespace fa {
 
 // A mask runs on the banded kernel (with unlimited edges when there is no band).
 template <>
-fa_status fwd_dispatch_slice<(bool)FA_INST_BF16, FA_INST_D>(const Params& p, bool band, bool am, bool drop,
+fa_status fwd_dispatch_slice<(bool)FA_INST_BF16, FA_INST_D>(const Params& p, bool band, bool am, bool drop, int fm,
                                                             bool out_f32, int kb, hipStream_t s) {
   constexpr bool BF = (bool)FA_INST_BF16;
   constexpr int D = FA_INST_D;
+  // the additive mask runs on the banded kernel, alone
+  if (fm == 2) return dispatch_out<BF, D, true, false, false, 2>(p, out_f32, kb, s);
+  if (fm == 4) return dispatch_out<BF, D, true, false, false, 4>(p, out_f32, kb, s);
   // dropout has its own instances (no mask input with it)
   if (drop)
     return band ? dispatch_out<BF, D, true, false, true>(p, out_f32, kb, s)

@@ -143,6 +143,36 @@ struct Params {
   const int2* am_hull;
   long long hull_sb, hull_sh;
   int hull_nch;
+  // additive mask (kernels built with FM = its element bytes: 2 fp16, 4 fp32): score (i, j) of
+  // head (b, hq) gains fm[b*fm_sb + hq*fm_sh + i*fm_ld + j] (element strides; 0 along an axis the
+  // mask shares) before the softmax. It enters the unscaled score as M * inv_scale.
+  const void* fm;
+  long long fm_sb, fm_sh;
+  int fm_ld;
+  float inv_scale;  // 1 / scale
+};
+
+// The additive mask's values of 4 consecutive keys: 4 fp16 in two words, or 4 fp32.
+template <int FM>
+struct FmVec {
+  typedef u32x2 T;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, int vo) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, vo, 0, 0));
+  }
+  // (the word is copied out first: a bit cast applied straight to a vector element compiles to a
+  // read of element 0)
+  __device__ static float at(const T& w, int e) {
+    const unsigned x = w[e >> 1];
+    return (float)__builtin_bit_cast(f16x2, x)[e & 1];
+  }
+};
+template <>
+struct FmVec<4> {
+  typedef f32x4 T;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, int vo) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, vo, 0, 0));
+  }
+  __device__ static float at(const T& w, int e) { return w[e]; }
 };
 
 // The lane id, formed where it is used by an opaque instruction sequence: it cannot be hoisted
@@ -320,9 +350,9 @@ constexpr int waves_per_simd(int d, int kb, bool drop) { return d > 64 && kb == 
 
 // One work-group of NW waves computes BM = 32*NW query rows of one (batch, query head); a
 // pipeline step takes KB blocks of 32 keys.
-template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB, bool AM, bool DROP = false>
+template <bool BF16, int D, bool BAND, bool OUT_F32, int NW, int KB, bool AM, bool DROP = false, int FM = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP)))) void fa_fwd_kernel(const Params p) {
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP || FM != 0)))) void fa_fwd_kernel(const Params p) {
   using E = Elt<BF16>;
   static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 16 from 32 to 128");
   constexpr int BM = 32 * NW;
@@ -341,6 +371,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP)))) void fa_fwd_ke
   constexpr int RPI = NW * 1024 / ROWBL;  // tile rows between a wave's consecutive load instructions
   static_assert(NLD >= 1 && TILE_BYTES % (NW * 1024) == 0, "each wave issues the same number of tile loads");
   static_assert(!AM || BAND, "the masked kernel is built on the banded one");
+  static_assert(FM == 0 || (BAND && !AM && !DROP), "the additive mask runs on the banded kernel, alone");
 
   // Two K and two V buffers as four separate arrays: the compiler can then prove that a
   // prefetch into one buffer never aliases the reads of another, and does not stall on it.
@@ -565,6 +596,37 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP)))) void fa_fwd_ke
       }
     }
   };
+  // Additive mask: fm_w[kb][g] holds the mask values of keys kbase + 32kb + 8g + 4h .. +3 of this
+  // lane's query row (score 4g + e of block kb). One descriptor spans the plane and the whole
+  // offset goes into the vector operand, so reads past the plane return zeros; keys past the
+  // row's end read the next row, and the band and key-end selects below replace those scores.
+  using FV = FmVec<FM == 4 ? 4 : 2>;
+  typename FV::T fm_w[FM ? KB : 1][4];
+  __amdgpu_buffer_rsrc_t fm_rs;
+  auto load_fm = [&](int jt, typename FV::T(&w)[FM ? KB : 1][4]) {
+    if constexpr (FM != 0) {
+      const int row = min(q0w + (lane_id_here() & 31), Nq - 1);
+      const int vo = (row * p.fm_ld + jt * BN + 4 * h) * FM;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) w[kb][g4] = FV::load(fm_rs, vo + (32 * kb + 8 * g4) * FM);
+    }
+  };
+  // the unscaled score gains M / scale (before the band's selects)
+  auto apply_fm = [&](f32x16(&st)[KB], const typename FV::T(&w)[FM ? KB : 1][4]) {
+    if constexpr (FM != 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kb][i] = __builtin_fmaf(FV::at(w[kb][i >> 2], i & 3), p.inv_scale, st[kb][i]);
+    }
+  };
+  if constexpr (FM != 0) {
+    const char* plane = (const char*)p.fm + (b * p.fm_sb + hq * p.fm_sh) * FM;
+    fm_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.fm_ld * FM, kBufferWord3);
+    load_fm(j_lo, fm_w);
+  }
   // Dropout: Philox call (key tile, row tile, plane, offset) covers 4 rows x 4 keys, byte
   // 4 (row & 3) + (key & 3). The 4 lanes of a quad (rows 4a .. 4a+3, one half) need the calls of
   // their 4 key groups g (keys 32 kb + 8 g + 4 h .. + 3 of a block): lane s of the quad computes
@@ -664,6 +726,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP)))) void fa_fwd_ke
           st[kb][i] = hide ? -__builtin_inff() : st[kb][i];
         }
     };
+    if constexpr (FM != 0) {
+      apply_fm(scur, fm_w);
+      load_fm(j + 1, fm_w);  // the next step's values
+    }
     if (need_mask) mask(scur);
     if constexpr (AM) {
       apply_am(scur, am_w);
@@ -789,6 +855,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP)))) void fa_fwd_ke
           st[kb] = (f32x16){};
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) st[kb] = E::mfma(src[2 * ks], qreg[ks], st[kb]);
+        }
+        if constexpr (FM != 0) {
+          typename FV::T wj[KB][4];
+          load_fm(j, wj);
+          apply_fm(st, wj);
         }
         if (need_mask) mask(st);
         if constexpr (AM) {

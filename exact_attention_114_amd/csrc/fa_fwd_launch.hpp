@@ -16,7 +16,8 @@ namespace fa {
 constexpr int kFwdWaves = 4;
 
 // The attention kernel for one problem (p filled by the host), after its argument checks.
-fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool drop, bool out_f32, int kb,
+// fm: the additive mask's element bytes (0: none, 2: fp16, 4: fp32).
+fa_status fwd_dispatch(const Params& p, bool bf16, int d, bool band, bool am, bool drop, int fm, bool out_f32, int kb,
                        hipStream_t s);
 // The fp32-input kernel (fa_fwd_f32.hip): no split keys, no mask input, fp32 O.
 fa_status fwd_dispatch_f32(const Params& p, int d, bool band, hipStream_t s);
@@ -29,14 +30,15 @@ void merge_dispatch(bool bf16, int d, bool out_f32, dim3 mg, const float* ow, co
 
 // One slice: defined in the slice's object only.
 template <bool BF16, int D>
-fa_status fwd_dispatch_slice(const Params& p, bool band, bool am, bool drop, bool out_f32, int kb, hipStream_t s);
+fa_status fwd_dispatch_slice(const Params& p, bool band, bool am, bool drop, int fm, bool out_f32, int kb,
+                             hipStream_t s);
 template <bool BF16, int D>
 void merge_dispatch_slice(bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse, int64_t rows,
                           int nsplit, hipStream_t s);
 
 #define FA_FWD_SLICE_DECL(BF, D)                                                                              \
   template <>                                                                                                 \
-  fa_status fwd_dispatch_slice<BF, D>(const Params& p, bool band, bool am, bool drop, bool out_f32, int kb,      \
+  fa_status fwd_dispatch_slice<BF, D>(const Params& p, bool band, bool am, bool drop, int fm, bool out_f32, int kb, \
                                       hipStream_t s);                                                           \
   template <>                                                                                                 \
   void merge_dispatch_slice<BF, D>(bool out_f32, dim3 mg, const float* ow, const float* lw, void* o, float* lse,  \
@@ -54,10 +56,10 @@ FA_FWD_SLICE_DECL_D(128)
 
 #ifdef FA_INST_D
 // ---- kernel launches, compiled in the slice objects only
-template <bool BF16, int D, bool BAND, bool OUT_F32, int KB, bool AM, bool DROP>
+template <bool BF16, int D, bool BAND, bool OUT_F32, int KB, bool AM, bool DROP, int FM>
 fa_status launch(const Params& p, hipStream_t stream) {
   // The K/V double buffer is static LDS inside the kernel (4 tiles of 32*KB rows).
-  auto kern = fa_fwd_kernel<BF16, D, BAND, OUT_F32, kFwdWaves, KB, AM, DROP>;
+  auto kern = fa_fwd_kernel<BF16, D, BAND, OUT_F32, kFwdWaves, KB, AM, DROP, FM>;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(kFwdWaves * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -67,17 +69,22 @@ fa_status launch(const Params& p, hipStream_t stream) {
   return FA_OK;
 }
 
-template <bool BF16, int D, bool BAND, bool OUT_F32, bool AM, bool DROP>
+// The additive mask at d > 64 takes one key block per step only (its values need registers).
+template <bool BF16, int D, bool BAND, bool OUT_F32, bool AM, bool DROP, int FM>
 fa_status dispatch_kb(const Params& p, int kb, hipStream_t s) {
-  if constexpr (D > 64) {
-    if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1, AM, DROP>(p, s);
+  if constexpr (D > 64 && FM != 0) {
+    return launch<BF16, D, BAND, OUT_F32, 1, AM, DROP, FM>(p, s);
+  } else {
+    if constexpr (D > 64) {
+      if (kb == 1) return launch<BF16, D, BAND, OUT_F32, 1, AM, DROP, FM>(p, s);
+    }
+    return launch<BF16, D, BAND, OUT_F32, 2, AM, DROP, FM>(p, s);
   }
-  return launch<BF16, D, BAND, OUT_F32, 2, AM, DROP>(p, s);
 }
-template <bool BF16, int D, bool BAND, bool AM, bool DROP = false>
+template <bool BF16, int D, bool BAND, bool AM, bool DROP = false, int FM = 0>
 fa_status dispatch_out(const Params& p, bool out_f32, int kb, hipStream_t s) {
-  return out_f32 ? dispatch_kb<BF16, D, BAND, true, AM, DROP>(p, kb, s)
-                 : dispatch_kb<BF16, D, BAND, false, AM, DROP>(p, kb, s);
+  return out_f32 ? dispatch_kb<BF16, D, BAND, true, AM, DROP, FM>(p, kb, s)
+                 : dispatch_kb<BF16, D, BAND, false, AM, DROP, FM>(p, kb, s);
 }
 #endif
 

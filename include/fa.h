@@ -269,6 +269,35 @@ fa_status fa_fwd_mask(const void* q, const void* k, const void* v, void* o, floa
                       fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
 
 /*
+ * fa_fwd_float_mask — fa_fwd_ex with a float attn_mask: the Ascend operator's
+ * optional attn_mask in its fp16 and fp32 forms (the intelliparadigm page,
+ * section 2.2). The pages give those forms no meaning; the reading taken is
+ * an additive mask (PyTorch's convention for a float attention mask): score
+ * (i, j) of head (b, h) becomes
+ *   scale * q_i . k_j + mask[b * mask_b_stride + h * mask_h_stride + i * mask_row_stride + j]
+ * (strides in elements) before the softmax, on top of the band. -inf hides the
+ * key; a row whose visible keys are all hidden gets O = 0 and lse = -inf. The
+ * lse is the logsumexp of the masked scores. Entries must be finite or -inf.
+ *
+ *   mask            device pointer, 16-byte aligned, owned by the caller; read only
+ *   mask_dtype      FA_F16 or FA_F32 (FA_ERR_UNSUPPORTED otherwise)
+ *   mask_b_stride, mask_h_stride   elements between batch elements and between
+ *                   query heads; 0 shares one plane across them. Multiples of 4
+ *   mask_row_stride elements between query rows: >= Nk, a multiple of 4, with
+ *                   (Nq + 32) * mask_row_stride * (element bytes) at most 2^31 - 2^16
+ * Inputs FA_F16 or FA_BF16; no split keys. The attention kernel reads the mask
+ * values of the tiles it visits (the band still skips whole tiles). Other
+ * arguments, errors and execution as fa_fwd_ex; a NULL mask is FA_ERR_NULLPTR,
+ * a misaligned one FA_ERR_ALIGN.
+ */
+fa_status fa_fwd_float_mask(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const void* mask, fa_dtype mask_dtype, int64_t mask_b_stride,
+                            int64_t mask_h_stride, int64_t mask_row_stride, int64_t B,
+                            int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                            float scale, int64_t window_left, int64_t window_right,
+                            fa_dtype in_dtype, fa_dtype out_dtype, void* stream);
+
+/*
  * fa_fwd_mask_workspace_bytes — bytes of workspace fa_fwd_mask needs for a mask
  * with these batch and head strides (0: shared along that axis), each part
  * starting at a 256-byte boundary: the split partials of
@@ -373,6 +402,23 @@ fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void
                          int64_t Nk, int64_t d, float scale, int64_t window_left,
                          int64_t window_right, float keep_prob, uint64_t seed, uint32_t offset,
                          fa_dtype in_dtype, fa_dtype o_dtype, void* stream);
+
+/*
+ * fa_bwd_float_mask — fa_bwd_ex for a forward run with fa_fwd_float_mask: the
+ * same additive mask (arguments and layout as fa_fwd_float_mask) enters the
+ * recomputed scores, so P and dS are those of the masked softmax; the mask
+ * takes no gradient. The LSE must come from the masked forward.
+ * Other arguments, workspace, errors and execution as fa_bwd_ex; a NULL mask is
+ * FA_ERR_NULLPTR, a misaligned one FA_ERR_ALIGN.
+ */
+fa_status fa_bwd_float_mask(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                            float* workspace, const void* mask, fa_dtype mask_dtype,
+                            int64_t mask_b_stride, int64_t mask_h_stride,
+                            int64_t mask_row_stride, int64_t B, int64_t Hq, int64_t Hkv,
+                            int64_t Nq, int64_t Nk, int64_t d, float scale,
+                            int64_t window_left, int64_t window_right, fa_dtype in_dtype,
+                            fa_dtype o_dtype, void* stream);
 
 /*
  * fa_bwd_mask — fa_bwd_ex for a forward run with fa_fwd_mask: the same mask

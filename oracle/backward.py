@@ -157,8 +157,9 @@ def head_attention_bwd_magnitude_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarra
                 vis &= np.isfinite(Ma)
                 S = S + np.where(vis, Ma, 0.0)
             seen = np.isfinite(lse[r0:r1])
-            P = np.where(vis & seen[:, None],
-                         np.exp(np.where(vis, S, 0.0) - np.where(seen, lse[r0:r1], 0.0)[:, None]), 0.0)
+            keep = vis & seen[:, None]
+            # (exponents formed only where kept: a hidden pair's would be discarded anyway)
+            P = np.where(keep, np.exp(np.where(keep, S - np.where(seen, lse[r0:r1], 0.0)[:, None], -np.inf)), 0.0)
         else:
             if causal:
                 S = np.where(np.arange(kend)[None, :] > np.arange(r0, r1)[:, None], -np.inf, S)

@@ -419,3 +419,28 @@ def test_bwd_dropout_validation():
     assert call(in_dtype=bnd.FA_F32) == bnd.FA_ERR_UNSUPPORTED
     assert call() == bnd.FA_ERR_ALIGN
     assert call(keep=1.0) == bnd.FA_ERR_ALIGN
+
+
+def test_float_mask_validation():
+    """fa_fwd_float_mask and fa_bwd_float_mask check the mask argument on the host: NULL, its type,
+    strides (>= Nk rows, non-negative planes, 32-bit plane offsets), alignment; fp32 inputs are
+    refused."""
+    def fwd(mask=BAD, mdt=bnd.FA_F16, sb=0, sh=0, ld=80, Nk=80, in_dtype=bnd.FA_F16, d=64):
+        return bnd.fwd_float_mask_raw(BAD, BAD, BAD, BAD, BAD, mask, mdt, sb, sh, ld, 1, 2, 1, 64, Nk, d, 0.125, -1,
+                                      0, in_dtype, bnd.FA_F32, 0)
+
+    def bwd(mask=BAD, mdt=bnd.FA_F32, ld=80):
+        return bnd.bwd_float_mask_raw(BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, mask, mdt, 0, 0, ld, 1, 2, 1,
+                                      64, 80, 64, 0.125, -1, 0, bnd.FA_BF16, bnd.FA_F32, 0)
+    for call in (fwd, bwd):
+        assert call(mask=0) == bnd.FA_ERR_NULLPTR
+        assert call(mdt=bnd.FA_BF16) == bnd.FA_ERR_UNSUPPORTED
+        assert call(ld=76) == bnd.FA_ERR_SHAPE
+        assert call(ld=((1 << 31) // (2 * 96) // 4 + 1) * 4) == bnd.FA_ERR_SHAPE
+        assert call(ld=84) == bnd.FA_ERR_ALIGN  # the misaligned pointer
+        assert call(mask=0x1000, ld=82) == bnd.FA_ERR_ALIGN  # a row stride not a multiple of 4
+    assert fwd(sh=-4) == bnd.FA_ERR_SHAPE
+    assert fwd(sb=6, mask=0x1000) == bnd.FA_ERR_ALIGN
+    assert fwd(d=40) == bnd.FA_ERR_UNSUPPORTED
+    assert fwd(in_dtype=bnd.FA_F32) == bnd.FA_ERR_UNSUPPORTED
+    assert fwd(mask=0x1000) == bnd.FA_ERR_ALIGN  # a good mask: the misaligned q stops it
