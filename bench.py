@@ -21,6 +21,11 @@ workloads the library splits, a second line without the split.
 one step = one fa_bwd call (row statistics, dK/dV and dQ kernels) with O and LSE from fa_fwd.
 --calibrate-copy runs, after the timed region, one elementwise copy kernel of a known
 size, used to scale the FETCH_SIZE / WRITE_SIZE hardware counters into bytes.
+--variant V times another form of the forward on the workload's shape instead and prints its
+own line (not the bench line): fp32 (the inputs kept in fp32: fa_fwd_ex on the fp32 matrix
+cores, peak 157.3 TFLOP/s), fp8 (e4m3 inputs with per-tensor descales: fa_fwd_fp8, peak
+5000), dropout (keep 0.9: fa_fwd_dropout) or alibi (an fp16 additive distance bias
+-2^-3 |i - j| shared by the heads: fa_fwd_float_mask).
 
   python bench.py --summarize-counters FETCH_CSV WRITE_CSV --workload NAME --command CMD
 
@@ -157,6 +162,64 @@ def time_gpu(w, steps: int, warmup: int, splits: int = 0, mask=None):
     ev_ms = ev0.elapsed_time(ev1)
     assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
     return wall, ev_ms / steps
+
+
+VARIANT_PEAK = {"fp32": 157.3, "fp8": 5000.0, "dropout": 2500.0, "alibi": 2500.0}
+
+
+def time_variant(w, variant: str, steps: int, warmup: int):
+    """HIP-event milliseconds per forward call of the workload's shape in another form (the
+    --variant option): fp32 inputs, fp8 inputs, dropout or an additive fp16 distance bias."""
+    import torch
+
+    import exact_attention_114_amd as fa
+    from exact_attention_114_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    window = w.band if (w.window_left is not None or w.nk != w.N) else None
+    causal = w.causal if window is None else False
+    if variant == "fp32":
+        q, k, v = (torch.from_numpy(x).to(dev) for x in I.draw_qkv_f32(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed,
+                                                                         w.k_mult, w.nk))
+
+        def call():
+            fa.fwd(q, k, v, scale=w.scale, causal=causal, window=window, stream=stream)
+    elif variant == "fp8":
+        (q8, k8, v8), ds = I.draw_qkv_fp8(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, w.k_mult, w.nk)
+        q, k, v = (torch.from_numpy(x).to(dev) for x in (q8, k8, v8))
+        del q8, k8, v8
+
+        def call():
+            fa.fwd_fp8(q, k, v, *ds, scale=w.scale, causal=causal, window=window, stream=stream)
+    elif variant in ("dropout", "alibi"):
+        qkv = I.workload_qkv(w)
+        q, k, v = (to_device(x, w.dtype, dev) for x in (qkv.q, qkv.k, qkv.v))
+        del qkv
+        mask = None
+        if variant == "alibi":
+            i = torch.arange(w.N, device=dev, dtype=torch.float32)[:, None] + (w.nk - w.N)
+            j = torch.arange(w.nk, device=dev, dtype=torch.float32)[None, :]
+            mask = (-0.125 * (i - j).abs()).to(torch.float16)[None, None].contiguous()
+            if w.nk % 4:
+                raise SystemExit("--variant alibi needs Nk a multiple of 4")
+
+        def call():
+            fa.fwd(q, k, v, scale=w.scale, causal=causal, window=window, stream=stream,
+                   dropout=(0.9, 1234, 0) if variant == "dropout" else None, mask=mask)
+    else:
+        raise SystemExit(f"--variant {variant}: one of fp32, fp8, dropout, alibi")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
 
 
 def bench_mask(w, kind: str):
@@ -394,6 +457,7 @@ def main():
     ap.add_argument("--mask", default="", help="'document': packed-document byte mask (fa_fwd_mask)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="")
+    ap.add_argument("--variant", default="", help="fp32, fp8, dropout or alibi: time that form instead")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -417,6 +481,13 @@ def main():
     binding.load_library()  # fails loudly if the HIP library is missing
 
     w = I.WORKLOADS[args.workload]
+    if args.variant:
+        ms = time_variant(w, args.variant, args.steps, args.warmup)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        peak = VARIANT_PEAK[args.variant]
+        print(json.dumps({"variant": args.variant, "workload": w.name, "steps": args.steps, "ms": round(ms, 5),
+                          "tflops": round(tf, 2), "peak": peak, "frac": round(tf / peak, 4)}), flush=True)
+        return
     if args.bwd:
         if args.sweep:
             for name in I.WORKLOADS:

@@ -267,3 +267,63 @@ def test_dropout_forward_then_backward(dt, causal):
     ref = bwd_reference(q, k, v, do, s, None, right, Z_of, keep)
     mags = bwd_check.magnitudes(q, k, v, do, s, band=(None, right), drop=(keep, seed, offset))
     bwd_check.check(label, got, ref, mags, dt, d, N, (Hq // Hkv) * N)
+
+
+def test_dropout_at_the_benchmark_shape_sampled_rows():
+    """fa_fwd_dropout on the full-size causal workload the benchmark times (B=4, H=48, N=16384,
+    d=64, fp16, keep 0.9): sampled rows of four heads against the oracle, each row computed
+    alone at its own position with its own row of the keep mask."""
+    w = I.WORKLOADS["causal_b4_h48_n16384_d64_f16"]
+    keep, seed, offset = 0.9, 1234, 0
+    print(f"[gpu] fa_fwd_dropout {w.name} keep={keep}", flush=True)
+    qkv = I.workload_qkv(w)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v))
+    O, L = fa.fwd(qd, kd, vd, scale=w.scale, causal=True, dropout=(keep, seed, offset))
+    torch.cuda.synchronize()
+    O = O.cpu().numpy()
+    L = L.cpu().numpy()
+    s = I.scale_f32(w.scale)
+    rng = np.random.default_rng(w.seed)
+    inv_keep = 256.0 / keep_threshold(keep)
+    worst = 0.0
+    for b, h in [(0, 0), (1, 5), (2, 24), (3, 47)]:
+        k = I.bits_to_f64(qkv.k[b, h], w.dtype)
+        v = I.bits_to_f64(qkv.v[b, h], w.dtype)
+        rows = sorted({0, 1, 127, 128, 8191, w.N - 1} | {int(x) for x in rng.integers(0, w.N, 10)})
+        for i in rows:
+            q = I.bits_to_f64(qkv.q[b, h, i:i + 1], w.dtype)
+            Z = keep_mask(seed, offset, b * w.Hq + h, np.array([i]), np.arange(w.N), keep)
+            O_ref, L_ref = head_attention_dropout_fp64(q, k, v, s, None, 0, i, Z, keep)
+            assert abs(L[b, h, i] - L_ref[0]) <= TOL_LSE * max(1.0, abs(L_ref[0]))
+            P = np.exp(np.where(np.arange(w.N) <= i, s * (q @ k.T)[0], -np.inf) - L_ref[0])
+            bar = TOL_O[w.dtype] * np.maximum(1.0, (P * Z[0] * inv_keep) @ np.abs(v) + np.abs(O_ref[0]))
+            ratio = (np.abs(O[b, h, i] - O_ref[0]) / bar).max()
+            worst = max(worst, ratio)
+            assert ratio <= 1.0, f"row ({b}, {h}, {i}): error / bar {ratio:.3f}"
+    print(f"[gpu]   worst error / bar {worst:.3f}", flush=True)
+
+
+def test_dropout_backward_larger():
+    """Forward then backward with dropout on a causal N = 2048 grouped-query case, every gradient
+    element against the oracle."""
+    B, Hq, Hkv, N, d, dt, keep, seed, offset = 1, 4, 2, 2048, 128, I.BF16, 0.85, 77, 9
+    label = f"fa_fwd_dropout + fa_bwd_dropout N={N} d={d} {dt}"
+    print(f"[gpu] {label}", flush=True)
+    g = np.random.Generator(np.random.PCG64(seed))
+    qb, kb, vb = (I.to_bits(g.standard_normal(sh, dtype=np.float32), dt)
+                  for sh in ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)))
+    dob = I.to_bits(g.standard_normal((B, Hq, N, d), dtype=np.float32), dt)
+    qd, kd, vd, dod = (to_dev(x, dt) for x in (qb, kb, vb, dob))
+    O, L = fa.fwd(qd, kd, vd, causal=True, dropout=(keep, seed, offset))
+    dq, dk, dv = fa.bwd(qd, kd, vd, O, L, dod, causal=True, dropout=(keep, seed, offset))
+    torch.cuda.synchronize()
+    q, k, v, do = (I.bits_to_f64(x, dt) for x in (qb, kb, vb, dob))
+    s = I.scale_f32(1.0 / math.sqrt(d))
+
+    def Z_of(b, h):
+        return keep_mask(seed, offset, b * Hq + h, np.arange(N), np.arange(N), keep)
+
+    got = [t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    ref = bwd_reference(q, k, v, do, s, None, 0, Z_of, keep)
+    mags = bwd_check.magnitudes(q, k, v, do, s, band=(None, 0), drop=(keep, seed, offset))
+    bwd_check.check(label, got, ref, mags, dt, d, N, (Hq // Hkv) * N)

@@ -206,3 +206,41 @@ def test_float_mask_forward_then_backward(B, Hq, Hkv, Nq, Nk, d, dt, left, right
                 + np.where(np.isfinite(Lr), np.abs(Lr), 0.0)[:, None]
             amax = max(amax, float(np.where(vis, a, 0.0).max()))
     bwd_check.check(label, got, ref, mags, dt, d, Nk, G * Nq, extra_rel=2 * 4 * E32 * amax)
+
+
+def test_alibi_at_a_benchmark_shape_sampled_rows():
+    """fa_fwd_float_mask on the full-size causal N = 8192 workload (B=4, H=48, d=64, fp16) with an
+    fp16 distance bias -2^-3 |i - j| shared by the heads (the bench.py --variant alibi form):
+    sampled rows of four heads against the oracle."""
+    w = I.WORKLOADS["causal_b4_h48_n8192_d64_f16"]
+    print(f"[gpu] fa_fwd_float_mask {w.name} alibi", flush=True)
+    qkv = I.workload_qkv(w)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (qkv.q, qkv.k, qkv.v))
+    i = torch.arange(w.N, device=DEV, dtype=torch.float32)[:, None]
+    j = torch.arange(w.N, device=DEV, dtype=torch.float32)[None, :]
+    Mt = (-0.125 * (i - j).abs()).to(torch.float16)[None, None].contiguous()
+    O, L = fa.fwd(qd, kd, vd, scale=w.scale, causal=True, mask=Mt)
+    torch.cuda.synchronize()
+    O = O.cpu().numpy()
+    L = L.cpu().numpy()
+    s = I.scale_f32(w.scale)
+    rng = np.random.default_rng(w.seed + 5)
+    rows = np.array(sorted({0, 1, 127, 128, 4095, w.N - 1} | {int(x) for x in rng.integers(0, w.N, 12)}))
+    M = Mt[0, 0][torch.from_numpy(rows).to(DEV)].to(torch.float64).cpu().numpy()
+    worst = 0.0
+    for b, h in [(0, 0), (1, 5), (2, 24), (3, 47)]:
+        k = I.bits_to_f64(qkv.k[b, h], w.dtype)
+        v = I.bits_to_f64(qkv.v[b, h], w.dtype)
+        for n, r in enumerate(rows):
+            q = I.bits_to_f64(qkv.q[b, h, r:r + 1], w.dtype)
+            O_ref, L_ref = head_attention_additive_fp64(q, k, v, s, None, 0, int(r), M[n:n + 1])
+            vis = np.arange(w.N) <= r
+            sS = s * (q @ k.T)[0]
+            P = np.where(vis, np.exp(np.where(vis, sS + M[n] - L_ref[0], -np.inf)), 0.0)
+            eps = 4 * E32 * (np.abs(sS) + np.abs(M[n]) + abs(L_ref[0]))
+            assert abs(L[b, h, r] - L_ref[0]) <= TOL_LSE * max(1.0, abs(L_ref[0])) + (P * eps).sum()
+            bar = TOL_O[w.dtype] * np.maximum(1.0, P @ np.abs(v) + np.abs(O_ref[0])) + (P * eps) @ np.abs(v - O_ref[0])
+            ratio = (np.abs(O[b, h, r] - O_ref[0]) / bar).max()
+            worst = max(worst, ratio)
+            assert ratio <= 1.0, f"row ({b}, {h}, {r}): error / bar {ratio:.3f}"
+    print(f"[gpu]   worst error / bar {worst:.3f}", flush=True)
