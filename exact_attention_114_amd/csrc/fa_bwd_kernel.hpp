@@ -9,7 +9,7 @@
 //   dQ = s dS K,  dK = s dS^T Q  (K/V-head gradients summed over the head's query group)
 // Three kernels:
 //   1. prep: per query row, D = rowsum(dO o O) and the LSE in log2 units, into a workspace laid
-//      out per 32-row block as [32 LSE*log2(e) | 32 D] (rows past Nq hold zeros; a row that
+//      out per 32-row block as [32 LSE*log2(e) | 32 -D] (rows past Nq hold zeros; a row that
 //      sees no key holds +inf, which makes its P zero).
 // Masks are the forward's band (causal is left unlimited, right 0; query row i sits at key
 // position i + Nk - Nq); each kernel visits only the tiles a band touches.
@@ -41,7 +41,7 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* ws;     // per (b, hq) and 32-row block: 32 floats LSE*log2(e), then 32 floats D
+  float* ws;     // per (b, hq) and 32-row block: 32 floats LSE*log2(e), then 32 floats -D
   int B, Hq, Hkv;
   int Nq, Nk;    // query and key rows per head
   int off;       // Nk - Nq: key position of query row 0
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const BwdParams p) {
   if (row < rows && ch == 0) {
     float* w = p.ws + (head * p.ws_blk + i / 32) * 64;
     w[i % 32] = lse2;
-    w[32 + i % 32] = acc;
+    w[32 + i % 32] = -acc;  // -D: the dK/dV kernel's dP accumulator starts from it
   }
 }
 
@@ -422,10 +422,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   const float c = p.c;
 
   if (n_it > 0) issue_loads(0, (lds_char*)sQ0, (lds_char*)sG0, sW0);
-  for (int it = 0; it < n_it; ++it) {
+  // One iteration; even iterations read the 0 buffers and odd ones the 1 buffers. The loop runs
+  // them in pairs, so each buffer's address is a compile-time constant of its iteration and the
+  // LDS reads take it as an immediate offset.
+  auto iter = [&](const int it, auto oddc) {
+    constexpr bool odd = decltype(oddc)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const bool odd = it & 1;
     const lds_char* tq = (const lds_char*)(odd ? sQ1 : sQ0);
     const lds_char* tg = (const lds_char*)(odd ? sG1 : sG0);
     const float* tw = odd ? sW1 : sW0;
@@ -473,8 +476,18 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
 #pragma unroll
       for (int i = 0; i < 16; ++i) fmv[i] = fm_load1<FM>(rs, v0 + (8 * (i >> 2) + (i & 3)) * p.fm_ld * FM);
     }
-    // S = Q K^T, dP = dO V^T: lane holds key l32 (column), queries 8(i/4) + 4h + i%4 (rows)
+    // S = Q K^T, dP = dO V^T: lane holds key l32 (column), queries 8(i/4) + 4h + i%4 (rows).
+    // Without dropout dP accumulates onto -D of its queries (4 groups of 4 consecutive rows in
+    // the statistics), so the products give dP - D directly.
     f32x16 s = (f32x16){}, dp = (f32x16){};
+    if constexpr (!DROP) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + 128 + (8 * g4 + 4 * h) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dp[4 * g4 + r] = nd[r];
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       s = E::mfma(*(const lds_u32x4*)(tq + aoff[ks]), kreg[ks], s);
@@ -498,7 +511,8 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 a = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + (8 * g4 + 4 * h) * 4);
-      const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + 128 + (8 * g4 + 4 * h) * 4);
+      f32x4 nd4 = {};  // -D of the 4 rows (dropout only: the other kernels hold dP - D already)
+      if constexpr (DROP) nd4 = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + 128 + (8 * g4 + 4 * h) * 4);
 #pragma unroll
       for (int r2 = 0; r2 < 2; ++r2) {
         const int i = 4 * g4 + 2 * r2;
@@ -528,12 +542,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
           const float g0 = kept(zw[g4], 2 * r2, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
           const float g1 = kept(zw[g4], 2 * r2 + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
           pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1) & keep_pair_mask(zw[g4], r2 != 0, p.keep_t);
-          sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 - d4[2 * r2]), p1 * (g1 - d4[2 * r2 + 1]));
+          sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 + nd4[2 * r2]), p1 * (g1 + nd4[2 * r2 + 1]));
         } else {
-          const float d0 = p0 * (dp[i] - d4[2 * r2]);
-          const float d1 = p1 * (dp[i + 1] - d4[2 * r2 + 1]);
           pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1);
-          sw[q2 >> 2][q2 & 3] = E::pack2(d0, d1);
+          sw[q2 >> 2][q2 & 3] = E::pack2(p0 * dp[i], p1 * dp[i + 1]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -549,6 +561,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
         dv[db] = E::mfma(pw[t2], tr_operand(tg, ROWBL, t2, toff[db], x1[db]), dv[db]);
         dk[db] = E::mfma(sw[t2], tr_operand(tq, ROWBL, t2, toff[db], x1[db]), dk[db]);
       }
+  };
+  for (int it = 0; it < n_it; it += 2) {
+    iter(it, IC<false>{});
+    if (it + 1 < n_it) iter(it + 1, IC<true>{});
   }
 
   // no LDS-DMA may still be in flight when the work-group ends
@@ -623,7 +639,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
   }
   // the lane's query's statistics (rows past Nq hold zeros)
   const float* w = p.ws + (head * p.ws_blk + q0w / 32) * 64;
-  const float lse2 = w[l32], dlt = w[32 + l32];
+  const float lse2 = w[l32], ndlt = w[32 + l32];  // ndlt = -D
 
   const int ld_off = dma_lane_off<D>(wave, lane);
   int aoff[NKS], toff[NDB];
@@ -759,9 +775,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
         // dS = P o (Z dP / keep - D); key 32j + 8(i/4) + 4h + i%4 is byte i%4 of zw[i/4]
         const float g0 = kept(zw[q2 >> 1], i & 3, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
         const float g1 = kept(zw[q2 >> 1], (i & 3) + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
-        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 - dlt), p1 * (g1 - dlt));
+        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 + ndlt), p1 * (g1 + ndlt));
       } else {
-        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
+        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (dp[i] + ndlt), p1 * (dp[i + 1] + ndlt));
       }
     }
     // dQ += dS K: B operand is K read transposed
