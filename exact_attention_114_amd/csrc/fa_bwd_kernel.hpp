@@ -705,10 +705,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
     dma_rows<D, NW>(Kp, Nk, j_lo * 32, (lds_char*)sK0, wave, ld_off);
     dma_rows<D, NW>(Vp, Nk, j_lo * 32, (lds_char*)sV0, wave, ld_off);
   }
-  for (int r = 0; r < nt; ++r) {
+  // dP^T accumulates onto -D of the lane's query (without dropout), so the products give dP - D:
+  // one loop-invariant operand tuple
+  f32x16 nd16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nd16[i] = DROP ? 0.f : ndlt;
+  // One tile; even tiles read the 0 buffers, odd ones the 1 buffers: the loop runs them in
+  // pairs, so each buffer's address is a compile-time constant for the LDS reads.
+  auto tile = [&](const int r, auto oddc) {
+    constexpr bool odd = decltype(oddc)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const bool odd = r & 1;
     const int j = j_lo + r;
     const lds_char* tk = (const lds_char*)(odd ? sK1 : sK0);
     const lds_char* tv = (const lds_char*)(odd ? sV1 : sV0);
@@ -717,7 +724,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
       dma_rows<D, NW>(Vp, Nk, (j + 1) * 32, (lds_char*)(odd ? sV0 : sV1), wave, ld_off);
     }
     // S^T = K Q^T, dP^T = V dO^T: lane holds query l32, keys 32j + 8(i/4) + 4h + i%4
-    f32x16 s = (f32x16){}, dp = (f32x16){};
+    f32x16 s = (f32x16){}, dp = nd16;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       s = E::mfma(*(const lds_u32x4*)(tk + aoff[ks]), qreg[ks], s);
@@ -777,7 +784,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
         const float g1 = kept(zw[q2 >> 1], (i & 3) + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
         sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 + ndlt), p1 * (g1 + ndlt));
       } else {
-        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (dp[i] + ndlt), p1 * (dp[i + 1] + ndlt));
+        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * dp[i], p1 * dp[i + 1]);
       }
     }
     // dQ += dS K: B operand is K read transposed
@@ -788,6 +795,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] = E::mfma(sw[t2], tr_operand(tk, ROWBL, t2, toff[db], x1[db]), acc[db]);
+  };
+  for (int r = 0; r < nt; r += 2) {
+    tile(r, IC<false>{});
+    if (r + 1 < nt) tile(r + 1, IC<true>{});
   }
 
   // element i of block db: query q0w + 8(i/4) + 4h + i%4, column 32db + l32
