@@ -497,6 +497,8 @@ def main():
                 print(json.dumps({"sweep_bwd": name, "ms": round(ms, 5), "tflops": round(tf, 2),
                                   "pct_peak": round(100 * tf / PEAK_TFLOPS[wk.dtype], 2)}), flush=True)
         print(json.dumps(bwd_line(w, args)), flush=True)
+        if args.calibrate_copy:
+            calibrate_copy()
         return
     if args.sweep:
         for name in I.WORKLOADS:

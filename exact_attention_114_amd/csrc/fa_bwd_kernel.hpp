@@ -505,6 +505,17 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     // check of part - (t - right) against left + right
     const int vlo = k0w + l32 - q0 - 4 * h - p.off - p.right;
     const unsigned width = (unsigned)p.left + (unsigned)p.right;
+    // the additive mask, then the band (one uniform branch over the whole block: only the blocks
+    // that cross a band edge pay for the selects)
+    if constexpr (FM != 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = __builtin_fmaf(fmv[i], p.inv_scale, s[i]);
+    }
+    if (diag) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        s[i] = (unsigned)(8 * (i >> 2) + (i & 3) - vlo) > width ? -__builtin_inff() : s[i];
+    }
     // P and dS, four rows at a time: the lane's rows' statistics are 4 groups of 4 consecutive
     // queries, read from LDS just before use
     u32x4 pw[2], sw[2];
@@ -517,15 +528,6 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
       for (int r2 = 0; r2 < 2; ++r2) {
         const int i = 4 * g4 + 2 * r2;
         float s0 = s[i], s1 = s[i + 1];
-        if constexpr (FM != 0) {
-          s0 = __builtin_fmaf(fmv[i], p.inv_scale, s0);
-          s1 = __builtin_fmaf(fmv[i + 1], p.inv_scale, s1);
-        }
-        if (diag) {
-          const int pa = 8 * g4 + 2 * r2, pb = pa + 1;
-          s0 = (unsigned)(pa - vlo) > width ? -__builtin_inff() : s0;
-          s1 = (unsigned)(pb - vlo) > width ? -__builtin_inff() : s1;
-        }
         if constexpr (AM) {
           if (!mfree) {
             // the bits of queries 8g4 + 4h + 2r2 (+1) in the lane's column word
