@@ -319,8 +319,11 @@ __device__ inline void philox4x32_10(unsigned c0, unsigned c1, unsigned c2, unsi
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const unsigned hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-    const unsigned hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    // each 32 x 32 -> 64-bit product as one 64-bit multiply (one v_mad_u64_u32, both halves)
+    const unsigned long long m0 = (unsigned long long)0xD2511F53u * c0;
+    const unsigned long long m1 = (unsigned long long)0xCD9E8D57u * c2;
+    const unsigned hi0 = (unsigned)(m0 >> 32), lo0 = (unsigned)m0;
+    const unsigned hi1 = (unsigned)(m1 >> 32), lo1 = (unsigned)m1;
     c0 = hi1 ^ c1 ^ k0;
     c1 = lo1;
     c2 = hi0 ^ c3 ^ k1;
