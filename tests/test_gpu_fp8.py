@@ -52,7 +52,7 @@ def run(B, Hq, Hkv, Nq, Nk, d, seed, causal=False, window=None, k_mult=1.0, rows
         seen = np.isfinite(L_ref)
         assert (Og[~seen] == 0).all() and (Lg[~seen] == -np.inf).all()
         ro = (np.abs(Og - O_ref) / np.maximum(bo, 1e-300))[seen].max() if seen.any() else 0.0
-        rl = (np.abs(Lg - L_ref)[seen] / np.maximum(bl[seen], 1e-300)).max() if seen.any() else 0.0
+        rl = (np.abs(Lg[seen] - L_ref[seen]) / np.maximum(bl[seen], 1e-300)).max() if seen.any() else 0.0
         worst = [max(worst[0], ro), max(worst[1], rl)]
         assert ro <= 1.0, f"b={b} h={h}: O error reaches {ro:.3f} of the fp8 bar"
         assert rl <= 1.0, f"b={b} h={h}: LSE error reaches {rl:.3f} of the fp8 bar"
