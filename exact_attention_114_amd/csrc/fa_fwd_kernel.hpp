@@ -384,6 +384,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP || FM != 0)))) voi
   __shared__ __attribute__((aligned(1024))) char sV1[TILE_BYTES];
   // dropout: the four Philox words of each lane's call, exchanged within its quad (16 words a quad)
   __shared__ __attribute__((aligned(16))) unsigned sDrop[DROP ? NW * 256 : 4];
+  // additive mask: each wave's 32 rows x BN keys of the step's mask tile, two buffers
+  static_assert(FM == 0 || KB == 1, "the additive mask takes 32-key steps");
+  constexpr int MROW = BN * (FM ? FM : 2);  // mask bytes per row and step
+  __shared__ __attribute__((aligned(1024))) char sM0[FM ? NW * 32 * MROW : 16];
+  __shared__ __attribute__((aligned(1024))) char sM1[FM ? NW * 32 * MROW : 16];
   lds_char* const K0 = (lds_char*)sK0;
   lds_char* const V0 = (lds_char*)sV0;
   lds_char* const K1 = (lds_char*)sK1;
@@ -599,37 +604,67 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP || FM != 0)))) voi
       }
     }
   };
-  // Additive mask: fm_w[kb][g] holds the mask values of keys kbase + 32kb + 8g + 4h .. +3 of this
-  // lane's query row (score 4g + e of block kb). One descriptor spans the plane and the whole
-  // offset goes into the vector operand, so reads past the plane return zeros; keys past the
-  // row's end read the next row, and the band and key-end selects below replace those scores.
-  using FV = FmVec<FM == 4 ? 4 : 2>;
-  typename FV::T fm_w[FM ? KB : 1][4];
-  __amdgpu_buffer_rsrc_t fm_rs;
-  auto load_fm = [&](int jt, typename FV::T(&w)[FM ? KB : 1][4]) {
-    if constexpr (FM != 0) {
-      const int row = min(q0w + (lane_id_here() & 31), Nq - 1);
-      const int vo = (row * p.fm_ld + jt * BN + 4 * h) * FM;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) w[kb][g4] = FV::load(fm_rs, vo + (32 * kb + 8 * g4) * FM);
-    }
-  };
-  // the unscaled score gains M / scale (before the band's selects)
-  auto apply_fm = [&](f32x16(&st)[KB], const typename FV::T(&w)[FM ? KB : 1][4]) {
-    if constexpr (FM != 0) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st[kb][i] = __builtin_fmaf(FV::at(w[kb][i >> 2], i & 3), p.inv_scale, st[kb][i]);
-    }
-  };
+  // Additive mask, staged through LDS: each wave's 32 rows x 32 keys of a step (64 or 128 bytes a
+  // row) arrive by LDS-DMA in 1 KiB instructions of RPM rows (16 rows of 4 chunks of 16 bytes for
+  // fp16, 8 rows of 8 chunks for fp32). Chunk c of row r sits at chunk c ^ (r & (CPR - 1)) of its
+  // LDS row, so that the lanes' reads (one row each, the same logical chunk) spread over the banks;
+  // the swizzle repeats every RPM rows, so the lane's source offset is the same for every
+  // instruction, and each instruction's first row goes into its descriptor's base. The
+  // descriptor runs to the plane's end: rows past Nq read zeros, keys past a row's end read the
+  // next row, and the band and key-end selects below replace those scores.
+  constexpr int CPR = MROW / 16, RPM = 64 / CPR, NLM = 32 / RPM;
+  int fm_voff = 0, fm_roff = 0;
+  const char* fm_plane = nullptr;
+  int fm_bytes = 0;
   if constexpr (FM != 0) {
-    const char* plane = (const char*)p.fm + (b * p.fm_sb + hq * p.fm_sh) * FM;
-    fm_rs = __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.fm_ld * FM, kBufferWord3);
-    load_fm(j_lo, fm_w);
+    fm_plane = (const char*)p.fm + (b * p.fm_sb + hq * p.fm_sh) * FM;
+    fm_bytes = Nq * p.fm_ld * FM;
+    const int r = lane / CPR, c = lane % CPR;
+    fm_voff = r * p.fm_ld * FM + ((c ^ (r & (CPR - 1))) << 4);
+    // the lane's own row (l32) and its logical chunks, read back after the step's wait
+    fm_roff = wave * 32 * MROW + l32 * MROW;
   }
+  auto load_fm = [&](int jt, lds_char* dst) {
+    if constexpr (FM != 0) {
+#pragma unroll
+      for (int n = 0; n < NLM; ++n) {
+        const int first = (q0w + n * RPM) * p.fm_ld * FM + jt * BN * FM;
+        const int rest = fm_bytes - first;
+        void* bp = (void*)(fm_plane + first);
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(bp, (short)0, rest > 0 ? rest : 0, kBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + wave * 32 * MROW + n * 1024), 16, fm_voff, 0,
+                                                 0, 0);
+      }
+    }
+  };
+  // the unscaled score gains M / scale (before the band's selects): group g (keys 8g + 4h .. +3)
+  // is half h of logical chunk g (fp16) or chunk 2g + h (fp32)
+  auto apply_fm = [&](f32x16(&st)[KB], const lds_char* src) {
+    if constexpr (FM != 0) {
+      const lds_char* row = src + fm_roff;
+      const int sw = l32 & (CPR - 1);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float m4[4];
+        if constexpr (FM == 2) {
+          const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(row + ((g4 ^ sw) << 4) + 8 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned x = w[e >> 1];
+            m4[e] = (float)__builtin_bit_cast(f16x2, x)[e & 1];
+          }
+        } else {
+          const f32x4 w = *(const __attribute__((address_space(3))) f32x4*)(row + (((2 * g4 + h) ^ sw) << 4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m4[e] = w[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[0][4 * g4 + e] = __builtin_fmaf(m4[e], p.inv_scale, st[0][4 * g4 + e]);
+      }
+    }
+  };
+  if constexpr (FM != 0) load_fm(j_lo, (lds_char*)sM0);
   // Dropout: Philox call (key tile, row tile, plane, offset) covers 4 rows x 4 keys, byte
   // 4 (row & 3) + (key & 3). The 4 lanes of a quad (rows 4a .. 4a+3, one half) need the calls of
   // their 4 key groups g (keys 32 kb + 8 g + 4 h .. + 3 of a block): lane s of the quad computes
@@ -729,10 +764,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP || FM != 0)))) voi
           st[kb][i] = hide ? -__builtin_inff() : st[kb][i];
         }
     };
-    if constexpr (FM != 0) {
-      apply_fm(scur, fm_w);
-      load_fm(j + 1, fm_w);  // the next step's values
-    }
+    if constexpr (FM != 0) apply_fm(scur, (const lds_char*)(PAR ? sM1 : sM0));
     if (need_mask) mask(scur);
     if constexpr (AM) {
       apply_am(scur, am_w);
@@ -829,6 +861,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP || FM != 0)))) voi
       if constexpr (sl == (NM > 1 ? 1 : 0)) {
         load_v(j, PAR ? V1 : V0);
         if (HAS_S) load_k(j + 2, PAR ? K1 : K0);
+        if constexpr (FM != 0) load_fm(j + 1, (lds_char*)(PAR ? sM0 : sM1));  // the next step's mask tile
       }
       // items [lo, hi) of this slot: phase 1 spreads [0, I1) over slots [0, S1), phase 2
       // spreads [I1, NITEM) over slots [S1, NSLOT)
@@ -859,11 +892,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP || FM != 0)))) voi
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) st[kb] = E::mfma(src[2 * ks], qreg[ks], st[kb]);
         }
-        if constexpr (FM != 0) {
-          typename FV::T wj[KB][4];
-          load_fm(j, wj);
-          apply_fm(st, wj);
-        }
+        if constexpr (FM != 0) apply_fm(st, (const lds_char*)(PAR ? sM1 : sM0));
         if (need_mask) mask(st);
         if constexpr (AM) {
           unsigned wj[AM ? KB : 1];

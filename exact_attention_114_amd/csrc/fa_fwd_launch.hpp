@@ -69,10 +69,10 @@ fa_status launch(const Params& p, hipStream_t stream) {
   return FA_OK;
 }
 
-// The additive mask at d > 64 takes one key block per step only (its values need registers).
+// The additive mask takes one key block per step (its tile is staged through LDS).
 template <bool BF16, int D, bool BAND, bool OUT_F32, bool AM, bool DROP, int FM>
 fa_status dispatch_kb(const Params& p, int kb, hipStream_t s) {
-  if constexpr (D > 64 && FM != 0) {
+  if constexpr (FM != 0) {
     return launch<BF16, D, BAND, OUT_F32, 1, AM, DROP, FM>(p, s);
   } else {
     if constexpr (D > 64) {

@@ -135,7 +135,10 @@ def test_fwd_float_mask_parity(B, Hq, Hkv, Nq, Nk, d, dt, left, right, kind, mdt
 
 
 def test_zero_mask_equals_no_mask_and_neg_inf_equals_byte_mask():
-    """A zero float mask gives the unmasked result; a {0, -inf} mask gives the byte mask's."""
+    """A zero float mask gives the unmasked result; a {0, -inf} mask gives the byte mask's: equal
+    up to rounding order (the additive-mask kernel takes 32-key steps where the others take 64),
+    within the forward's fp16 bar on O and 1e-5 on the LSE; the rows with no visible key agree
+    exactly."""
     B, Hq, Hkv, N, d, dt = 1, 2, 1, 300, 64, I.F16
     g = np.random.Generator(np.random.PCG64(4100))
     qd, kd, vd = (to_dev(I.to_bits(g.standard_normal((B, h, N, d), dtype=np.float32), dt), dt)
@@ -151,10 +154,11 @@ def test_zero_mask_equals_no_mask_and_neg_inf_equals_byte_mask():
     ninf = torch.where(hid, torch.tensor(float("-inf")), torch.tensor(0.0)).to(torch.float32).to(DEV)
     Of, Lf = fa.fwd(qd, kd, vd, causal=True, mask=ninf)
     torch.cuda.synchronize()
-    assert (Oz - O0).abs().max().item() <= 1e-6 and (Lz - L0).abs().max().item() <= 1e-6
-    assert (Of - Ob).abs().max().item() <= 1e-6 and torch.equal(torch.isinf(Lf), torch.isinf(Lb))
+    assert (Oz - O0).abs().max().item() <= TOL_O[dt] and (Lz - L0).abs().max().item() <= 1e-5
+    assert (Of - Ob).abs().max().item() <= TOL_O[dt] and torch.equal(torch.isinf(Lf), torch.isinf(Lb))
     fin = torch.isfinite(Lb)
-    assert (Lf[fin] - Lb[fin]).abs().max().item() <= 1e-6
+    assert (Lf[fin] - Lb[fin]).abs().max().item() <= 1e-5
+    assert (Of[~fin.unsqueeze(-1).expand_as(Of)] == 0).all()
 
 
 BWD_CASES = [  # (B, Hq, Hkv, Nq, Nk, d, dt, left, right, kind, mdt, Bm, Hm, pad)
