@@ -263,7 +263,9 @@ __device__ inline u32x4 tr_operand(const lds_char* tile, int rowb, int t2, int o
 // At d = 112 and 128 the dK/dV kernel keeps V's rows in LDS rather than registers, which brings
 // it under the 256 VGPRs two waves per SIMD allow.
 constexpr bool bwd_v_in_lds(int d) { return d > 96; }
-constexpr int bwd_waves_per_simd(int d) { return 2; }
+// Waves per SIMD the dK/dV kernel is built for: three at d <= 64 without the dropout, mask and
+// additive-mask inputs (whose registers need the room of two).
+constexpr int bwd_waves_per_simd(int d, bool plain) { return d <= 64 && plain ? 3 : 2; }
 
 // 4 * (lane id), formed from scratch where it is used: as an opaque instruction sequence it
 // cannot be hoisted out of a loop, so it holds no register across the loop (the dK/dV kernel
@@ -278,7 +280,7 @@ __device__ inline int lane_bytes4() {
 // ---- 2. dK/dV ---------------------------------------------------------------------------------
 template <bool BF16, int D, bool BAND, int NW, bool AM, bool DROP = false, int FM = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D, !AM && !DROP && FM == 0)))) void fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
   static_assert(D % 16 == 0 && D >= 32 && D <= 128, "head dimension: a multiple of 16 from 32 to 128");
   constexpr int ROWBL = lds_pitch(D) * 2, TB = 32 * ROWBL;  // LDS row pitch and tile bytes
@@ -379,39 +381,57 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     if (p.flags_sh == 0 && nqb > 0 && tt <= q_hi / 128)
       mflag = p.am_flags[b * p.flags_sb + (int64_t)kt * p.flags_nq + tt];
   }
-  auto mask_free = [&](int it) -> bool {
+  // qb: an iteration's query block (wave-uniform)
+  auto mask_free = [&](int qb) -> bool {
     if constexpr (!AM) {
       return false;
     } else {
       if (p.flags_sh != 0) return false;
-      const int qt = (qb0 + it % nqb) / 4 - q_lo / 128;  // wave-uniform, >= 0
+      const int qt = qb / 4 - q_lo / 128;  // wave-uniform, >= 0
       return qt < 64 && __builtin_amdgcn_readlane(mflag, qt) == 2;
     }
   };
 
-  // The lane's mask column word for iteration it (query block qb of head g, its key), loaded
+  // Iteration it visits query block qb0 + it % nqb of head g = it / nqb. Both the iteration and
+  // the loads (one iteration ahead) carry their (g, qb) and head planes along, one block at a
+  // time, so the loop does no division and no 64-bit multiply.
+  const int64_t head0 = (int64_t)b * p.Hq + hkv * G;
+  const int64_t plane_b = (int64_t)Nq * D * 2;
+  const int64_t wplane = (int64_t)p.ws_blk * 64;
+  const char* ld_q = (const char*)p.q + head0 * plane_b;
+  const char* ld_go = (const char*)p.dout + head0 * plane_b;
+  const float* ld_w = p.ws + head0 * wplane;
+  int ld_g = 0, ld_qb = qb0;
+
+  // The lane's mask column word for the block being loaded (head ld_g, block ld_qb, its key),
   // one iteration ahead; the key's offset is formed from an opaque lane id where it is used (no
   // register holds it across the loop). Keys past Nk read the last key's word: their results
   // are never stored.
   unsigned mw = 0u, mw_next = 0u;
-  auto load_mw = [&](int it) {
-    const int g = it / nqb, qb = qb0 + (it - g * nqb);
+  auto load_mw = [&]() {
     const int key = min(k0w + (lane_id_here() & 31), Nk - 1);
-    mw_next = p.am_cbits[b * p.cbits_sb + (hkv * G + g) * p.cbits_sh + (int64_t)key * p.cbits_nqb + qb];
+    mw_next = p.am_cbits[b * p.cbits_sb + (hkv * G + ld_g) * p.cbits_sh + (int64_t)key * p.cbits_nqb + ld_qb];
   };
-  auto issue_loads = [&](int it, lds_char* dq_, lds_char* dg_, float* dw_) {
-    const int g = it / nqb, qb = qb0 + (it - g * nqb);
-    const int64_t head = (int64_t)b * p.Hq + hkv * G + g;
-    dma_rows<D, NW>((const char*)((const T*)p.q + head * Nq * D), Nq, qb * 32, dq_, wave, ld_off);
-    dma_rows<D, NW>((const char*)((const T*)p.dout + head * Nq * D), Nq, qb * 32, dg_, wave, ld_off);
+  // the next iteration's Q and dO rows and row statistics, then one block further on
+  auto issue_loads = [&](lds_char* dq_, lds_char* dg_, float* dw_) {
+    dma_rows<D, NW>(ld_q, Nq, ld_qb * 32, dq_, wave, ld_off);
+    dma_rows<D, NW>(ld_go, Nq, ld_qb * 32, dg_, wave, ld_off);
     if constexpr (AM)
-      if (!mask_free(it)) load_mw(it);
+      if (!mask_free(ld_qb)) load_mw();
     if (wave == 0) {
-      void* wp = (void*)(p.ws + (head * p.ws_blk + qb) * 64);
+      void* wp = (void*)(ld_w + ld_qb * 64);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(wp, (short)0, 256, kBufferWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dw_, 4, lane_bytes4(), 0, 0, 0);
     }
+    if (++ld_qb == qb0 + nqb) {
+      ld_qb = qb0;
+      ++ld_g;
+      ld_q += plane_b;
+      ld_go += plane_b;
+      ld_w += wplane;
+    }
   };
+  int cur_g = 0, cur_qb = qb0;  // of the iteration running
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -421,7 +441,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
   }
   const float c = p.c;
 
-  if (n_it > 0) issue_loads(0, (lds_char*)sQ0, (lds_char*)sG0, sW0);
+  if (n_it > 0) issue_loads((lds_char*)sQ0, (lds_char*)sG0, sW0);
   // One iteration; even iterations read the 0 buffers and odd ones the 1 buffers. The loop runs
   // them in pairs, so each buffer's address is a compile-time constant of its iteration and the
   // LDS reads take it as an immediate offset.
@@ -433,11 +453,14 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     const lds_char* tg = (const lds_char*)(odd ? sG1 : sG0);
     const float* tw = odd ? sW1 : sW0;
     if constexpr (AM) mw = mw_next;  // loaded during the previous iteration (or before the loop)
-    if (it + 1 < n_it)
-      issue_loads(it + 1, (lds_char*)(odd ? sQ0 : sQ1), (lds_char*)(odd ? sG0 : sG1), odd ? sW0 : sW1);
-    const int qb = qb0 + (it % nqb);
+    [[maybe_unused]] const int g = cur_g;
+    const int qb = cur_qb;
+    if (++cur_qb == qb0 + nqb) {
+      cur_qb = qb0;
+      ++cur_g;
+    }
     const int q0 = qb * 32;
-    const bool mfree = mask_free(it);
+    const bool mfree = mask_free(qb);
     // Dropout: the lane's key meets queries q0 + 8 g4 + 4h + r; Philox call (key / 4, query / 4)
     // covers a 4 x 4 block, byte 4 (query & 3) + (key & 3). The quad of lanes with keys 4a .. 4a+3
     // (one half) needs the calls of its 4 query groups g4: lane s computes group s, transposes
@@ -449,7 +472,6 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
       const int sq = lane & 3;
       __attribute__((address_space(3))) unsigned* slot =
           (__attribute__((address_space(3))) unsigned*)sDrop + wave * 256 + (lane >> 2) * 16;
-      const int g = it / nqb;
       unsigned w[4], tw4[4];
       philox4x32_10((unsigned)(k0w + (l32 & ~3)) >> 2, (unsigned)(q0 >> 2) + 2 * sq + h,
                     (unsigned)(b * p.Hq + hkv * G + g), p.drop_offset, p.seed_lo, p.seed_hi, w);
@@ -468,7 +490,6 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     // plane's descriptor and read zeros; keys past Nk only reach gradients that are not stored.
     float fmv[FM ? 16 : 1];
     if constexpr (FM != 0) {
-      const int g = it / nqb;
       const char* plane = (const char*)p.fm + (b * p.fm_sb + (hkv * G + g) * p.fm_sh) * FM;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)plane, (short)0, Nq * p.fm_ld * FM, kBufferWord3);
@@ -488,16 +509,6 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
         for (int r = 0; r < 4; ++r) dp[4 * g4 + r] = nd[r];
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      s = E::mfma(*(const lds_u32x4*)(tq + aoff[ks]), kreg[ks], s);
-      u32x4 vb;
-      if constexpr (VL)
-        vb = *(const lds_u32x4*)((const lds_char*)sV + wave * TB + aoff[ks]);
-      else
-        vb = vreg[ks];
-      dp = E::mfma(*(const lds_u32x4*)(tg + aoff[ks]), vb, dp);
-    }
     // band: key k0w + l32 is hidden from query q0 + part + 4h when it lies after the query's
     // right edge (part < t_lo) or before its left edge (part > t_hi)
     const bool diag = BAND && (k0w + 31 > q0 + p.off + p.right || k0w < q0 + 31 + p.off - p.left);
@@ -505,64 +516,132 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D)))) void fa_bwd_dkdv_ker
     // check of part - (t - right) against left + right
     const int vlo = k0w + l32 - q0 - 4 * h - p.off - p.right;
     const unsigned width = (unsigned)p.left + (unsigned)p.right;
-    // the additive mask, then the band (one uniform branch over the whole block: only the blocks
-    // that cross a band edge pay for the selects)
-    if constexpr (FM != 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = __builtin_fmaf(fmv[i], p.inv_scale, s[i]);
-    }
-    if (diag) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        s[i] = (unsigned)(8 * (i >> 2) + (i & 3) - vlo) > width ? -__builtin_inff() : s[i];
-    }
-    // P and dS, four rows at a time: the lane's rows' statistics are 4 groups of 4 consecutive
-    // queries, read from LDS just before use
-    u32x4 pw[2], sw[2];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 a = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + (8 * g4 + 4 * h) * 4);
-      f32x4 nd4 = {};  // -D of the 4 rows (dropout only: the other kernels hold dP - D already)
-      if constexpr (DROP) nd4 = *(const __attribute__((address_space(3))) f32x4*)((const lds_char*)tw + 128 + (8 * g4 + 4 * h) * 4);
-#pragma unroll
-      for (int r2 = 0; r2 < 2; ++r2) {
-        const int i = 4 * g4 + 2 * r2;
-        float s0 = s[i], s1 = s[i + 1];
-        if constexpr (AM) {
-          if (!mfree) {
-            // the bits of queries 8g4 + 4h + 2r2 (+1) in the lane's column word
-            const unsigned x = mw >> (4 * h + 8 * g4 + 2 * r2);
-            s0 = (x & 1u) != 0u ? -__builtin_inff() : s0;
-            s1 = (x & 2u) != 0u ? -__builtin_inff() : s1;
-          }
-        }
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a[2 * r2]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -a[2 * r2 + 1]));
-        const int q2 = i >> 1;
-        if constexpr (DROP) {
-          // dV takes the kept P (scaled at the end); dS = P o (Z dP / keep - D)
-          const float g0 = kept(zw[g4], 2 * r2, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
-          const float g1 = kept(zw[g4], 2 * r2 + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
-          pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1) & keep_pair_mask(zw[g4], r2 != 0, p.keep_t);
-          sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 + nd4[2 * r2]), p1 * (g1 + nd4[2 * r2 + 1]));
-        } else {
-          pw[q2 >> 2][q2 & 3] = E::pack2(p0, p1);
-          sw[q2 >> 2][q2 & 3] = E::pack2(p0 * dp[i], p1 * dp[i + 1]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dV += P^T dO, dK += dS^T Q: B operands are dO and Q read transposed
+
+    // The products run as slots of one MFMA each, in the order S (NKS), dP (NKS), dV (2 NDB),
+    // dK (2 NDB). A slot issues the LDS reads of a later slot's MFMA and its share of the
+    // VALU work, so that the work of one block overlaps its own products: P is formed from S
+    // while the dP products run, dS while the dV products run. The rows' statistics (LSE
+    // times log2(e)) are read during the S products.
+    constexpr int M = 2 * NKS + 4 * NDB;
+    constexpr int MDV = 2 * NKS, MDK = 2 * NKS + 2 * NDB;  // first slots of dV and dK
     int x1[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) x1[db] = tr_half1(toff[db]);
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv[db] = E::mfma(pw[t2], tr_operand(tg, ROWBL, t2, toff[db], x1[db]), dv[db]);
-        dk[db] = E::mfma(sw[t2], tr_operand(tq, ROWBL, t2, toff[db], x1[db]), dk[db]);
+    u32x4 opnd[M], vop[VL ? NKS : 1];
+    f32x2 a2[8];  // pair q's two rows' statistics
+    float ex[16];
+    u32x4 pw[2], sw[2];
+    auto fetch = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NKS) {
+        opnd[m] = *(const lds_u32x4*)(tq + aoff[m]);
+      } else if constexpr (m < MDV) {
+        opnd[m] = *(const lds_u32x4*)(tg + aoff[m - NKS]);
+        if constexpr (VL) vop[m - NKS] = *(const lds_u32x4*)((const lds_char*)sV + wave * TB + aoff[m - NKS]);
+      } else if constexpr (m < MDK) {
+        constexpr int t2 = (m - MDV) / NDB, db = (m - MDV) % NDB;
+        opnd[m] = tr_operand(tg, ROWBL, t2, toff[db], x1[db]);
+      } else {
+        constexpr int t2 = (m - MDK) / NDB, db = (m - MDK) % NDB;
+        opnd[m] = tr_operand(tq, ROWBL, t2, toff[db], x1[db]);
       }
+    };
+    auto issue = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NKS) {
+        s = E::mfma(opnd[m], kreg[m], s);
+      } else if constexpr (m < MDV) {
+        if constexpr (VL)
+          dp = E::mfma(opnd[m], vop[m - NKS], dp);
+        else
+          dp = E::mfma(opnd[m], vreg[m - NKS], dp);
+      } else if constexpr (m < MDK) {
+        constexpr int t2 = (m - MDV) / NDB, db = (m - MDV) % NDB;
+        dv[db] = E::mfma(pw[t2], opnd[m], dv[db]);
+      } else {
+        constexpr int t2 = (m - MDK) / NDB, db = (m - MDK) % NDB;
+        dk[db] = E::mfma(sw[t2], opnd[m], dk[db]);
+      }
+    };
+    // The hidden scores, once S is complete: the band (one uniform branch over the whole block:
+    // only the blocks that cross a band edge pay for the selects) and the byte mask's bits.
+    auto mask_s = [&]() {
+      if (diag) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[i] = (unsigned)(8 * (i >> 2) + (i & 3) - vlo) > width ? -__builtin_inff() : s[i];
+      }
+      if constexpr (AM) {
+        if (!mfree) {
+          // bit 4h + 8(i/4) + i%4 of the lane's column word: query 8(i/4) + 4h + i%4
+          const unsigned x = mw >> (4 * h);
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            s[i] = ((x >> (8 * (i >> 2) + (i & 3))) & 1u) != 0u ? -__builtin_inff() : s[i];
+        }
+      }
+    };
+    // pair q (queries of elements 2q, 2q + 1): P, packed for dV (dropout hides the dropped halves)
+    auto p_item = [&](auto qc) {
+      constexpr int q = decltype(qc)::value, i = 2 * q, g4 = q >> 1, r2 = q & 1;
+      float s0 = s[i], s1 = s[i + 1];
+      if constexpr (FM != 0) {
+        // the additive mask (a hidden key's -inf stays -inf)
+        s0 = __builtin_fmaf(fmv[i], p.inv_scale, s0);
+        s1 = __builtin_fmaf(fmv[i + 1], p.inv_scale, s1);
+      }
+      ex[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -a2[q][0]));
+      ex[i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -a2[q][1]));
+      if constexpr (DROP)
+        pw[q >> 2][q & 3] = E::pack2(ex[i], ex[i + 1]) & keep_pair_mask(zw[g4], r2 != 0, p.keep_t);
+      else
+        pw[q >> 2][q & 3] = E::pack2(ex[i], ex[i + 1]);
+    };
+    // pair q: dS = P o (dP - D), packed for dK; with dropout dS = P o (Z dP / keep - D)
+    auto ds_item = [&](auto qc) {
+      constexpr int q = decltype(qc)::value, i = 2 * q, g4 = q >> 1, r2 = q & 1;
+      if constexpr (DROP) {
+        const f32x2 nd2 = *(const __attribute__((address_space(3))) f32x2*)((const lds_char*)tw + 128 + (8 * g4 + 4 * h + 2 * r2) * 4);
+        const float g0 = kept(zw[g4], 2 * r2, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
+        const float g1 = kept(zw[g4], 2 * r2 + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
+        sw[q >> 2][q & 3] = E::pack2(ex[i] * (g0 + nd2[0]), ex[i + 1] * (g1 + nd2[1]));
+      } else {
+        sw[q >> 2][q & 3] = E::pack2(ex[i] * dp[i], ex[i + 1] * dp[i + 1]);
+      }
+    };
+    // slot of each pair: P once S is complete, before the first dV product; dS once dP is
+    // complete, before the first dK product. A pair's two rows' statistics are read two slots
+    // before it.
+    auto p_slot = [](int q) { return NKS + 1 + (q * (NKS - 1)) / 8; };
+    auto ds_slot = [](int q) { return MDV + 1 + (q * (2 * NDB - 1)) / 8; };
+
+    // operands are read FD slots ahead (one at d >= 112, where registers are shortest)
+    constexpr int FD = (D >= 112 || D == 64) ? 1 : 2;
+    static_for<0, FD>([&](auto mc) { fetch(mc); });
+    static_for<0, M>([&](auto slc) {
+      constexpr int sl = decltype(slc)::value;
+      if constexpr (sl + FD < M) fetch(IC<sl + FD>{});
+      static_for<0, 8>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (p_slot(q) - 2 == sl)
+          a2[q] = *(const __attribute__((address_space(3))) f32x2*)((const lds_char*)tw + (8 * (q >> 1) + 4 * h + 2 * (q & 1)) * 4);
+      });
+      // the next iteration's loads, issued in the shadow of the products (into the buffers the
+      // barrier above freed)
+      if constexpr (sl == 1)
+        if (it + 1 < n_it) issue_loads((lds_char*)(odd ? sQ0 : sQ1), (lds_char*)(odd ? sG0 : sG1), odd ? sW0 : sW1);
+      if constexpr (sl == NKS + 1) mask_s();
+      static_for<0, 8>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (p_slot(q) == sl) p_item(qc);
+      });
+      static_for<0, 8>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (ds_slot(q) == sl) ds_item(qc);
+      });
+      issue(slc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   for (int it = 0; it < n_it; it += 2) {
     iter(it, IC<false>{});
