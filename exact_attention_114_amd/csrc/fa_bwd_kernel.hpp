@@ -804,39 +804,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
       dma_rows<D, NW>(Kp, Nk, (j + 1) * 32, (lds_char*)(odd ? sK0 : sK1), wave, ld_off);
       dma_rows<D, NW>(Vp, Nk, (j + 1) * 32, (lds_char*)(odd ? sV0 : sV1), wave, ld_off);
     }
-    // S^T = K Q^T, dP^T = V dO^T: lane holds query l32, keys 32j + 8(i/4) + 4h + i%4
-    f32x16 s = (f32x16){}, dp = nd16;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      s = E::mfma(*(const lds_u32x4*)(tk + aoff[ks]), qreg[ks], s);
-      dp = E::mfma(*(const lds_u32x4*)(tv + aoff[ks]), greg[ks], dp);
-    }
-    const int kbase = 32 * j;
-    if constexpr (FM != 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = __builtin_fmaf(FV::at(fmw[i >> 2], i & 3), p.inv_scale, s[i]);
-      if (r + 1 < nt) load_fm(j + 1);
-    }
-    if ((BAND && (kbase + 31 > min(q0w, Nq - 1) + p.off + p.right || kbase < min(q0w + 31, Nq - 1) + p.off - p.left)) ||
-        kbase + 32 > Nk) {
-      const int hi = khi - kbase - 4 * h, lo = klo - kbase - 4 * h;  // hide if part > hi or part < lo
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int part = 8 * (i >> 2) + (i & 3);
-        s[i] = (part > hi || (BAND && part < lo)) ? -__builtin_inff() : s[i];
-      }
-    }
-    if constexpr (AM) {
-      const unsigned x = am_w >> h;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        s[i] = ((x >> (8 * (i & 3) + 2 * (i >> 2))) & 1u) != 0u ? -__builtin_inff() : s[i];
-      if (r + 1 < nt) load_am(j + 1);  // the next iteration's opening wait covers it
-    }
     // Dropout, as in the forward: the quad of lanes with queries 4a .. 4a+3 (one half) needs the
     // Philox calls of its 4 key groups (keys 32j + 8g + 4h .. +3); lane s computes group s,
     // writes word r (query 4a + r) to slot [r][s] and reads back slot [s][0..3]: zw[g] holds the
     // lane's query's bytes for key group g, byte key & 3.
+    const int kbase = 32 * j;
     unsigned zw[DROP ? 4 : 1];
     if constexpr (DROP) {
       const int sq = lane & 3;
@@ -853,29 +825,110 @@ __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(const BwdParams p)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) zw[g4] = x[g4];
     }
-    u32x4 sw[2];
-#pragma unroll
-    for (int q2 = 0; q2 < 8; ++q2) {
-      const int i = 2 * q2;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -lse2));
-      if constexpr (DROP) {
-        // dS = P o (Z dP / keep - D); key 32j + 8(i/4) + 4h + i%4 is byte i%4 of zw[i/4]
-        const float g0 = kept(zw[q2 >> 1], i & 3, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
-        const float g1 = kept(zw[q2 >> 1], (i & 3) + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
-        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * (g0 + ndlt), p1 * (g1 + ndlt));
-      } else {
-        sw[q2 >> 2][q2 & 3] = E::pack2(p0 * dp[i], p1 * dp[i + 1]);
-      }
-    }
-    // dQ += dS K: B operand is K read transposed
+
+    // S^T = K Q^T, dP^T = V dO^T: lane holds query l32, keys 32j + 8(i/4) + 4h + i%4. The products
+    // run as slots of one MFMA each, in the order S^T (NKS), dP^T (NKS), dQ (2 NDB), each slot
+    // also reading a later slot's operands and doing a share of the VALU work: the exponentials
+    // run while the dP^T products do, dS while the dQ products do.
+    f32x16 s = (f32x16){}, dp = nd16;
+    constexpr int M = 2 * NKS + 2 * NDB, MDQ = 2 * NKS;
     int x1[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) x1[db] = tr_half1(toff[db]);
+    u32x4 opnd[M];
+    float ex[16];
+    u32x4 sw[2];
+    auto fetch = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NKS) {
+        opnd[m] = *(const lds_u32x4*)(tk + aoff[m]);
+      } else if constexpr (m < MDQ) {
+        opnd[m] = *(const lds_u32x4*)(tv + aoff[m - NKS]);
+      } else {
+        constexpr int t2 = (m - MDQ) / NDB, db = (m - MDQ) % NDB;
+        opnd[m] = tr_operand(tk, ROWBL, t2, toff[db], x1[db]);
+      }
+    };
+    auto issue = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < NKS) {
+        s = E::mfma(opnd[m], qreg[m], s);
+      } else if constexpr (m < MDQ) {
+        dp = E::mfma(opnd[m], greg[m - NKS], dp);
+      } else {
+        constexpr int t2 = (m - MDQ) / NDB, db = (m - MDQ) % NDB;
+        acc[db] = E::mfma(sw[t2], opnd[m], acc[db]);
+      }
+    };
+    // the hidden scores, once S^T is complete: the band and the key end (one uniform branch for
+    // the tiles that cross them), the byte mask's bits
+    auto mask_s = [&]() {
+      if ((BAND && (kbase + 31 > min(q0w, Nq - 1) + p.off + p.right || kbase < min(q0w + 31, Nq - 1) + p.off - p.left)) ||
+          kbase + 32 > Nk) {
+        const int hi = khi - kbase - 4 * h, lo = klo - kbase - 4 * h;  // hide if part > hi or part < lo
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+        for (int i = 0; i < 16; ++i) {
+          const int part = 8 * (i >> 2) + (i & 3);
+          s[i] = (part > hi || (BAND && part < lo)) ? -__builtin_inff() : s[i];
+        }
+      }
+      if constexpr (AM) {
+        const unsigned x = am_w >> h;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = E::mfma(sw[t2], tr_operand(tk, ROWBL, t2, toff[db], x1[db]), acc[db]);
+        for (int i = 0; i < 16; ++i)
+          s[i] = ((x >> (8 * (i & 3) + 2 * (i >> 2))) & 1u) != 0u ? -__builtin_inff() : s[i];
+      }
+    };
+    // element pair q: P (the additive mask first; a hidden key's -inf stays -inf)
+    auto p_item = [&](auto qc) {
+      constexpr int q = decltype(qc)::value, i = 2 * q;
+      float s0 = s[i], s1 = s[i + 1];
+      if constexpr (FM != 0) {
+        s0 = __builtin_fmaf(FV::at(fmw[i >> 2], i & 3), p.inv_scale, s0);
+        s1 = __builtin_fmaf(FV::at(fmw[i >> 2], (i & 3) + 1), p.inv_scale, s1);
+      }
+      ex[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -lse2));
+      ex[i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -lse2));
+    };
+    // element pair q: dS = P o (dP - D), packed for dQ; with dropout dS = P o (Z dP / keep - D),
+    // key 32j + 8(i/4) + 4h + i%4 being byte i%4 of zw[i/4]
+    auto ds_item = [&](auto qc) {
+      constexpr int q = decltype(qc)::value, i = 2 * q;
+      if constexpr (DROP) {
+        const float g0 = kept(zw[q >> 1], i & 3, p.keep_t) ? dp[i] * p.drop_scale : 0.f;
+        const float g1 = kept(zw[q >> 1], (i & 3) + 1, p.keep_t) ? dp[i + 1] * p.drop_scale : 0.f;
+        sw[q >> 2][q & 3] = E::pack2(ex[i] * (g0 + ndlt), ex[i + 1] * (g1 + ndlt));
+      } else {
+        sw[q >> 2][q & 3] = E::pack2(ex[i] * dp[i], ex[i + 1] * dp[i + 1]);
+      }
+    };
+    // slots: P pairs once S^T is complete, through the dP^T products; dS pairs 0-3 once dP^T is
+    // complete, before the first dQ product (they are its operand), pairs 4-7 before the second half
+    auto p_slot = [](int q) { return NKS + 1 + (q * (NKS - 1)) / 8; };
+    auto ds_slot = [](int q) { return q < 4 ? MDQ : MDQ + ((q - 4) * NDB) / 4; };
+    static_for<0, 2>([&](auto mc) { fetch(mc); });
+    static_for<0, M>([&](auto slc) {
+      constexpr int sl = decltype(slc)::value;
+      if constexpr (sl + 2 < M) fetch(IC<sl + 2>{});
+      if constexpr (sl == NKS + 1) {
+        mask_s();
+        // the next tile's mask words and values (the next iteration's opening wait covers them)
+        if constexpr (AM)
+          if (r + 1 < nt) load_am(j + 1);
+      }
+      static_for<0, 8>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (p_slot(q) == sl) p_item(qc);
+      });
+      if constexpr (FM != 0 && sl == 2 * NKS - 1)
+        if (r + 1 < nt) load_fm(j + 1);  // after the last use of this tile's values
+      static_for<0, 8>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (ds_slot(q) == sl) ds_item(qc);
+      });
+      issue(slc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   for (int r = 0; r < nt; r += 2) {
     tile(r, IC<false>{});
