@@ -932,20 +932,53 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd(D, KB, DROP || FM != 0)))) voi
     sync_tiles();
   };
 
+  // The last product, O += P_{nt-1} V_{nt-1}, alone: V_{nt-1} is in the buffer of parity nt % 2
+  // (loaded and waited for by step nt - 1), P_{nt-1} in the registers that step filled.
+  auto pv_tail = [&](auto par, const u32x4(&pprev)[2 * KB]) {
+    constexpr int PAR = decltype(par)::value;
+    const lds_char* vread = PAR ? V0 : V1;
+    static_for<0, 2 * KB * NDB>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      acc_o[m % NDB] = E::mfma(v_operand(vread, m / NDB, m % NDB), pprev[m / NDB], acc_o[m % NDB]);
+    });
+  };
+
   // Buffers and registers alternate with j: even j uses (sA -> sB, pA), odd j (sB -> sA, pB).
-  // Every step after the first is a full one, run in pairs until step nt has added
-  // P_{nt-1} V_{nt-1}. Tiles from nt on lie wholly past the last visible key (past the Q-tile's
-  // last row when causal, else past the sequence end), so the mask hides all their scores:
-  // such a step adds exactly zero (no rescale, P = 0, zero row sum). One code path with a fixed
-  // register assignment costs at most one and a half extra steps per Q-tile.
+  // Tiles from nt on lie wholly past the last visible key (past the Q-tile's last row when
+  // causal, else past the sequence end), so the mask hides all their scores: a step on one adds
+  // exactly zero (no rescale, P = 0, zero row sum).
   const IC<0> E0;
   const IC<1> E1;
   const IC<true> Y;
   const IC<false> Nn;
   step(0, E0, Y, Nn, sA, sB, pB, pA);
-  for (int r = 1; r <= nt; r += 2) {
-    step(r, E1, Y, Y, sB, sA, pA, pB);
-    step(r + 1, E0, Y, Y, sA, sB, pB, pA);
+  if constexpr (KB == 2) {
+    // Full steps in pairs while both tiles of the pair exist; the step of the last tile forms
+    // no S of a further tile, and the last P V product runs on its own, so no step is spent on a
+    // tile past the band.
+    int r = 1;
+    for (; r + 1 < nt; r += 2) {
+      step(r, E1, Y, Y, sB, sA, pA, pB);
+      step(r + 1, E0, Y, Y, sA, sB, pB, pA);
+    }
+    // r is odd and r >= nt - 1
+    if (r < nt) {
+      // nt even: step nt - 1 (odd) without S_nt, then P_{nt-1} V_{nt-1} from pB
+      step(r, E1, Nn, Y, sB, sA, pA, pB);
+      pv_tail(E0, pB);
+    } else {
+      // nt odd: P_{nt-1} V_{nt-1} from the registers of the even step nt - 1
+      pv_tail(E1, pA);
+    }
+  } else {
+    // 32-key steps (the instances whose registers are shortest): one code path with a fixed
+    // register assignment, full steps in pairs until step nt has added P_{nt-1} V_{nt-1}; this
+    // costs at most one and a half extra steps per Q-tile. (A separate last step and product
+    // raise the register pressure past what three waves per SIMD allow.)
+    for (int r = 1; r <= nt; r += 2) {
+      step(r, E1, Y, Y, sB, sA, pA, pB);
+      step(r + 1, E0, Y, Y, sA, sB, pB, pA);
+    }
   }
 
   // ---- epilogue: O = acc / lr, LSE = ln2 * (m + log2 l). O is divided by the sum of the very
