@@ -520,8 +520,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(D, !AM && !DROP && FM == 0
     // The products run as slots of one MFMA each, in the order S (NKS), dP (NKS), dV (2 NDB),
     // dK (2 NDB). A slot issues the LDS reads of a later slot's MFMA and its share of the
     // VALU work, so that the work of one block overlaps its own products: P is formed from S
-    // while the dP products run, dS while the dV products run. The rows' statistics (LSE
-    // times log2(e)) are read during the S products.
+    // while the dP products run, dS while the dV products run.
     constexpr int M = 2 * NKS + 4 * NDB;
     constexpr int MDV = 2 * NKS, MDK = 2 * NKS + 2 * NDB;  // first slots of dV and dK
     int x1[NDB];
