@@ -11,65 +11,16 @@
 #include <cstdint>
 
 #include "../../include/fa.h"
-#include "fa_bwd_kernel.hpp"
+#include "fa_bwd_launch.hpp"
 #include "fa_mask.hpp"
 #include "fa_status.hpp"
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kTile = 32 * kWaves;                                       // keys or queries per work-group
+constexpr int kTile = 32 * fa::kBwdWaves;                                // keys or queries per work-group
 constexpr int64_t kMaxPlaneElems = ((int64_t)1 << 30) - ((int64_t)1 << 16);  // as the forward
 constexpr int kUnlimited = 1 << 30;                                       // an unlimited band edge
 
-fa_status launched() {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    fa::last_hip_error = (int)e;
-    return FA_ERR_HIP;
-  }
-  return FA_OK;
-}
-
-template <bool BF16, int D, bool BAND, bool AM, bool DROP, int FM = 0>
-fa_status launch_all(fa::BwdParams p, bool o_f32, int64_t prep_rows, int64_t grid_kv, int64_t grid_q,
-                     hipStream_t s) {
-  constexpr int RPB = 256 / fa::prep_lanes(D);  // the prep kernel's rows per work-group
-  const unsigned prep_grid = (unsigned)((prep_rows + RPB - 1) / RPB);
-  if (o_f32)
-    hipLaunchKernelGGL((fa::fa_bwd_prep_kernel<BF16, D, true>), dim3(prep_grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((fa::fa_bwd_prep_kernel<BF16, D, false>), dim3(prep_grid), dim3(256), 0, s, p);
-  fa_status st = launched();
-  if (st != FA_OK) return st;
-  p.n_tiles = (int)((p.Nk + kTile - 1) / kTile);
-  p.total_wg = (int)grid_kv;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, BAND, kWaves, AM, DROP, FM>), dim3((unsigned)grid_kv),
-                     dim3(kWaves * 64), 0, s, p);
-  st = launched();
-  if (st != FA_OK) return st;
-  p.n_tiles = (int)((p.Nq + kTile - 1) / kTile);
-  p.total_wg = (int)grid_q;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, BAND, kWaves, AM, DROP, FM>), dim3((unsigned)grid_q),
-                     dim3(kWaves * 64), 0, s, p);
-  return launched();
-}
-
-// A mask runs on the banded kernels (with unlimited edges when there is no band); dropout has
-// its own instances (no mask input with it).
-template <bool BF16, int D>
-fa_status dispatch_band(const fa::BwdParams& p, bool band, bool am, bool drop, int fm, bool o_f32, int64_t pr,
-                        int64_t gkv, int64_t gq, hipStream_t s) {
-  // the additive mask runs on the banded kernels, alone
-  if (fm == 2) return launch_all<BF16, D, true, false, false, 2>(p, o_f32, pr, gkv, gq, s);
-  if (fm == 4) return launch_all<BF16, D, true, false, false, 4>(p, o_f32, pr, gkv, gq, s);
-  if (drop)
-    return band ? launch_all<BF16, D, true, false, true>(p, o_f32, pr, gkv, gq, s)
-                : launch_all<BF16, D, false, false, true>(p, o_f32, pr, gkv, gq, s);
-  if (am) return launch_all<BF16, D, true, true, false>(p, o_f32, pr, gkv, gq, s);
-  return band ? launch_all<BF16, D, true, false, false>(p, o_f32, pr, gkv, gq, s)
-              : launch_all<BF16, D, false, false, false>(p, o_f32, pr, gkv, gq, s);
-}
 
 // The optional mask of fa_bwd_mask (data == nullptr: none).
 struct MaskArg {
@@ -224,8 +175,8 @@ fa_status bwd_run(const void* q, const void* k, const void* v, const void* o, co
   switch (d) {
 #define FA_BWD_D(DD)                                                                            \
   case DD:                                                                                      \
-    return bf16 ? dispatch_band<true, DD>(p, band, am, dropping, fm, o_f32, prep_rows, grid_kv, grid_q, s)    \
-                : dispatch_band<false, DD>(p, band, am, dropping, fm, o_f32, prep_rows, grid_kv, grid_q, s);
+    return bf16 ? fa::bwd_dispatch_slice<true, DD>(p, band, am, dropping, fm, o_f32, prep_rows, grid_kv, grid_q, s) \
+                : fa::bwd_dispatch_slice<false, DD>(p, band, am, dropping, fm, o_f32, prep_rows, grid_kv, grid_q, s);
     FA_BWD_D(32)
     FA_BWD_D(48)
     FA_BWD_D(64)
